@@ -1,0 +1,110 @@
+// Internal declarations shared by the HIP translation units of libbsfp8.so.
+// Device helpers (bf16 <-> fp32, E4M3 packing, UE8M0 exponent) and the host
+// launchers that the C-ABI layer (capi.hip) calls after argument checks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsfp8 {
+
+constexpr int kBlock = 128;        // weight block edge and act group width
+constexpr float kE4M3Max = 448.0f; // largest finite OCP E4M3FN magnitude
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- device
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load (data read once: non-temporal hint).
+__device__ __forceinline__ uint4 ld_stream16(const void* p) {
+  u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Four fp32 values -> four E4M3 bytes (little-endian in the result), round
+// to nearest even, saturating at +-448.  The clamp makes the hardware
+// conversion saturating; values in (448, 464) would round to 448 anyway.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  a = fminf(fmaxf(a, -kE4M3Max), kE4M3Max);
+  b = fminf(fmaxf(b, -kE4M3Max), kE4M3Max);
+  c = fminf(fmaxf(c, -kE4M3Max), kE4M3Max);
+  d = fminf(fmaxf(d, -kE4M3Max), kE4M3Max);
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+  return (uint32_t)r;
+}
+
+// e = ceil(log2(amax / 448)) clamped to [-127, 127]; 0 for amax == 0.
+// amax = f * 2^E with f in [1, 2): e = E - 8 when f <= 1.75, else E - 7.
+// Pure integer logic on the fp32 bits (subnormals normalised).
+__device__ __forceinline__ int ue8m0_exp(float amax) {
+  uint32_t u = __float_as_uint(amax) & 0x7fffffffu;
+  if (u == 0) return 0;
+  int E;
+  uint32_t frac;
+  uint32_t ef = u >> 23;
+  if (ef == 0) {                      // subnormal: value = u * 2^-149
+    int msb = 31 - __clz(u);          // position of the leading one
+    E = msb - 149;
+    frac = (u << (23 - msb)) & 0x7fffffu;
+  } else {
+    E = (int)ef - 127;
+    frac = u & 0x7fffffu;
+  }
+  int e = (frac <= 0x600000u) ? E - 8 : E - 7;   // 0x600000 = 0.75 * 2^23
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// ---------------------------------------------------------------- host
+
+hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                            int fmt, uint8_t* xq, void* scale, hipStream_t s);
+hipError_t launch_quant_weight(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
+                               int fmt, uint8_t* wq, void* scale, hipStream_t s);
+
+struct GemmArgs {
+  const uint8_t* xq;
+  const void* xs;          // [M][KB] fp32 or u8
+  const uint8_t* wq;       // [E][N][K]
+  const void* ws;          // [E][NB][KB]
+  const uint16_t* bias;    // [N] or null
+  uint16_t* y;             // [M][N]
+  int64_t M, N, K;
+  int fmt;
+  const int32_t* seg;      // grouped: [E+1] device offsets, else null
+  int E;
+  void* workspace;
+  size_t workspace_bytes;
+  // fused act quant (fp8_linear decode path): bf16 input, else null
+  const uint16_t* x_bf16;
+  int64_t ldx;
+};
+
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+size_t linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
+size_t grouped_workspace_bytes(int64_t T, int64_t N, int64_t K, int E);
+hipError_t launch_block_gemm(const GemmArgs& a, hipStream_t s);
+hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t s);
+
+size_t fp4_quant_workspace_bytes(int64_t R, int64_t K);
+size_t fp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_fp4_quant(const uint16_t* x, int64_t R, int64_t K, int dynamic,
+                            uint8_t* q4, uint8_t* gs, float* ts, void* ws, hipStream_t s);
+hipError_t launch_fp4_gemm(const uint8_t* xq, const uint8_t* xs, const float* xt,
+                           const uint8_t* wq, const uint8_t* wsc, const float* wt,
+                           uint16_t* y, int64_t M, int64_t N, int64_t K, void* ws,
+                           size_t ws_bytes, hipStream_t s);
+
+}  // namespace bsfp8

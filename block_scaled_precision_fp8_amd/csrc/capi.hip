@@ -1,0 +1,269 @@
+// C-ABI of libbsfp8.so (declared in include/bsfp8.h).
+//
+// Every entry point validates its arguments on the host first (no HIP call
+// before that), so every error return is reachable without a GPU.  Then it
+// checks, once per device, that the current device is a gfx950, checks that
+// the stream belongs to the current device, and enqueues the kernels.
+#include <atomic>
+#include <cstring>
+
+#include "bsfp8.h"
+#include "bsfp8_internal.h"
+
+using namespace bsfp8;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_state[kMaxDevices];   // 0 unknown, 1 gfx950, 2 other
+
+bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool fits_i32(int64_t v) { return v >= 0 && v <= 0x7fffffffLL; }
+bool valid_fmt(int32_t f) { return f == BSFP8_SCALE_FLOAT || f == BSFP8_SCALE_UE8M0; }
+
+// block sizes: the pages allow any positive pair ([FG-FP8] §四); only 128
+// is provided here.
+int32_t check_blocks(int32_t bn, int32_t bk) {
+  if (bn <= 0 || bk <= 0) return BSFP8_EINVAL;
+  if (bn != 128 || bk != 128) return BSFP8_ENOTSUP;
+  return BSFP8_OK;
+}
+
+int32_t check_device(void* stream) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return BSFP8_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return BSFP8_ENOTSUP;
+  int st = g_arch_state[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return BSFP8_EHIP;
+    st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_arch_state[dev].store(st, std::memory_order_relaxed);
+  }
+  if (st != 1) return BSFP8_ENOTSUP;
+  if (stream != nullptr) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice((hipStream_t)stream, &sdev) != hipSuccess) return BSFP8_EHIP;
+    if (sdev != dev) return BSFP8_ENOTSUP;
+  }
+  return BSFP8_OK;
+}
+
+int32_t hip_status(hipError_t e) {
+  if (e == hipSuccess) return BSFP8_OK;
+  return e == hipErrorNotSupported ? BSFP8_ENOTSUP : BSFP8_EHIP;
+}
+
+// shared checks of the FP8 GEMM operand set
+int32_t check_gemm(const void* xq, const void* xs, const void* wq, const void* ws,
+                   const void* bias, const void* y, int64_t M, int64_t N, int64_t K,
+                   int32_t bn, int32_t bk, int32_t fmt) {
+  if (M < 0 || N < 0 || K < 0) return BSFP8_EINVAL;
+  if (!fits_i32(M) || !fits_i32(N) || !fits_i32(K)) return BSFP8_EINVAL;
+  if (K % 16 != 0 || N % 8 != 0) return BSFP8_EINVAL;
+  if (!valid_fmt(fmt)) return BSFP8_EINVAL;
+  int32_t r = check_blocks(bn, bk);
+  if (r != BSFP8_OK) return r;
+  if (M == 0) return BSFP8_OK;
+  if (N == 0 || K == 0) return BSFP8_EINVAL;
+  if (!xq || !xs || !wq || !ws || !y) return BSFP8_EINVAL;
+  if (!al16(xq) || !al16(wq) || !al16(y) || (bias && !al16(bias))) return BSFP8_EINVAL;
+  if (!al16(xs) || !al16(ws)) return BSFP8_EINVAL;
+  return BSFP8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t bsfp8_version(void) { return 100; }
+
+const char* bsfp8_status_string(int32_t s) {
+  switch (s) {
+    case BSFP8_OK: return "ok";
+    case BSFP8_EINVAL: return "invalid argument";
+    case BSFP8_ENOTSUP: return "not supported (option, block size or device)";
+    case BSFP8_ENOSPC: return "workspace too small";
+    case BSFP8_EHIP: return "HIP runtime or launch error";
+    default: return "unknown status";
+  }
+}
+
+size_t bsfp8_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int32_t E) {
+  if (M < 0 || N < 0 || K < 0 || E < 0) return (size_t)-1;
+  switch (op) {
+    case BSFP8_OP_BLOCK_GEMM: return gemm_workspace_bytes(M, N, K);
+    case BSFP8_OP_LINEAR: return linear_workspace_bytes(M, N, K);
+    case BSFP8_OP_GROUPED_GEMM: return grouped_workspace_bytes(M, N, K, E);
+    case BSFP8_OP_FP4_QUANT: return fp4_quant_workspace_bytes(M, K);
+    case BSFP8_OP_FP4_GEMM: return fp4_gemm_workspace_bytes(M, N, K);
+    default: return (size_t)-1;
+  }
+}
+
+int32_t fp8_quant_act(const void* x, int64_t M, int64_t K, int64_t ldx, int32_t group_k,
+                      int32_t act_scheme, int32_t scale_fmt, void* xq, void* x_scale,
+                      void* stream) {
+  if (M < 0 || K < 0 || !fits_i32(M) || !fits_i32(K)) return BSFP8_EINVAL;
+  if (K % 16 != 0 || ldx < K || ldx % 8 != 0) return BSFP8_EINVAL;
+  if (act_scheme != BSFP8_ACT_DYNAMIC && act_scheme != BSFP8_ACT_STATIC) return BSFP8_EINVAL;
+  if (!valid_fmt(scale_fmt)) return BSFP8_EINVAL;
+  if (group_k <= 0) return BSFP8_EINVAL;
+  if (group_k != 128) return BSFP8_ENOTSUP;
+  if (act_scheme == BSFP8_ACT_STATIC) return BSFP8_ENOTSUP;
+  if (M == 0) return BSFP8_OK;
+  if (K == 0) return BSFP8_EINVAL;
+  if (!x || !xq || !x_scale) return BSFP8_EINVAL;
+  if (!al16(x) || !al16(xq) || !al16(x_scale)) return BSFP8_EINVAL;
+  if (!fits_i32(M * ((K + 127) / 128))) return BSFP8_EINVAL;
+  int32_t r = check_device(stream);
+  if (r != BSFP8_OK) return r;
+  return hip_status(launch_quant_act((const uint16_t*)x, M, K, ldx, scale_fmt, (uint8_t*)xq,
+                                     x_scale, (hipStream_t)stream));
+}
+
+int32_t fp8_quant_weight(const void* w, int64_t N, int64_t K, int64_t ldw, int32_t block_n,
+                         int32_t block_k, int32_t scale_fmt, void* wq, void* w_scale_inv,
+                         void* stream) {
+  if (N < 0 || K < 0 || !fits_i32(N) || !fits_i32(K)) return BSFP8_EINVAL;
+  if (K % 16 != 0 || ldw < K || ldw % 8 != 0) return BSFP8_EINVAL;
+  if (!valid_fmt(scale_fmt)) return BSFP8_EINVAL;
+  int32_t r = check_blocks(block_n, block_k);
+  if (r != BSFP8_OK) return r;
+  if (N == 0) return BSFP8_OK;
+  if (K == 0) return BSFP8_EINVAL;
+  if (!w || !wq || !w_scale_inv) return BSFP8_EINVAL;
+  if (!al16(w) || !al16(wq) || !al16(w_scale_inv)) return BSFP8_EINVAL;
+  if ((N + 127) / 128 > 65535) return BSFP8_EINVAL;
+  r = check_device(stream);
+  if (r != BSFP8_OK) return r;
+  return hip_status(launch_quant_weight((const uint16_t*)w, N, K, ldw, scale_fmt, (uint8_t*)wq,
+                                        w_scale_inv, (hipStream_t)stream));
+}
+
+int32_t fp8_block_gemm(const void* xq, const void* x_scale, const void* wq,
+                       const void* w_scale_inv, const void* bias, void* y, int64_t M, int64_t N,
+                       int64_t K, int32_t block_n, int32_t block_k, int32_t scale_fmt,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  int32_t r = check_gemm(xq, x_scale, wq, w_scale_inv, bias, y, M, N, K, block_n, block_k,
+                         scale_fmt);
+  if (r != BSFP8_OK || M == 0) return r;
+  const size_t need = gemm_workspace_bytes(M, N, K);
+  if (workspace_bytes < need) return BSFP8_ENOSPC;
+  if (need && (!workspace || !al16(workspace))) return BSFP8_EINVAL;
+  r = check_device(stream);
+  if (r != BSFP8_OK) return r;
+  GemmArgs a{};
+  a.xq = (const uint8_t*)xq; a.xs = x_scale; a.wq = (const uint8_t*)wq; a.ws = w_scale_inv;
+  a.bias = (const uint16_t*)bias; a.y = (uint16_t*)y; a.M = M; a.N = N; a.K = K;
+  a.fmt = scale_fmt; a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+  return hip_status(launch_block_gemm(a, (hipStream_t)stream));
+}
+
+int32_t fp8_linear(const void* x, int64_t ldx, const void* wq, const void* w_scale_inv,
+                   const void* bias, void* y, int64_t M, int64_t N, int64_t K, int32_t block_n,
+                   int32_t block_k, int32_t act_scheme, int32_t scale_fmt, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  if (act_scheme != BSFP8_ACT_DYNAMIC && act_scheme != BSFP8_ACT_STATIC) return BSFP8_EINVAL;
+  // the staged activations stand in for xq / x_scale in the operand checks
+  static const uint8_t dummy[16] __attribute__((aligned(16))) = {0};
+  int32_t r = check_gemm(x, dummy, wq, w_scale_inv, bias, y, M, N, K, block_n, block_k,
+                         scale_fmt);
+  if (r != BSFP8_OK) return r;
+  if (act_scheme == BSFP8_ACT_STATIC) return BSFP8_ENOTSUP;
+  if (M == 0) return BSFP8_OK;
+  if (ldx < K || ldx % 8 != 0) return BSFP8_EINVAL;
+  if (!fits_i32(M * ((K + 127) / 128))) return BSFP8_EINVAL;
+  const size_t need = linear_workspace_bytes(M, N, K);
+  if (workspace_bytes < need) return BSFP8_ENOSPC;
+  if (need && (!workspace || !al16(workspace))) return BSFP8_EINVAL;
+  r = check_device(stream);
+  if (r != BSFP8_OK) return r;
+  // workspace: [xq M*K][x_scale M*G*4][gemm workspace], 256-byte aligned parts
+  const int64_t G = (K + 127) / 128;
+  auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  uint8_t* ws = (uint8_t*)workspace;
+  uint8_t* xq = ws;
+  void* xs = ws + up((size_t)M * K);
+  void* gw = ws + up((size_t)M * K) + up((size_t)M * G * 4);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = launch_quant_act((const uint16_t*)x, M, K, ldx, scale_fmt, xq, xs, st);
+  if (e != hipSuccess) return BSFP8_EHIP;
+  GemmArgs a{};
+  a.xq = xq; a.xs = xs; a.wq = (const uint8_t*)wq; a.ws = w_scale_inv;
+  a.bias = (const uint16_t*)bias; a.y = (uint16_t*)y; a.M = M; a.N = N; a.K = K;
+  a.fmt = scale_fmt; a.workspace = gw;
+  a.workspace_bytes = workspace_bytes - (size_t)((uint8_t*)gw - ws);
+  return hip_status(launch_block_gemm(a, st));
+}
+
+int32_t fp8_grouped_gemm(const void* xq, const void* x_scale, const void* wq,
+                         const void* w_scale_inv, const int32_t* seg_offsets, int32_t E, void* y,
+                         int64_t T, int64_t N, int64_t K, int32_t block_n, int32_t block_k,
+                         int32_t scale_fmt, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  if (E < 1 || E > 1024) return BSFP8_EINVAL;
+  int32_t r = check_gemm(xq, x_scale, wq, w_scale_inv, nullptr, y, T, N, K, block_n, block_k,
+                         scale_fmt);
+  if (r != BSFP8_OK) return r;
+  if (T == 0) return BSFP8_OK;
+  if (!seg_offsets || ((uintptr_t)seg_offsets & 3u)) return BSFP8_EINVAL;
+  const size_t need = grouped_workspace_bytes(T, N, K, E);
+  if (workspace_bytes < need) return BSFP8_ENOSPC;
+  if (need && (!workspace || !al16(workspace))) return BSFP8_EINVAL;
+  const int64_t NT = (N + 255) / 256;
+  if (!fits_i32(((T + 127) / 128 + E) * NT)) return BSFP8_EINVAL;
+  r = check_device(stream);
+  if (r != BSFP8_OK) return r;
+  GemmArgs a{};
+  a.xq = (const uint8_t*)xq; a.xs = x_scale; a.wq = (const uint8_t*)wq; a.ws = w_scale_inv;
+  a.bias = nullptr; a.y = (uint16_t*)y; a.M = T; a.N = N; a.K = K; a.fmt = scale_fmt;
+  a.seg = seg_offsets; a.E = E; a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+  return hip_status(launch_grouped_gemm(a, (hipStream_t)stream));
+}
+
+int32_t fp4_quant(const void* x, int64_t R, int64_t K, int32_t dynamic_tscale, void* q4,
+                  void* gscale, float* tscale, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  if (R < 0 || K < 0 || !fits_i32(R) || !fits_i32(K)) return BSFP8_EINVAL;
+  if (K % 32 != 0) return BSFP8_EINVAL;
+  if (dynamic_tscale != 0 && dynamic_tscale != 1) return BSFP8_EINVAL;
+  if (R == 0) return BSFP8_OK;
+  if (K == 0) return BSFP8_EINVAL;
+  if (!x || !q4 || !gscale || !tscale) return BSFP8_EINVAL;
+  if (!al16(x) || !al16(q4) || !al16(gscale) || ((uintptr_t)tscale & 3u)) return BSFP8_EINVAL;
+  const size_t need = fp4_quant_workspace_bytes(R, K);
+  if (workspace_bytes < need) return BSFP8_ENOSPC;
+  if (need && (!workspace || !al16(workspace))) return BSFP8_EINVAL;
+  int32_t r = check_device(stream);
+  if (r != BSFP8_OK) return r;
+  return hip_status(launch_fp4_quant((const uint16_t*)x, R, K, dynamic_tscale, (uint8_t*)q4,
+                                     (uint8_t*)gscale, tscale, workspace, (hipStream_t)stream));
+}
+
+int32_t fp4_group_gemm(const void* xq4, const void* x_gscale, const float* x_tscale,
+                       const void* wq4, const void* w_gscale, const float* w_tscale, void* y,
+                       int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  if (M < 0 || N < 0 || K < 0 || !fits_i32(M) || !fits_i32(N) || !fits_i32(K))
+    return BSFP8_EINVAL;
+  if (K % 32 != 0 || N % 8 != 0) return BSFP8_EINVAL;
+  if (M == 0) return BSFP8_OK;
+  if (N == 0 || K == 0) return BSFP8_EINVAL;
+  if (!xq4 || !x_gscale || !x_tscale || !wq4 || !w_gscale || !w_tscale || !y)
+    return BSFP8_EINVAL;
+  if (!al16(xq4) || !al16(x_gscale) || !al16(wq4) || !al16(w_gscale) || !al16(y))
+    return BSFP8_EINVAL;
+  if (((uintptr_t)x_tscale & 3u) || ((uintptr_t)w_tscale & 3u)) return BSFP8_EINVAL;
+  const size_t need = fp4_gemm_workspace_bytes(M, N, K);
+  if (workspace_bytes < need) return BSFP8_ENOSPC;
+  if (need && (!workspace || !al16(workspace))) return BSFP8_EINVAL;
+  int32_t r = check_device(stream);
+  if (r != BSFP8_OK) return r;
+  return hip_status(launch_fp4_gemm((const uint8_t*)xq4, (const uint8_t*)x_gscale, x_tscale,
+                                    (const uint8_t*)wq4, (const uint8_t*)w_gscale, w_tscale,
+                                    (uint16_t*)y, M, N, K, workspace, workspace_bytes,
+                                    (hipStream_t)stream));
+}
+
+}  // extern "C"

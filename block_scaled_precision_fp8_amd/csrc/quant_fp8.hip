@@ -1,0 +1,196 @@
+// FP8 quantization kernels for gfx950.
+//
+//  * quant_act_kernel:    per-token 1x128 dynamic activation groups
+//                         (fine-grained FP8 guide, section 一, second bullet)
+//  * quant_weight_kernel: per 128x128 weight blocks
+//                         (same section, first bullet; scale tensor shape
+//                         (ceil(N/128), ceil(K/128)) from its third paragraph)
+//
+// Both are HBM-bound codecs: 2 bytes read and 1 byte written per element
+// plus one scale per group.  Every read is a coalesced 16-byte load of eight
+// bf16 values; every write is an 8-byte store of eight E4M3 codes.
+//
+// Scale formats (section 七 of the guide; readings for the open points):
+//   FLOAT: s = fl32(amax / 448) (1.0 for amax == 0), code = E4M3(fl32(x / s))
+//          with IEEE (correctly rounded) fp32 division.
+//   UE8M0: s = 2^e, e = ceil(log2(amax / 448)) clamped to [-127, 127] (fp32
+//          scales round *up* to UE8M0), code = E4M3(x * 2^-e) (exact scaling).
+#include "bsfp8_internal.h"
+
+namespace bsfp8 {
+namespace {
+
+constexpr int kActRows = 8;     // rows per quarter-wave per workgroup
+constexpr int kActUnroll = 4;   // loads in flight per lane
+
+struct Unpacked { float f[8]; };
+
+__device__ __forceinline__ Unpacked unpack8(uint4 v) {
+  Unpacked u;
+  u.f[0] = bf16_lo(v.x); u.f[1] = bf16_hi(v.x);
+  u.f[2] = bf16_lo(v.y); u.f[3] = bf16_hi(v.y);
+  u.f[4] = bf16_lo(v.z); u.f[5] = bf16_hi(v.z);
+  u.f[6] = bf16_lo(v.w); u.f[7] = bf16_hi(v.w);
+  return u;
+}
+
+__device__ __forceinline__ float amax8(const Unpacked& u) {
+  float a = fabsf(u.f[0]);
+#pragma unroll
+  for (int i = 1; i < 8; ++i) a = fmaxf(a, fabsf(u.f[i]));
+  return a;
+}
+
+// Encode eight values of one group with the group's scale.  Returns the
+// codes packed little-endian; writes the stored scale representation.
+template <int FMT>
+__device__ __forceinline__ uint2 encode8(const Unpacked& u, float amax, float* s_f32, int* s_exp) {
+  if (FMT == 0) {
+    const float s = (amax == 0.0f) ? 1.0f : amax / kE4M3Max;
+    *s_f32 = s;
+    uint2 r;
+    r.x = e4m3x4(u.f[0] / s, u.f[1] / s, u.f[2] / s, u.f[3] / s);
+    r.y = e4m3x4(u.f[4] / s, u.f[5] / s, u.f[6] / s, u.f[7] / s);
+    return r;
+  } else {
+    const int e = ue8m0_exp(amax);
+    *s_exp = e;
+    uint2 r;
+    r.x = e4m3x4(ldexpf(u.f[0], -e), ldexpf(u.f[1], -e), ldexpf(u.f[2], -e), ldexpf(u.f[3], -e));
+    r.y = e4m3x4(ldexpf(u.f[4], -e), ldexpf(u.f[5], -e), ldexpf(u.f[6], -e), ldexpf(u.f[7], -e));
+    return r;
+  }
+}
+
+// One 16-lane quarter-wave owns one 1x128 group of one row: each lane holds
+// eight consecutive bf16 values (one 16-byte load).  A workgroup of 16
+// quarters covers QG consecutive groups of RQ rows (QG * RQ = 16) and walks
+// kActRows such row sets, with kActUnroll loads issued before use.
+template <int FMT>
+__global__ __launch_bounds__(256) void quant_act_kernel(
+    const uint16_t* __restrict__ x, int M, int K, int64_t ldx, int G, int qg_log2,
+    uint8_t* __restrict__ xq, void* __restrict__ scale) {
+  const int tid = threadIdx.x;
+  const int l16 = tid & 15;
+  const int q = tid >> 4;
+  const int QG = 1 << qg_log2;
+  const int RQ = 16 >> qg_log2;
+  const int g = blockIdx.x * QG + (q & (QG - 1));
+  const int k0 = g * kBlock + l16 * 8;
+  const bool gvalid = g < G;
+  const bool kvalid = gvalid && k0 < K;
+  for (int mb = blockIdx.y; mb * (RQ * kActRows) < M; mb += gridDim.y) {
+  const int mbase = mb * (RQ * kActRows) + (q >> qg_log2);
+#pragma unroll
+  for (int jb = 0; jb < kActRows; jb += kActUnroll) {
+    uint4 v[kActUnroll];
+#pragma unroll
+    for (int u = 0; u < kActUnroll; ++u) {
+      const int m = mbase + RQ * (jb + u);
+      v[u] = make_uint4(0, 0, 0, 0);
+      if (kvalid && m < M)
+        v[u] = ld_stream16(x + (int64_t)m * ldx + k0);
+    }
+#pragma unroll
+    for (int u = 0; u < kActUnroll; ++u) {
+      const int m = mbase + RQ * (jb + u);
+      const Unpacked f = unpack8(v[u]);
+      float amax = amax8(f);
+      amax = fmaxf(amax, __shfl_xor(amax, 1, 16));
+      amax = fmaxf(amax, __shfl_xor(amax, 2, 16));
+      amax = fmaxf(amax, __shfl_xor(amax, 4, 16));
+      amax = fmaxf(amax, __shfl_xor(amax, 8, 16));
+      float sf = 0.0f;
+      int se = 0;
+      const uint2 codes = encode8<FMT>(f, amax, &sf, &se);
+      if (m < M) {
+        if (kvalid) *(uint2*)(xq + (int64_t)m * K + k0) = codes;
+        if (gvalid && l16 == 0) {
+          if (FMT == 0) ((float*)scale)[(int64_t)m * G + g] = sf;
+          else ((uint8_t*)scale)[(int64_t)m * G + g] = (uint8_t)(se + 127);
+        }
+      }
+    }
+  }
+  }
+}
+
+// One workgroup per 128x128 weight block.  Thread t loads column chunk
+// (t % 16) of rows (t / 16) + 16 i, i = 0..7: each wave reads four full
+// 256-byte row segments per load instruction.
+template <int FMT>
+__global__ __launch_bounds__(256) void quant_weight_kernel(
+    const uint16_t* __restrict__ w, int N, int K, int64_t ldw, int KB,
+    uint8_t* __restrict__ wq, void* __restrict__ scale) {
+  __shared__ float red[4];
+  const int kb = blockIdx.x, nb = blockIdx.y;
+  const int t = threadIdx.x;
+  const int ch = t & 15, r0 = t >> 4;
+  const int k0 = kb * kBlock + ch * 8;
+  const bool kvalid = k0 < K;
+  uint4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int n = nb * kBlock + r0 + 16 * i;
+    v[i] = make_uint4(0, 0, 0, 0);
+    if (kvalid && n < N)
+      v[i] = ld_stream16(w + (int64_t)n * ldw + k0);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, amax8(unpack8(v[i])));
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+  if ((t & 63) == 0) red[t >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+
+  float sf = 0.0f;
+  int se = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int n = nb * kBlock + r0 + 16 * i;
+    const uint2 codes = encode8<FMT>(unpack8(v[i]), amax, &sf, &se);
+    if (kvalid && n < N) *(uint2*)(wq + (int64_t)n * K + k0) = codes;
+  }
+  if (t == 0) {
+    if (FMT == 0) ((float*)scale)[(int64_t)nb * KB + kb] = sf;
+    else ((uint8_t*)scale)[(int64_t)nb * KB + kb] = (uint8_t)(se + 127);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int fmt,
+                            uint8_t* xq, void* scale, hipStream_t s) {
+  const int G = (int)((K + kBlock - 1) / kBlock);
+  int qg_log2 = 0;
+  while ((1 << qg_log2) < G && qg_log2 < 4) ++qg_log2;
+  const int QG = 1 << qg_log2, RQ = 16 >> qg_log2;
+  int64_t gy = (M + RQ * kActRows - 1) / (RQ * kActRows);
+  if (gy > 65535) gy = 65535;
+  dim3 grid((G + QG - 1) / QG, (unsigned)gy);
+  if (fmt == 0)
+    hipLaunchKernelGGL(quant_act_kernel<0>, grid, dim3(256), 0, s, x, (int)M, (int)K, ldx, G,
+                       qg_log2, xq, scale);
+  else
+    hipLaunchKernelGGL(quant_act_kernel<1>, grid, dim3(256), 0, s, x, (int)M, (int)K, ldx, G,
+                       qg_log2, xq, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_weight(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, int fmt,
+                               uint8_t* wq, void* scale, hipStream_t s) {
+  const int KB = (int)((K + kBlock - 1) / kBlock);
+  const int NB = (int)((N + kBlock - 1) / kBlock);
+  dim3 grid(KB, NB);
+  if (fmt == 0)
+    hipLaunchKernelGGL(quant_weight_kernel<0>, grid, dim3(256), 0, s, w, (int)N, (int)K, ldw, KB,
+                       wq, scale);
+  else
+    hipLaunchKernelGGL(quant_weight_kernel<1>, grid, dim3(256), 0, s, w, (int)N, (int)K, ldw, KB,
+                       wq, scale);
+  return hipGetLastError();
+}
+
+}  // namespace bsfp8

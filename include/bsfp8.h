@@ -1,0 +1,246 @@
+/*
+ * bsfp8.h -- C-ABI of libbsfp8.so: block-scaled FP8 and NVFP4-style linear
+ * layers on AMD MI355X (gfx950).
+ *
+ * Page citations use the page titles:
+ *   [FG-FP8] "Transformers 中的细粒度 FP8 量化：配置、DeepGEMM 加速路径与
+ *            UE8M0 缩放格式完全指南", sections 一 .. 九
+ *   [HF-PT]  "FP8 de granularidade fina" (Transformers docs)
+ *   [NVFP4]  "混合精度策略解析：NVIDIA Mistral-Medium-3.5-128B-NVFP4中FP8与
+ *            NVFP4的协同工作", sections on NVFP4 and on the config files
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor pointer is a DEVICE pointer on the current HIP device,
+ *   except where a parameter says "host".  The caller allocates and owns all
+ *   memory; the library allocates nothing, keeps no state between calls
+ *   (apart from a per-device architecture check done once), never
+ *   synchronises the device and never prints.
+ * - `stream` is a hipStream_t passed as void*; NULL means the default
+ *   stream.  Every call only enqueues work on that stream.
+ * - Matrices are row-major and dense unless a leading dimension is given.
+ *   bf16 tensors are raw 16-bit patterns (uint16_t); FP8 tensors are OCP
+ *   E4M3FN bytes; UE8M0 scales are E8M0 bytes (value 2^(b-127)); fp32
+ *   scales are IEEE binary32.
+ * - All argument checks run on the host before any HIP call, so the error
+ *   returns below are reachable without a GPU.  A zero-sized problem
+ *   (M, T or R == 0) returns BSFP8_OK without launching anything.
+ * - Return value: a bsfp8_status; BSFP8_EHIP means a HIP call or a kernel
+ *   launch failed (the HIP error is not cleared and can be read with
+ *   hipGetLastError / hipPeekAtLastError).
+ * - Pointers must be 16-byte aligned and leading dimensions must keep every
+ *   row 16-byte aligned (EINVAL otherwise).
+ */
+#ifndef BSFP8_H
+#define BSFP8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifndef BSFP8_API
+#define BSFP8_API __attribute__((visibility("default")))
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BSFP8_OK = 0,
+  BSFP8_EINVAL = 1,   /* bad argument: enum, size, null pointer, alignment  */
+  BSFP8_ENOTSUP = 2,  /* legal on the pages but not provided here, or a     */
+                      /* device that is not gfx950, or a stream that       */
+                      /* belongs to another device                         */
+  BSFP8_ENOSPC = 3,   /* workspace smaller than bsfp8_workspace_size()      */
+  BSFP8_EHIP = 4      /* HIP runtime / launch error                         */
+} bsfp8_status;
+
+/* scale_fmt: [FG-FP8] §四 allows "float" or "ue8m0"; §七 stores UE8M0 scales
+   as float8_e8m0fnu bytes. */
+typedef enum { BSFP8_SCALE_FLOAT = 0, BSFP8_SCALE_UE8M0 = 1 } bsfp8_scale_fmt;
+
+/* activation_scheme: [FG-FP8] §四 allows "dynamic" or "static"; the static
+   scheme is served by a separate kernel path on the pages (§6.1, §6.3) and is
+   not provided here (ENOTSUP). */
+typedef enum { BSFP8_ACT_DYNAMIC = 0, BSFP8_ACT_STATIC = 1 } bsfp8_act_scheme;
+
+/* Operation ids for bsfp8_workspace_size. */
+typedef enum {
+  BSFP8_OP_BLOCK_GEMM = 0,
+  BSFP8_OP_LINEAR = 1,
+  BSFP8_OP_GROUPED_GEMM = 2,
+  BSFP8_OP_FP4_QUANT = 3,
+  BSFP8_OP_FP4_GEMM = 4
+} bsfp8_op;
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+BSFP8_API int32_t bsfp8_version(void);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+BSFP8_API const char* bsfp8_status_string(int32_t status);
+
+/*
+ * fp8_quant_act -- per-token dynamic activation quantization in 1 x group_k
+ * groups ([FG-FP8] §一, second bullet; [HF-PT] opening list).
+ *
+ *   x        bf16 [M][ldx], read-only; only the first K columns are used.
+ *   M, K     rows (tokens) and columns (input channels); K % 16 == 0.
+ *   ldx      row stride of x in elements, ldx >= K, ldx % 8 == 0.
+ *   group_k  group width; must equal the weight block's K size, 128
+ *            ([FG-FP8] §一: the groups line up with the weight blocks).
+ *   act_scheme  BSFP8_ACT_DYNAMIC (STATIC -> ENOTSUP).
+ *   scale_fmt   FLOAT: s = fl32(amax/448), codes = E4M3(fl32(x/s)).
+ *               UE8M0: s = 2^e, e = ceil(log2(amax/448)) clamped to
+ *               [-127,127] ([FG-FP8] §七 note: fp32 scales round *up* to
+ *               UE8M0), stored as byte e+127; codes = E4M3(x * 2^-e).
+ *               amax = 0 gives s = 1.  E4M3 rounding is to nearest even,
+ *               saturating at +-448, sign of zero kept.
+ *   xq       out, E4M3 [M][K] (dense).
+ *   x_scale  out, [M][ceil(K/group_k)] fp32 (FLOAT) or uint8 (UE8M0); the
+ *            dequantization multiplier of each group.
+ * Errors: EINVAL (null pointers, M or K < 0, K % 16, ldx < K, ldx % 8,
+ * group_k != 128 when positive, group_k <= 0, bad enum, misalignment);
+ * ENOTSUP (static scheme; group_k other than 128).
+ */
+BSFP8_API int32_t fp8_quant_act(const void* x, int64_t M, int64_t K, int64_t ldx,
+                      int32_t group_k, int32_t act_scheme, int32_t scale_fmt,
+                      void* xq, void* x_scale, void* stream);
+
+/*
+ * fp8_quant_weight -- per 2D block weight quantization
+ * (weight_block_size = (block_n, block_k), [FG-FP8] §一 first bullet; the
+ * scale tensor weight_scale_inv has shape (ceil(N/128), ceil(K/128)),
+ * [FG-FP8] §一 third paragraph).
+ *
+ *   w        bf16 [N][ldw] in nn.Linear orientation (out, in); read-only.
+ *   N, K     output and input features; K % 16 == 0.
+ *   ldw      row stride in elements, ldw >= K, ldw % 8 == 0.
+ *   block_n, block_k   must be 128 (other positive sizes -> ENOTSUP).
+ *   scale_fmt  as for fp8_quant_act, with the amax over the whole block.
+ *   wq       out, E4M3 [N][K].
+ *   w_scale_inv  out, [ceil(N/128)][ceil(K/128)] fp32 or uint8 E8M0.
+ * A partial edge block takes its amax over its in-range elements only.
+ */
+BSFP8_API int32_t fp8_quant_weight(const void* w, int64_t N, int64_t K, int64_t ldw,
+                         int32_t block_n, int32_t block_k, int32_t scale_fmt,
+                         void* wq, void* w_scale_inv, void* stream);
+
+/*
+ * fp8_block_gemm -- the block-scaled FP8 GEMM ([FG-FP8] §一: aligned act
+ * groups and weight blocks let the matmul run block by block):
+ *
+ *   Y[m][n] = bf16_rne( sum_kb S_a[m][kb] * S_w[n/128][kb]
+ *                          * sum_{k in kb} Xq[m][k] * Wq[n][k]  + bias[n] )
+ *
+ * with exact FP8 products, fp32 accumulation, the combined scale applied to
+ * the fp32 partial sum once per 128-wide K block, and the unquantized bias
+ * ([FG-FP8] §三: bias is not quantized) added in fp32.
+ *
+ *   xq, x_scale       as written by fp8_quant_act (M rows).
+ *   wq, w_scale_inv   as written by fp8_quant_weight (N rows).
+ *   bias              bf16 [N] or NULL.
+ *   y                 out, bf16 [M][N].
+ *   block_n, block_k  must be 128.
+ *   workspace         device buffer of at least
+ *                     bsfp8_workspace_size(BSFP8_OP_BLOCK_GEMM, M, N, K, 0)
+ *                     bytes (may be NULL when that size is 0); contents on
+ *                     entry are ignored, on exit undefined.
+ * Errors: EINVAL (dims < 0, K % 16, null required pointers, bad enum,
+ * misalignment); ENOTSUP (block sizes other than 128); ENOSPC.
+ */
+BSFP8_API int32_t fp8_block_gemm(const void* xq, const void* x_scale, const void* wq,
+                       const void* w_scale_inv, const void* bias, void* y,
+                       int64_t M, int64_t N, int64_t K, int32_t block_n,
+                       int32_t block_k, int32_t scale_fmt, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/*
+ * fp8_linear -- one FP8 linear layer on bf16 activations: fp8_quant_act
+ * followed by fp8_block_gemm, i.e. the forward of the pages' FP8Linear
+ * ([FG-FP8] §八 step 6).  Results are identical to calling the two entry
+ * points in sequence.  For small M the quantization runs inside the GEMM
+ * launch; otherwise the quantized activations are staged in `workspace`.
+ *
+ *   x      bf16 [M][ldx];  other arguments as above.
+ *   workspace  >= bsfp8_workspace_size(BSFP8_OP_LINEAR, M, N, K, 0) bytes.
+ */
+BSFP8_API int32_t fp8_linear(const void* x, int64_t ldx, const void* wq,
+                   const void* w_scale_inv, const void* bias, void* y,
+                   int64_t M, int64_t N, int64_t K, int32_t block_n,
+                   int32_t block_k, int32_t act_scheme, int32_t scale_fmt,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fp8_grouped_gemm -- MoE expert GEMM over contiguous per-expert row
+ * segments ([FG-FP8] §一 FP8Experts; §6.4 and §七 expert backends).  For
+ * every expert e, rows [off[e], off[e+1]) of Y are the fp8_block_gemm of the
+ * same rows of (xq, x_scale) with expert e's (wq[e], w_scale_inv[e]).
+ *
+ *   xq           E4M3 [T][K];  x_scale [T][ceil(K/128)] (fp32 | UE8M0).
+ *   wq           E4M3 [E][N][K];  w_scale_inv [E][ceil(N/128)][ceil(K/128)].
+ *   seg_offsets  DEVICE int32 [E+1]: off[0] = 0, nondecreasing, off[E] = T.
+ *                This is a precondition and is not checked (checking would
+ *                need a device synchronisation).
+ *   E            number of experts, 1 <= E <= 1024.
+ *   y            out, bf16 [T][N]; rows of empty segments do not exist.
+ *   workspace    >= bsfp8_workspace_size(BSFP8_OP_GROUPED_GEMM, T, N, K, E).
+ */
+BSFP8_API int32_t fp8_grouped_gemm(const void* xq, const void* x_scale, const void* wq,
+                         const void* w_scale_inv, const int32_t* seg_offsets,
+                         int32_t E, void* y, int64_t T, int64_t N, int64_t K,
+                         int32_t block_n, int32_t block_k, int32_t scale_fmt,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fp4_quant -- NVFP4-style quantization ([NVFP4]: 4-bit float weights and
+ * input activations in 16-element groups, group_size 16): E2M1 codes with
+ * an E4M3 scale per 16-element group and one fp32 scale per tensor.
+ *
+ *   g   = fl32(amax_tensor / 2688)  (1.0 for an all-zero tensor)
+ *   sg  = E4M3(fl32(amax_group / fl32(6 g)))
+ *   eff = fl32(dec(sg) * g);  codes = E2M1(fl32(x / eff)), 0 when eff == 0
+ *
+ *   x          bf16 [R][K], K % 32 == 0.
+ *   dynamic_tscale  1: compute g from x and write it to *tscale;
+ *                   0: read g from *tscale (must be > 0, finite).
+ *   q4         out, uint8 [R][K/2]; element 2i in the low nibble of byte i.
+ *   gscale     out, E4M3 [R][K/16].
+ *   tscale     DEVICE float[1], out (dynamic) or in (static).
+ *   workspace  >= bsfp8_workspace_size(BSFP8_OP_FP4_QUANT, R, 0, K, 0).
+ */
+BSFP8_API int32_t fp4_quant(const void* x, int64_t R, int64_t K, int32_t dynamic_tscale,
+                  void* q4, void* gscale, float* tscale, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
+/*
+ * fp4_group_gemm -- GEMM of two NVFP4-style operands (the MLP projections of
+ * [NVFP4]):
+ *
+ *   Y[m][n] = bf16_rne( g_a g_w sum_k dec(qa[m][k]) dec(sa[m][k/16])
+ *                                    * dec(qw[n][k]) dec(sw[n][k/16]) )
+ *
+ *   xq4, x_gscale, x_tscale   as written by fp4_quant for X (M rows).
+ *   wq4, w_gscale, w_tscale   as written by fp4_quant for W (N rows).
+ *   y                          out, bf16 [M][N].  K % 32 == 0.
+ *   workspace  >= bsfp8_workspace_size(BSFP8_OP_FP4_GEMM, M, N, K, 0).
+ */
+BSFP8_API int32_t fp4_group_gemm(const void* xq4, const void* x_gscale,
+                       const float* x_tscale, const void* wq4,
+                       const void* w_gscale, const float* w_tscale, void* y,
+                       int64_t M, int64_t N, int64_t K, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of device workspace the given operation needs for this problem
+ * (0 if none).  `op` is a bsfp8_op; M is T for the grouped GEMM and R for
+ * fp4_quant; E is used by the grouped GEMM only.  Returns (size_t)-1 for an
+ * unknown op or negative sizes.
+ */
+BSFP8_API size_t bsfp8_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K,
+                            int32_t E);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSFP8_H */

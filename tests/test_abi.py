@@ -1,0 +1,148 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before any HIP call (no GPU needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_scaled_precision_fp8_amd import lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsfp8.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(L.LIB_PATH),
+                                reason="libbsfp8.so not built")
+
+FAKE = 0x100000       # 16-byte aligned, never dereferenced by the checks
+MIS = 0x100008        # misaligned
+
+
+def declared():
+    src = open(HEADER).read()
+    return re.findall(r"BSFP8_API\s+[\w\s\*]+?\b(\w+)\s*\(", src)
+
+
+def test_header_declarations_match_binding():
+    names = declared()
+    assert sorted(names) == sorted(L.EXPORTS)
+
+
+def test_every_declared_symbol_exported():
+    lib = ctypes.CDLL(L.LIB_PATH)
+    for name in declared():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings():
+    lib = L.load()
+    assert lib.bsfp8_version() >= 100
+    for s in range(5):
+        assert L.status_string(s)
+    assert L.status_string(99) == "unknown status"
+
+
+def _qa(**kw):
+    a = dict(x=FAKE, M=16, K=256, ldx=256, gk=128, sch=0, fmt=0, xq=FAKE, xs=FAKE, st=None)
+    a.update(kw)
+    return L.load().fp8_quant_act(a["x"], a["M"], a["K"], a["ldx"], a["gk"], a["sch"], a["fmt"],
+                                  a["xq"], a["xs"], a["st"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=-1), L.EINVAL), (dict(K=-16), L.EINVAL), (dict(K=200), L.EINVAL),
+    (dict(ldx=128), L.EINVAL), (dict(ldx=260), L.EINVAL), (dict(fmt=2), L.EINVAL),
+    (dict(sch=5), L.EINVAL), (dict(gk=0), L.EINVAL), (dict(gk=64), L.ENOTSUP),
+    (dict(sch=1), L.ENOTSUP), (dict(x=None), L.EINVAL), (dict(xq=None), L.EINVAL),
+    (dict(xs=None), L.EINVAL), (dict(x=MIS), L.EINVAL), (dict(M=0), L.OK),
+    (dict(M=0, x=None), L.OK),
+])
+def test_quant_act_argument_checks(kw, code):
+    assert _qa(**kw) == code
+
+
+def _qw(**kw):
+    a = dict(w=FAKE, N=256, K=256, ldw=256, bn=128, bk=128, fmt=0, wq=FAKE, ws=FAKE)
+    a.update(kw)
+    return L.load().fp8_quant_weight(a["w"], a["N"], a["K"], a["ldw"], a["bn"], a["bk"],
+                                     a["fmt"], a["wq"], a["ws"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=-1), L.EINVAL), (dict(K=8), L.EINVAL), (dict(bn=0), L.EINVAL),
+    (dict(bk=-128), L.EINVAL), (dict(bn=32, bk=32), L.ENOTSUP), (dict(fmt=-1), L.EINVAL),
+    (dict(wq=None), L.EINVAL), (dict(ws=MIS), L.EINVAL), (dict(N=0), L.OK),
+])
+def test_quant_weight_argument_checks(kw, code):
+    assert _qw(**kw) == code
+
+
+def _gemm(**kw):
+    a = dict(xq=FAKE, xs=FAKE, wq=FAKE, ws=FAKE, b=None, y=FAKE, M=16, N=256, K=256, bn=128,
+             bk=128, fmt=0, w=None, wb=0)
+    a.update(kw)
+    return L.load().fp8_block_gemm(a["xq"], a["xs"], a["wq"], a["ws"], a["b"], a["y"], a["M"],
+                                   a["N"], a["K"], a["bn"], a["bk"], a["fmt"], a["w"], a["wb"],
+                                   None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=-1), L.EINVAL), (dict(N=12), L.EINVAL), (dict(K=100), L.EINVAL),
+    (dict(fmt=3), L.EINVAL), (dict(bn=64), L.ENOTSUP), (dict(bk=0), L.EINVAL),
+    (dict(y=None), L.EINVAL), (dict(wq=None), L.EINVAL), (dict(b=MIS), L.EINVAL),
+    (dict(M=0), L.OK), (dict(N=0), L.EINVAL), (dict(M=2**31), L.EINVAL),
+])
+def test_block_gemm_argument_checks(kw, code):
+    assert _gemm(**kw) == code
+
+
+def test_block_gemm_workspace_too_small():
+    need = L.workspace_size(L.OP_BLOCK_GEMM, 16, 4096, 4096)
+    assert need > 0
+    assert _gemm(M=16, N=4096, K=4096, w=FAKE, wb=need - 1) == L.ENOSPC
+    assert _gemm(M=16, N=4096, K=4096, w=None, wb=need) == L.EINVAL
+
+
+def test_linear_argument_checks():
+    lib = L.load()
+    f = lib.fp8_linear
+    assert f(FAKE, 256, FAKE, FAKE, None, FAKE, 16, 256, 256, 128, 128, 1, 0, FAKE, 1 << 20,
+             None) == L.ENOTSUP
+    assert f(FAKE, 128, FAKE, FAKE, None, FAKE, 16, 256, 256, 128, 128, 0, 0, FAKE, 1 << 20,
+             None) == L.EINVAL
+    need = L.workspace_size(L.OP_LINEAR, 16, 256, 256)
+    assert need > 0
+    assert f(FAKE, 256, FAKE, FAKE, None, FAKE, 16, 256, 256, 128, 128, 0, 0, FAKE, need - 1,
+             None) == L.ENOSPC
+
+
+def test_grouped_argument_checks():
+    f = L.load().fp8_grouped_gemm
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, 64, 256, 256, 128, 128, 0, None, 0, None]
+    bad = list(args); bad[5] = 0
+    assert f(*bad) == L.EINVAL
+    bad = list(args); bad[5] = 1025
+    assert f(*bad) == L.EINVAL
+    bad = list(args); bad[4] = None
+    assert f(*bad) == L.EINVAL
+    bad = list(args); bad[12] = 7
+    assert f(*bad) == L.EINVAL
+    bad = list(args); bad[7] = 0
+    assert f(*bad) == L.OK
+
+
+def test_fp4_argument_checks():
+    lib = L.load()
+    assert lib.fp4_quant(FAKE, 4, 48, 1, FAKE, FAKE, FAKE, None, 0, None) == L.EINVAL
+    assert lib.fp4_quant(FAKE, 4, 64, 2, FAKE, FAKE, FAKE, None, 0, None) == L.EINVAL
+    assert lib.fp4_quant(FAKE, 0, 64, 1, FAKE, FAKE, FAKE, None, 0, None) == L.OK
+    assert lib.fp4_group_gemm(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 64, 48, None, 0,
+                              None) == L.EINVAL
+    assert lib.fp4_group_gemm(FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 4, 64, 64, None, 0,
+                              None) == L.EINVAL
+
+
+def test_workspace_size_unknown_op():
+    assert L.workspace_size(99, 1, 1, 16) == 2**64 - 1
+    assert L.load().bsfp8_workspace_size(0, -1, 1, 16, 0) == 2**64 - 1

@@ -1,0 +1,138 @@
+"""GPU parity of the FP8 quantizers against the oracle: codes and scales
+must match bit for bit."""
+
+import numpy as np
+import pytest
+
+from block_scaled_precision_fp8_amd import synth
+from oracle import formats as F
+from oracle import quant as Q
+
+from gpu_util import to_dev_bf16, u8, empty_u8, guard_intact, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_act(x_bits, fmt, ldx_pad=0):
+    import torch
+    from block_scaled_precision_fp8_amd import lib as L
+    M, K = x_bits.shape
+    if ldx_pad:
+        big = np.zeros((M, K + ldx_pad), np.uint16)
+        big[:, :K] = x_bits
+        xd = to_dev_bf16(big)[:, :K]
+    else:
+        xd = to_dev_bf16(x_bits)
+    G = -(-K // 128)
+    xq, xq_full = empty_u8((M, K))
+    if fmt == 0:
+        xs = torch.full((M, G), float("nan"), dtype=torch.float32, device=xd.device)
+    else:
+        xs = torch.full((M, G), 0xEE, dtype=torch.uint8, device=xd.device)
+    L.fp8_quant_act(xd, xq, xs, scale_fmt=fmt)
+    torch.cuda.synchronize()
+    assert guard_intact(xq_full, M * K)
+    return u8(xq), xs.cpu().numpy()
+
+
+def _check_act(x_bits, fmt, **kw):
+    say(f"act quant M={x_bits.shape[0]} K={x_bits.shape[1]} fmt={fmt}")
+    xq, xs = _run_act(x_bits, fmt, **kw)
+    rq, rs = Q.quant_act(x_bits, 128, fmt)
+    bad = np.argwhere(xq != rq)
+    assert bad.size == 0, f"{len(bad)} code mismatches, first {bad[:5].tolist()}"
+    if fmt == 0:
+        assert np.array_equal(xs.view(np.uint32), rs.view(np.uint32))
+    else:
+        assert np.array_equal(xs, rs)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("M,K,gen", [
+    (16, 256, "single"),           # the single-linear case
+    (1, 4096, "llama"), (64, 4096, "llama"), (33, 14336, "llama"),
+    (64, 7168, "deepseek"), (3, 1536, "deepseek"), (5, 18432, "deepseek"),
+    (7, 400, "deepseek"), (130, 16, "single"), (2, 2064, "llama"),
+])
+def test_act_quant_parity(M, K, gen, fmt):
+    if gen == "single":
+        x = synth.normal_bf16((M, K), 1.0, "single", "x", seed=M)
+    elif gen == "llama":
+        x = synth.llama_acts(M, K, seed=M)
+    else:
+        x = synth.deepseek_acts(M, K, seed=M)
+    _check_act(x, fmt)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_act_quant_row_stride(fmt):
+    _check_act(synth.llama_acts(9, 384, seed=3), fmt, ldx_pad=72)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_act_quant_every_bf16_pattern(fmt):
+    # every finite bf16 value appears once, in groups whose amax is set by a
+    # planted element, so each value is divided by many different scales
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    v = F.bf16_decode(bits)
+    fin = bits[np.isfinite(v)]
+    g = np.random.default_rng(0)
+    g.shuffle(fin)
+    n = (len(fin) // 127) * 127
+    body = fin[:n].reshape(-1, 127)
+    vals = np.abs(F.bf16_decode(body)).max(axis=1)
+    planted = synth.f32_to_bf16_bits(
+        (vals * g.uniform(1.0, 3.0, len(vals))).astype(np.float32).clip(0, 3e38))
+    x = np.concatenate([body, planted[:, None]], axis=1)
+    x = x[: (len(x) // 8) * 8].reshape(-1, 1024)
+    _check_act(x, fmt)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_act_quant_edge_values(fmt):
+    rows = []
+    rows.append(np.zeros(256, np.uint16))                                   # all zero
+    rows.append(np.full(256, 0x8000, np.uint16))                            # all -0
+    sub = np.arange(1, 257, dtype=np.uint16)                                # bf16 subnormals
+    rows.append(sub)
+    rows.append(sub | 0x8000)
+    rows.append(synth.f32_to_bf16_bits(np.linspace(-3e38, 3e38, 256).astype(np.float32)))
+    t = np.full(256, 0x3F80, np.uint16); t[7] = 0x4300                      # 1.0 and one 128
+    rows.append(t)
+    mix = synth.f32_to_bf16_bits(np.float32([1e-30, -1e-30, 448, -449, 0.0, 2 ** -126] * 43)[:256])
+    rows.append(mix)
+    _check_act(np.stack(rows), fmt)
+
+
+def _run_weight(w_bits, fmt):
+    import torch
+    from block_scaled_precision_fp8_amd import lib as L
+    N, K = w_bits.shape
+    wd = to_dev_bf16(w_bits)
+    wq, wq_full = empty_u8((N, K))
+    NB, KB = -(-N // 128), -(-K // 128)
+    if fmt == 0:
+        ws = torch.full((NB, KB), float("nan"), dtype=torch.float32, device=wd.device)
+    else:
+        ws = torch.full((NB, KB), 0xEE, dtype=torch.uint8, device=wd.device)
+    L.fp8_quant_weight(wd, wq, ws, scale_fmt=fmt)
+    torch.cuda.synchronize()
+    assert guard_intact(wq_full, N * K)
+    return u8(wq), ws.cpu().numpy()
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("N,K,sigma,work", [
+    (256, 256, 0.02, "single"), (130, 272, 0.02, "llama"), (4096, 4096, 0.02, "llama"),
+    (1536, 7168, 0.01, "deepseek"), (1000, 1040, 0.015, "nvfp4"),
+])
+def test_weight_quant_parity(N, K, sigma, work, fmt):
+    say(f"weight quant N={N} K={K} fmt={fmt}")
+    w = synth.normal_bf16((N, K), sigma, work, "w", seed=N)
+    wq, ws = _run_weight(w, fmt)
+    rq, rs = Q.quant_weight(w, 128, 128, fmt)
+    assert np.array_equal(wq, rq), f"{np.count_nonzero(wq != rq)} code mismatches"
+    if fmt == 0:
+        assert np.array_equal(ws.view(np.uint32), rs.view(np.uint32))
+    else:
+        assert np.array_equal(ws, rs)
