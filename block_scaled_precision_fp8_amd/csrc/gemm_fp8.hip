@@ -23,10 +23,12 @@
 //   gemm_stream_kernel  small M (<= 128): weight-streaming split-K kernel,
 //                       W fragments loaded straight into registers.
 //   splitk_reduce_kernel  fp32 partials -> bf16 (+ bias).
+#include <type_traits>
+
 #include "bsfp8_internal.h"
 
 namespace bsfp8 {
-namespace {
+namespace detail {
 
 constexpr int kRowBytes = 128;   // one K block of FP8 codes
 
@@ -35,6 +37,15 @@ __device__ __forceinline__ v8i join(uint4 a, uint4 b) {
   r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = a.w;
   r[4] = b.x; r[5] = b.y; r[6] = b.z; r[7] = b.w;
   return r;
+}
+
+// compile-time loop: f(std::integral_constant<int, 0>) .. f(<N - 1>)
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
 }
 
 template <int FMT>
@@ -163,20 +174,63 @@ __device__ __forceinline__ Tile grouped_tile(const int32_t* __restrict__ seg, in
   return tl;
 }
 
-template <int FMT, int BM, int BN, int WAVES_M, int WAVES_N, bool GROUPED>
+// Buffer resource over [base, base + bytes): loads past the end return 0,
+// which handles ragged M, N and K edges without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes > 0x7fffffffLL ? 0x7fffffff : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+constexpr uint32_t kOOB = 0x80000000u;   // an offset past any buffer's end
+
+#define BSFP8_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// s_waitcnt vmcnt(n), other counters untouched (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// One fragment read from LDS.  The restrict-qualified pointer gives the
+// loads alias-scope information; without it the compiler assumes they may
+// read what the in-flight LDS-DMA of the next stage writes and waits for
+// that DMA first, which would serialise the prefetch with the MFMAs.
+__device__ __forceinline__ v8i read_frag(const uint8_t* __restrict__ row, int ch0, int ch1) {
+  return join(*(const uint4*)(row + ch0), *(const uint4*)(row + ch1));
+}
+
+// Workgroup tile BM x BN = (WAVES_M * WM) x (WAVES_N * WN), K step 128 (one
+// scale block).  Operands go global -> LDS directly (buffer_load ... lds,
+// 16 bytes per lane), double-buffered; in LDS every 128-byte row keeps
+// its eight 16-byte chunks XOR-swizzled by ((row >> 1) & 7).  The LDS has
+// 64 four-byte banks (two 128-byte rows per sweep) and a ds_read_b128 serves
+// 16 lanes at a time; a fragment read has 16 lanes on 16 consecutive rows
+// and one logical chunk, so (row parity, physical chunk) must be distinct
+// over any 16 consecutive rows -- which this swizzle gives.  Each wave
+// computes a WM (m) x WN (n) tile with 16x16x128 MFMAs: W is the A operand,
+// X the B operand.
+template <int FMT, int WAVES_M, int WAVES_N, int WM, int WN, bool GROUPED>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
     const uint8_t* __restrict__ xq, const void* __restrict__ xs, const uint8_t* __restrict__ wq,
     const void* __restrict__ wsc, const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
     int64_t M, int64_t N, int64_t K, const int32_t* __restrict__ seg, int E) {
-  constexpr int THREADS = 64 * WAVES_M * WAVES_N;
-  constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  // The body exists only in the device pass; the host pass needs nothing
+  // but the launch stub of each instantiation.
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int STAGES = 2;
+  constexpr int WAVES = WAVES_M * WAVES_N;
+  constexpr int THREADS = 64 * WAVES;
+  constexpr int BM = WAVES_M * WM, BN = WAVES_N * WN;
   constexpr int MI = WM / 16, NI = WN / 16;
-  static_assert(128 % WN == 0 || WN % 128 == 0, "wave N range inside one weight block");
-  static_assert(WN <= 128, "wave N range inside one weight block");
-  constexpr int XCH = BM * 8 / THREADS;     // 16-byte chunks per thread per stage
-  constexpr int WCH = BN * 8 / THREADS;
+  static_assert(WN == 64 || WN == 128, "a wave's N range lies inside one weight block");
+  constexpr int XJ = BM * 8 / THREADS;      // DMA loads per lane per stage (X)
+  constexpr int WJ = BN * 8 / THREADS;      // (W)
+  static_assert(XJ * THREADS == BM * 8 && WJ * THREADS == BN * 8, "tile / thread mismatch");
+  constexpr int XBYTES = BM * kRowBytes;
   constexpr int STAGE = (BM + BN) * kRowBytes;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
+  constexpr int SB = FMT == 0 ? 4 : 1;      // bytes per scale
+  constexpr int LOADS = XJ + WJ + MI + 1;   // vector-memory ops per stage per lane
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES * STAGE];
   __shared__ int s_pref[GROUPED ? 1025 : 1];
 
   Tile tl;
@@ -184,62 +238,83 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
   else tl = dense_tile<BM, BN>(M, N);
   if (!tl.valid) return;
 
-  const int64_t KB = (K + 127) / 128;
+  const int KB = (int)((K + 127) / 128);
   const int64_t NB = (N + 127) / 128;
   const uint8_t* wbase = wq + (int64_t)tl.expert * N * K;
-  const uint8_t* wsb = (const uint8_t*)wsc + (int64_t)tl.expert * NB * KB * (FMT == 0 ? 4 : 1);
+  const uint8_t* wsb = (const uint8_t*)wsc + (int64_t)tl.expert * NB * KB * SB;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave % WAVES_M, wn = wave / WAVES_M;
   const int l16 = lane & 15, g4 = lane >> 4;
 
-  // ---- global -> register staging of one K block
-  uint4 xr[XCH], wr[WCH];
-  auto gload = [&](int64_t kb) {
-#pragma unroll
-    for (int i = 0; i < XCH; ++i) {
-      const int c = tid + THREADS * i;
-      const int row = c >> 3, ch = c & 7;
-      const int64_t m = tl.m0 + row;
-      const int64_t k = kb * 128 + ch * 16;
-      xr[i] = make_uint4(0, 0, 0, 0);
-      if (m < tl.mlim && k < K) xr[i] = *(const uint4*)(xq + m * K + k);
-    }
-#pragma unroll
-    for (int i = 0; i < WCH; ++i) {
-      const int c = tid + THREADS * i;
-      const int row = c >> 3, ch = c & 7;
-      const int64_t n = tl.n0 + row;
-      const int64_t k = kb * 128 + ch * 16;
-      wr[i] = make_uint4(0, 0, 0, 0);
-      if (n < N && k < K) wr[i] = *(const uint4*)(wbase + n * K + k);
-    }
+  const int64_t mrows = min((int64_t)BM, tl.mlim - tl.m0);
+  const int64_t nrows = min((int64_t)BN, N - tl.n0);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(xq + tl.m0 * K, mrows * K);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(wbase + tl.n0 * K, nrows * K);
+  const __amdgpu_buffer_rsrc_t rsa = make_rsrc((const uint8_t*)xs + tl.m0 * KB * SB,
+                                               mrows * KB * SB);
+  const __amdgpu_buffer_rsrc_t rsw = make_rsrc(wsb, NB * KB * SB);
+
+  // per-lane DMA source for LDS chunk q of a tile: row q / 8 holds, in its
+  // physical chunk q % 8, the logical chunk (q % 8) ^ ((row >> 1) & 7)
+  auto dma_src = [&](int q, int64_t rows, uint32_t kbyte) -> uint32_t {
+    const int row = q >> 3, c = (q & 7) ^ ((row >> 1) & 7);
+    const uint32_t kc = kbyte + c * 16;
+    return (row < rows && kc < (uint32_t)K) ? (uint32_t)(row * K) + kc : kOOB;
   };
-  auto sstore = [&](int buf) {
+  // scale sources: this lane's token rows, and this wave's weight block
+  uint32_t saoff[MI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    const int r = wm * WM + i * 16 + l16;
+    saoff[i] = r < mrows ? (uint32_t)(r * KB * SB) : kOOB;
+  }
+  const int64_t nwave = tl.n0 + wn * WN;
+  const uint32_t swoff = nwave < N ? (uint32_t)((nwave >> 7) * KB * SB) : kOOB;
+
+  float sa_reg[STAGES][MI];
+  float sw_reg[STAGES];
+
+  // issue one stage: X and W tiles into LDS buffer `buf`, scales into
+  // registers; exactly LOADS vector-memory ops per lane, in this order.
+  auto issue = [&](int kb, int buf) {
     uint8_t* sx = lds + buf * STAGE;
-    uint8_t* sw = sx + BM * kRowBytes;
+    uint8_t* sw = sx + XBYTES;
+    const uint32_t kbyte = (uint32_t)kb * 128;
 #pragma unroll
-    for (int i = 0; i < XCH; ++i) {
-      const int c = tid + THREADS * i;
-      const int row = c >> 3, ch = c & 7;
-      *(uint4*)(sx + row * kRowBytes + ((ch ^ (row & 7)) << 4)) = xr[i];
+    for (int j = 0; j < XJ; ++j) {
+      const int q = (j * WAVES + wave) * 64 + lane;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, BSFP8_LDS(sx + (j * WAVES + wave) * 1024),
+                                               16, dma_src(q, mrows, kbyte), 0, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < WCH; ++i) {
-      const int c = tid + THREADS * i;
-      const int row = c >> 3, ch = c & 7;
-      *(uint4*)(sw + row * kRowBytes + ((ch ^ (row & 7)) << 4)) = wr[i];
+    for (int j = 0; j < WJ; ++j) {
+      const int q = (j * WAVES + wave) * 64 + lane;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, BSFP8_LDS(sw + (j * WAVES + wave) * 1024),
+                                               16, dma_src(q, nrows, kbyte), 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const uint32_t off = saoff[i] == kOOB ? kOOB : saoff[i] + kb * SB;
+      if (FMT == 0) sa_reg[buf][i] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsa, off, 0, 0));
+      else sa_reg[buf][i] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b8(rsa, off, 0, 0));
+    }
+    {
+      const uint32_t off = swoff == kOOB ? kOOB : swoff + kb * SB;
+      if (FMT == 0) sw_reg[buf] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsw, off, 0, 0));
+      else sw_reg[buf] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b8(rsw, off, 0, 0));
     }
   };
-  // fragment read: 16 rows x 128 codes, lane (l16, g4) gets row l16, bytes
-  // [32 g4, 32 g4 + 32) -- the same K split for both operands.
-  auto frag = [&](const uint8_t* base, int row) -> v8i {
-    const uint8_t* r = base + row * kRowBytes;
-    const uint4 a = *(const uint4*)(r + (((2 * g4) ^ (row & 7)) << 4));
-    const uint4 b = *(const uint4*)(r + (((2 * g4 + 1) ^ (row & 7)) << 4));
-    return join(a, b);
+
+  // fragment: 16 rows x 128 codes; lane (l16, g4) takes row l16, bytes
+  // [32 g4, 32 g4 + 32) -- the same K split for both operands.  Fragment
+  // rows start at multiples of 16, so a row's swizzle ((row >> 1) & 7) is
+  // the lane's (l16 >> 1): two per-lane chunk offsets serve every fragment.
+  const int ch0 = ((2 * g4) ^ (l16 >> 1)) << 4;
+  const int ch1 = ((2 * g4 + 1) ^ (l16 >> 1)) << 4;
+  auto frag = [&](const uint8_t* row) -> v8i {
+    return join(*(const uint4*)(row + ch0), *(const uint4*)(row + ch1));
   };
 
   v4f acc[NI][MI];
@@ -248,51 +323,81 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
 #pragma unroll
     for (int j = 0; j < MI; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // per-lane token rows for the scales and the epilogue
-  int64_t mrow[MI];
-#pragma unroll
-  for (int j = 0; j < MI; ++j) mrow[j] = tl.m0 + wm * WM + j * 16 + l16;
-  const int64_t nwave = tl.n0 + wn * WN;
-  const int64_t nblk = nwave >> 7;
-
-  gload(0);
-  sstore(0);
-  __syncthreads();
-
-  for (int64_t kb = 0; kb < KB; ++kb) {
-    const int buf = (int)(kb & 1);
-    if (kb + 1 < KB) gload(kb + 1);
+  // One K block: issue the next stage's DMA, read this stage's fragments
+  // (they may interleave freely with the MFMAs), run the MFMAs.
+  auto step = [&](auto buf_c, int kb_next) {
+    constexpr int buf = decltype(buf_c)::value;
+    const uint8_t* sx = lds + buf * STAGE + (wm * WM + l16) * kRowBytes;
+    const uint8_t* swl = lds + buf * STAGE + XBYTES + (wn * WN + l16) * kRowBytes;
+    issue(kb_next, buf ^ 1);
     float sa[MI];
+    float sw = sw_reg[buf];
+    if (FMT == 1) sw = __int_as_float(__float_as_int(sw) & 0xff);
 #pragma unroll
-    for (int j = 0; j < MI; ++j)
-      sa[j] = (mrow[j] < tl.mlim) ? load_scale<FMT>(xs, mrow[j] * KB + kb)
-                                  : (FMT == 0 ? 0.f : __int_as_float(127));
-    const float sw = (nwave < N) ? load_scale<FMT>(wsb, nblk * KB + kb)
-                                 : (FMT == 0 ? 0.f : __int_as_float(127));
-    const uint8_t* sx = lds + buf * STAGE;
-    const uint8_t* swl = sx + BM * kRowBytes;
+    for (int j = 0; j < MI; ++j) {
+      sa[j] = sa_reg[buf][j];
+      if (FMT == 1) sa[j] = __int_as_float(__float_as_int(sa[j]) & 0xff);
+    }
     v8i bx[MI];
 #pragma unroll
-    for (int j = 0; j < MI; ++j) bx[j] = frag(sx, wm * WM + j * 16 + l16);
+    for (int j = 0; j < MI; ++j) bx[j] = read_frag(sx + j * 16 * kRowBytes, ch0, ch1);
+    // W fragments: one 16-row subtile at a time, a group of NG subtiles
+    // between scheduling fences (bounds the live fragments)
+    constexpr int NG = (MI * NI > 32) ? 2 : NI;
+    static_for<NI / NG>([&](auto gc) {
+      constexpr int g = decltype(gc)::value;
+      v8i aw[NG];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const v8i aw = frag(swl, wn * WN + i * 16 + l16);
+      for (int ii = 0; ii < NG; ++ii)
+        aw[ii] = read_frag(swl + (g * NG + ii) * 16 * kRowBytes, ch0, ch1);
 #pragma unroll
-      for (int j = 0; j < MI; ++j) acc[i][j] = mfma_step<FMT>(acc[i][j], aw, bx[j], sa[j], sw);
-    }
-    if (kb + 1 < KB) sstore(buf ^ 1);
-    __syncthreads();
-  }
+      for (int ii = 0; ii < NG; ++ii)
+#pragma unroll
+        for (int j = 0; j < MI; ++j)
+          acc[g * NG + ii][j] = mfma_step<FMT>(acc[g * NG + ii][j], aw[ii], bx[j], sa[j], sw);
+      if constexpr (NG < NI) __builtin_amdgcn_sched_barrier(0);
+    });
+  };
 
-  // ---- epilogue: lane holds n = nwave + 16 i + 4 g4 + {0..3}, m = mrow[j]
+  // prologue: stage 0
+  issue(0, 0);
+
+  // Main loop, unrolled by two so every register / buffer index is static.
+  // Each step issues the next stage unconditionally (a stage past the end
+  // loads zeros: its offsets are out of range).
+  for (int kb0 = 0;; kb0 += 2) {
+    bool last = false;
+    static_for<2>([&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+      if (last) return;
+      const int kb = kb0 + s;
+      // stage kb landed (own loads), then everyone's loads landed and
+      // everyone is done reading the buffer about to be refilled
+      wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      step(std::integral_constant<int, s>{}, kb + 1);
+      last = kb + 1 >= KB;
+    });
+    if (last) break;
+  }
+done:
+  // drain: no DMA may land in LDS after this workgroup has finished
+  wait_vmcnt<0>();
+
+  // epilogue: lane holds n = nwave + 16 i + 4 g4 + {0..3} for token m_j
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int64_t n = nwave + i * 16 + 4 * g4;
     if (n >= N) continue;
 #pragma unroll
-    for (int j = 0; j < MI; ++j)
-      if (mrow[j] < tl.mlim) store_out4(y, N, mrow[j], n, acc[i][j], bias);
+    for (int j = 0; j < MI; ++j) {
+      const int64_t m = tl.m0 + wm * WM + j * 16 + l16;
+      if (m < tl.mlim) store_out4(y, N, m, n, acc[i][j], bias);
+    }
   }
+#endif
+
 }
 
 // ------------------------------------------------------------------------
@@ -389,10 +494,27 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   store_out4(y, N, m, n, v4f{s.x, s.y, s.z, s.w}, bias);
 }
 
+// Explicit instantiations of every tile configuration the dispatcher below
+// can launch (the host pass does not always emit launch stubs for kernel
+// templates that are only instantiated implicitly).
+#define BSFP8_INST(FMT, WMN, WNN, WM, WN, G)                                                  \
+  template __global__ void gemm_lds_kernel<FMT, WMN, WNN, WM, WN, G>(                        \
+      const uint8_t* __restrict__, const void* __restrict__, const uint8_t* __restrict__,     \
+      const void* __restrict__, const uint16_t* __restrict__, uint16_t* __restrict__, int64_t, \
+      int64_t, int64_t, const int32_t* __restrict__, int);
+#define BSFP8_INST_ALL(FMT, G)          \
+  BSFP8_INST(FMT, 2, 2, 64, 128, G)     \
+  BSFP8_INST(FMT, 2, 4, 64, 64, G)
+BSFP8_INST_ALL(0, false)
+BSFP8_INST_ALL(1, false)
+BSFP8_INST_ALL(0, true)
+BSFP8_INST_ALL(1, true)
+#undef BSFP8_INST_ALL
+#undef BSFP8_INST
+
 // ------------------------------------------------------------------------
 // host side
 // ------------------------------------------------------------------------
-constexpr int kBM = 128, kBN = 256, kWavesM = 2, kWavesN = 2;
 constexpr int64_t kStreamMaxM = 128;
 
 int stream_splits(int64_t M, int64_t N, int64_t K) {
@@ -432,18 +554,47 @@ hipError_t launch_stream(const GemmArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int FMT>
-hipError_t launch_lds(const GemmArgs& a, hipStream_t st) {
-  const int64_t MT = (a.M + kBM - 1) / kBM, NT = (a.N + kBN - 1) / kBN;
-  int64_t tiles = MT * NT;
-  tiles = (tiles + 7) / 8 * 8;   // whole rounds over the 8 XCDs
-  hipLaunchKernelGGL((gemm_lds_kernel<FMT, kBM, kBN, kWavesM, kWavesN, false>),
-                     dim3((unsigned)tiles), dim3(64 * kWavesM * kWavesN), 0, st, a.xq, a.xs, a.wq,
-                     a.ws, a.bias, a.y, a.M, a.N, a.K, nullptr, 0);
+// Large-M tile configurations (WAVES_M x WAVES_N waves, wave tile WM x WN,
+// two LDS stages): BM = WM WAVES_M, BN = WN WAVES_N.
+//   3: 128 x 256, 4 waves of 64 x 128 (one per SIMD)
+//   4: 128 x 256, 8 waves of 64 x 64 (two per SIMD)
+// Two stages wait for vmcnt(0) before each K block, which does not depend
+// on the completion order of the LDS-DMA loads and the scale loads.
+template <int FMT, int WMN, int WNN, int WM, int WN, bool GROUPED>
+hipError_t launch_cfg(const GemmArgs& a, hipStream_t st) {
+  constexpr int BM = WMN * WM, BN = WNN * WN;
+  const int64_t NT = (a.N + BN - 1) / BN;
+  int64_t tiles;
+  if (GROUPED) {
+    tiles = ((a.M + BM - 1) / BM + a.E) * NT;   // every expert adds <= 1 partial M tile
+  } else {
+    tiles = (a.M + BM - 1) / BM * NT;
+    tiles = (tiles + 7) / 8 * 8;                 // whole rounds over the 8 XCDs
+  }
+  hipLaunchKernelGGL((gemm_lds_kernel<FMT, WMN, WNN, WM, WN, GROUPED>), dim3((unsigned)tiles),
+                     dim3(64 * WMN * WNN), 0, st, a.xq, a.xs, a.wq, a.ws,
+                     GROUPED ? nullptr : a.bias, a.y, a.M, a.N, a.K, a.seg, a.E);
   return hipGetLastError();
 }
 
-}  // namespace
+int choose_cfg(int64_t M, int64_t N, int fmt) {
+#ifdef BSFP8_SWEEP_CFG
+  return BSFP8_SWEEP_CFG;
+#endif
+  (void)M; (void)N; (void)fmt;
+  return 4;
+}
+
+template <int FMT, bool GROUPED>
+hipError_t launch_lds(const GemmArgs& a, hipStream_t st) {
+  switch (GROUPED ? 4 : choose_cfg(a.M, a.N, FMT)) {
+    case 3: return launch_cfg<FMT, 2, 2, 64, 128, GROUPED>(a, st);
+    default: return launch_cfg<FMT, 2, 4, 64, 64, GROUPED>(a, st);
+  }
+}
+
+}  // namespace detail
+using namespace detail;
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || M > kStreamMaxM) return 0;
@@ -465,22 +616,11 @@ size_t grouped_workspace_bytes(int64_t, int64_t, int64_t, int) { return 0; }
 
 hipError_t launch_block_gemm(const GemmArgs& a, hipStream_t st) {
   if (a.M <= kStreamMaxM) return a.fmt == 0 ? launch_stream<0>(a, st) : launch_stream<1>(a, st);
-  return a.fmt == 0 ? launch_lds<0>(a, st) : launch_lds<1>(a, st);
+  return a.fmt == 0 ? launch_lds<0, false>(a, st) : launch_lds<1, false>(a, st);
 }
 
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t st) {
-  // upper bound on tiles: every expert adds at most one partial M tile
-  const int64_t NT = (a.N + kBN - 1) / kBN;
-  const int64_t tiles = ((a.M + kBM - 1) / kBM + a.E) * NT;
-  if (a.fmt == 0)
-    hipLaunchKernelGGL((gemm_lds_kernel<0, kBM, kBN, kWavesM, kWavesN, true>), dim3((unsigned)tiles),
-                       dim3(64 * kWavesM * kWavesN), 0, st, a.xq, a.xs, a.wq, a.ws, nullptr, a.y,
-                       a.M, a.N, a.K, a.seg, a.E);
-  else
-    hipLaunchKernelGGL((gemm_lds_kernel<1, kBM, kBN, kWavesM, kWavesN, true>), dim3((unsigned)tiles),
-                       dim3(64 * kWavesM * kWavesN), 0, st, a.xq, a.xs, a.wq, a.ws, nullptr, a.y,
-                       a.M, a.N, a.K, a.seg, a.E);
-  return hipGetLastError();
+  return a.fmt == 0 ? launch_lds<0, true>(a, st) : launch_lds<1, true>(a, st);
 }
 
 }  // namespace bsfp8

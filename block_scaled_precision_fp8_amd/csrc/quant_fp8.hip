@@ -18,7 +18,7 @@
 #include "bsfp8_internal.h"
 
 namespace bsfp8 {
-namespace {
+namespace detail {
 
 constexpr int kActRows = 8;     // rows per quarter-wave per workgroup
 constexpr int kActUnroll = 4;   // loads in flight per lane
@@ -159,7 +159,8 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(
   }
 }
 
-}  // namespace
+}  // namespace detail
+using namespace detail;
 
 hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int fmt,
                             uint8_t* xq, void* scale, hipStream_t s) {

@@ -103,3 +103,32 @@ def device_normal_bf16(shape, sigma, workload, tensor, index=0, seed=0, device="
         n = min(step, flat.numel() - i)
         flat[i:i + n] = (torch.randn(n, generator=gen, device=device) * sigma).to(torch.bfloat16)
     return out
+
+
+def device_llama_acts(M, K, seed=0, index=0, outlier_frac=0.001, outlier_mult=50.0,
+                      device="cuda"):
+    """The ``llama`` activation recipe drawn on the device: N(0, 1), with the
+    outlier channels picked by the same seeded permutation as llama_acts."""
+    import torch
+    x = device_normal_bf16((M, K), 1.0, "llama", "x", index, seed, device).float()
+    n_out = int(round(outlier_frac * K))
+    if n_out:
+        ch = rng("llama", "misc", index, seed).permutation(K)[:n_out]
+        x[:, torch.from_numpy(ch).to(device)] *= outlier_mult
+    return x.to(torch.bfloat16)
+
+
+def device_deepseek_acts(M, K, seed=0, index=0, heavy_frac=0.1, dof=3.0, device="cuda"):
+    """The ``deepseek`` activation recipe drawn on the device (normal with a
+    Student-t(3) share), from torch's device generator."""
+    import torch
+    key = ((int(seed) * 131 + WORKLOAD_IDS["deepseek"]) * 131 + TENSOR_IDS["x"]) * 1_000_003 + index
+    gen = torch.Generator(device=device)
+    gen.manual_seed(key)
+    z = torch.randn((M, K), generator=gen, device=device)
+    # Student-t(dof) = N / sqrt(chi2_dof / dof); chi2_dof from dof normals
+    n = torch.randn((M, K), generator=gen, device=device)
+    chi = sum(torch.randn((M, K), generator=gen, device=device) ** 2 for _ in range(int(dof)))
+    t = n / torch.sqrt(chi / dof)
+    pick = torch.rand((M, K), generator=gen, device=device) < heavy_frac
+    return torch.where(pick, t, z).to(torch.bfloat16)
