@@ -1,20 +1,472 @@
-// NVFP4-style path (placeholder until the kernels land).
+// NVFP4-style path for gfx950: quantization and GEMM.
+//
+// The NVFP4 page (Mistral-Medium-3.5-128B-NVFP4, config_groups group_1)
+// stores the MLP projections' weights and input activations as 4-bit floats
+// in 16-element groups.  Each group carries an E4M3 scale and each tensor an
+// fp32 scale g:
+//   g   = fl32(amax_tensor / 2688)         (1.0 for an all-zero tensor)
+//   sg  = E4M3(fl32(amax_group / fl32(6 g)))
+//   eff = fl32(dec(sg) * g),  code = E2M1(fl32(x / eff))   (0 when eff == 0)
+// Codes are packed two per byte, element 2i in the low nibble.
+//
+// GEMM: an E2M1 value (<= 2 significant bits) times an E4M3 group scale
+// (<= 4 significant bits) needs at most 6 significant bits and lies in
+// [2^-10, 2688], so it is exact in fp16.  Operands are dequantized to fp16
+// in registers (hardware fp4 -> fp16 convert, then one packed fp16 multiply
+// by the group scale) and multiplied with fp16 MFMAs accumulating in fp32;
+// the two tensor scales are applied once in the epilogue.  The scaled
+// f8f6f4 MFMA cannot be used here: its block scales are powers of two on
+// 32-element blocks, while these group scales are E4M3 values on 16.
+//
+// Kernels:
+//   fp4_amax_kernel        per-block partial max |x| (dynamic tensor scale)
+//   fp4_quant_kernel       tensor scale from the partials, then one 16-element
+//                          group per lane
+//   fp4_gemm_stream_kernel M <= 64: weight-streaming split-K, W dequantized
+//                          straight from global memory
+//   fp4_gemm_lds_kernel    larger M: 128 x 128 tiles, both operands
+//                          dequantized once per workgroup into fp16 LDS tiles
+//   fp4_splitk_reduce      fp32 partials -> bf16
+#include <type_traits>
+
 #include "bsfp8_internal.h"
 
 namespace bsfp8 {
+namespace fp4d {
 
-size_t fp4_quant_workspace_bytes(int64_t, int64_t) { return 0; }
-size_t fp4_gemm_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
-hipError_t launch_fp4_quant(const uint16_t*, int64_t, int64_t, int, uint8_t*, uint8_t*, float*,
-                            void*, hipStream_t) {
-  return hipErrorNotSupported;
+constexpr int kAmaxBlocks = 1024;
+
+__device__ __forceinline__ float amax_bf16x8(uint4 v) {
+  float a = fabsf(bf16_lo(v.x));
+  a = fmaxf(a, fabsf(bf16_hi(v.x)));
+  a = fmaxf(a, fabsf(bf16_lo(v.y)));
+  a = fmaxf(a, fabsf(bf16_hi(v.y)));
+  a = fmaxf(a, fabsf(bf16_lo(v.z)));
+  a = fmaxf(a, fabsf(bf16_hi(v.z)));
+  a = fmaxf(a, fabsf(bf16_lo(v.w)));
+  a = fmaxf(a, fabsf(bf16_hi(v.w)));
+  return a;
 }
 
-hipError_t launch_fp4_gemm(const uint8_t*, const uint8_t*, const float*, const uint8_t*,
-                           const uint8_t*, const float*, uint16_t*, int64_t, int64_t, int64_t,
-                           void*, size_t, hipStream_t) {
-  return hipErrorNotSupported;
+__device__ __forceinline__ float block_max(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = red[0];
+  for (int w = 1; w < (int)(blockDim.x >> 6); ++w) r = fmaxf(r, red[w]);
+  __syncthreads();
+  return r;
+}
+
+// Partial max |x| over a grid-stride slice of the tensor (16 bytes per lane
+// per step).  Rows are dense (K elements each, K % 32 == 0).
+__global__ __launch_bounds__(256) void fp4_amax_kernel(const uint16_t* __restrict__ x,
+                                                       int64_t n8, float* __restrict__ part) {
+  __shared__ float red[4];
+  float a = 0.0f;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256)
+    a = fmaxf(a, amax_bf16x8(ld_stream16(x + i * 8)));
+  a = block_max(a, red);
+  if (threadIdx.x == 0) part[blockIdx.x] = a;
+}
+
+// One lane per 16-element group.  The tensor scale is either reduced from
+// the partial maxima (every block reduces them the same way, so every block
+// gets the same g) or read from *tscale.
+__global__ __launch_bounds__(256) void fp4_quant_kernel(
+    const uint16_t* __restrict__ x, int64_t groups, const float* __restrict__ part, int nparts,
+    float* __restrict__ tscale, uint8_t* __restrict__ q4, uint8_t* __restrict__ gs) {
+  __shared__ float red[4];
+  float g;
+  if (part != nullptr) {
+    float a = 0.0f;
+    for (int i = threadIdx.x; i < nparts; i += 256) a = fmaxf(a, part[i]);
+    a = block_max(a, red);
+    g = (a == 0.0f) ? 1.0f : a / 2688.0f;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *tscale = g;
+  } else {
+    g = *tscale;
+  }
+  const float den = 6.0f * g;
+  for (int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x; gi < groups;
+       gi += (int64_t)gridDim.x * 256) {
+    const uint4 v0 = ld_stream16(x + gi * 16);
+    const uint4 v1 = ld_stream16(x + gi * 16 + 8);
+    const float a = fmaxf(amax_bf16x8(v0), amax_bf16x8(v1));
+    // group scale: E4M3 of a / (6 g), saturating, round to nearest even
+    float sgf = a / den;
+    sgf = fminf(sgf, kE4M3Max);
+    const uint32_t sg = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sgf, 0.0f, 0, false) & 0xffu;
+    const float eff = __builtin_amdgcn_cvt_f32_fp8((int)sg, 0) * g;
+    float f[16];
+    f[0] = bf16_lo(v0.x); f[1] = bf16_hi(v0.x); f[2] = bf16_lo(v0.y); f[3] = bf16_hi(v0.y);
+    f[4] = bf16_lo(v0.z); f[5] = bf16_hi(v0.z); f[6] = bf16_lo(v0.w); f[7] = bf16_hi(v0.w);
+    f[8] = bf16_lo(v1.x); f[9] = bf16_hi(v1.x); f[10] = bf16_lo(v1.y); f[11] = bf16_hi(v1.y);
+    f[12] = bf16_lo(v1.z); f[13] = bf16_hi(v1.z); f[14] = bf16_lo(v1.w); f[15] = bf16_hi(v1.w);
+    uint2 codes = make_uint2(0, 0);
+    if (eff > 0.0f) {
+      // E2M1 encode of fl32(x / eff): the hardware convert with a unit scale
+      // rounds to nearest even and saturates at 6; element 2i -> low nibble
+      uint32_t lo = 0, hi = 0;
+      lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, f[0] / eff, f[1] / eff, 1.0f, 0);
+      lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, f[2] / eff, f[3] / eff, 1.0f, 1);
+      lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, f[4] / eff, f[5] / eff, 1.0f, 2);
+      lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, f[6] / eff, f[7] / eff, 1.0f, 3);
+      hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, f[8] / eff, f[9] / eff, 1.0f, 0);
+      hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, f[10] / eff, f[11] / eff, 1.0f, 1);
+      hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, f[12] / eff, f[13] / eff, 1.0f, 2);
+      hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, f[14] / eff, f[15] / eff, 1.0f, 3);
+      codes = make_uint2(lo, hi);
+    }
+    *(uint2*)(q4 + gi * 8) = codes;
+    gs[gi] = (uint8_t)sg;
+  }
+}
+
+// ---------------------------------------------------------------- GEMM
+
+// Eight E2M1 codes (one 32-bit word, element 0 in the low nibble) times one
+// group scale -> eight fp16 values, exact.
+__device__ __forceinline__ half8 dequant8(uint32_t w, _Float16 s) {
+  const half2v s2 = {s, s};
+  half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
+  half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
+  half2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
+  half2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
+  half8 r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+__device__ __forceinline__ _Float16 e4m3_to_f16(uint32_t byte) {
+  return (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)byte, 0);
+}
+
+__device__ __forceinline__ void store4_bf16(uint16_t* y, int64_t N, int64_t m, int64_t n, v4f v) {
+  uint2 o;
+  o.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+  o.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+  *(uint2*)(y + m * N + n) = o;
+}
+
+// A 128-wide K block of one row: 64 bytes of codes + 8 group-scale bytes.
+// Lane (l16, g4) owns K [32 g4, 32 g4 + 32): 16 code bytes (4 words) and 2
+// scale bytes.  MFMA step t (0..3) uses word t: K [32 g4 + 8 t, + 8), group
+// 2 g4 + t / 2 -- the same K assignment for both operands.
+struct Frag128 {
+  uint4 codes;
+  uint32_t scales;   // two scale bytes in bits [15:0]
+};
+
+__device__ __forceinline__ Frag128 load_frag128(const uint8_t* q4, const uint8_t* gs, int64_t row,
+                                                int64_t K, int64_t kb, int g4, bool valid) {
+  Frag128 f;
+  f.codes = make_uint4(0, 0, 0, 0);
+  f.scales = 0;
+  const int64_t k0 = kb * 128 + 32 * g4;
+  if (valid && k0 < K) {
+    f.codes = *(const uint4*)(q4 + row * (K / 2) + k0 / 2);
+    f.scales = *(const uint16_t*)(gs + row * (K / 16) + k0 / 16);
+  }
+  return f;
+}
+
+__device__ __forceinline__ half8 frag_step(const Frag128& f, int t) {
+  const uint32_t w = t == 0 ? f.codes.x : t == 1 ? f.codes.y : t == 2 ? f.codes.z : f.codes.w;
+  return dequant8(w, e4m3_to_f16((f.scales >> (8 * (t >> 1))) & 0xffu));
+}
+
+constexpr int kStreamWaves = 4;
+
+template <int MT>
+__global__ __launch_bounds__(64 * kStreamWaves) void fp4_gemm_stream_kernel(
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
+    const float* __restrict__ xt, const uint8_t* __restrict__ wq,
+    const uint8_t* __restrict__ ws, const float* __restrict__ wt, uint16_t* __restrict__ y,
+    float* __restrict__ part, int M, int64_t N, int64_t K, int kb_per_split) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int64_t n0 = ((int64_t)blockIdx.x * kStreamWaves + wave) * 16;
+  if (n0 >= N) return;
+  const int64_t KB = (K + 127) / 128;
+  const int64_t kb0 = (int64_t)blockIdx.y * kb_per_split;
+  const int64_t kb1 = min(KB, kb0 + kb_per_split);
+  const bool nvalid = n0 + l16 < N;
+  v4f acc[MT];
+#pragma unroll
+  for (int j = 0; j < MT; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+  constexpr int U = 2;
+  for (int64_t kb = kb0; kb < kb1; kb += U) {
+    Frag128 fw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      fw[u] = load_frag128(wq, ws, n0 + l16, K, kb + u, g4, nvalid && kb + u < kb1);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (kb + u >= kb1) break;
+      Frag128 fx[MT];
+#pragma unroll
+      for (int j = 0; j < MT; ++j)
+        fx[j] = load_frag128(xq, xs, j * 16 + l16, K, kb + u, g4, j * 16 + l16 < M);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const half8 a = frag_step(fw[u], t);
+#pragma unroll
+        for (int j = 0; j < MT; ++j)
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, frag_step(fx[j], t), acc[j], 0, 0, 0);
+      }
+    }
+  }
+  const float gg = (*xt) * (*wt);
+  const int64_t n = n0 + 4 * g4;
+  if (n >= N) return;
+#pragma unroll
+  for (int j = 0; j < MT; ++j) {
+    const int m = j * 16 + l16;
+    if (m >= M) continue;
+    const v4f v = acc[j] * gg;
+    if (part == nullptr) store4_bf16(y, N, m, n, v);
+    else *(float4*)(part + ((int64_t)blockIdx.y * M + m) * N + n) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+}
+
+__global__ __launch_bounds__(256) void fp4_splitk_reduce(const float* __restrict__ part, int splits,
+                                                         int64_t MN, int64_t N,
+                                                         uint16_t* __restrict__ y) {
+  const int64_t i4 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i4 >= MN) return;
+  float4 s = *(const float4*)(part + i4);
+  for (int k = 1; k < splits; ++k) {
+    const float4 t = *(const float4*)(part + (int64_t)k * MN + i4);
+    s.x += t.x; s.y += t.y; s.z += t.z; s.w += t.w;
+  }
+  const int64_t m = i4 / N, n = i4 - m * N;
+  store4_bf16(y, N, m, n, v4f{s.x, s.y, s.z, s.w});
+}
+
+// Large-M kernel: 128 x 128 output tile, 4 waves of 64 x 64, K step 128.
+// Every K block: each thread loads half a row of codes + scales of X and of
+// W (global -> registers, one block ahead), dequantizes them to fp16 and
+// stores them to LDS; rows are 256 bytes (16 chunks of 8 halves) with chunk
+// c stored at c ^ (row & 15), so the 16 rows of a fragment read hit 16
+// different bank groups.
+constexpr int kLdsBM = 128, kLdsBN = 128;
+
+__global__ __launch_bounds__(256, 1) void fp4_gemm_lds_kernel(
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
+    const float* __restrict__ xt, const uint8_t* __restrict__ wq,
+    const uint8_t* __restrict__ ws, const float* __restrict__ wt, uint16_t* __restrict__ y,
+    int64_t M, int64_t N, int64_t K) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][(kLdsBM + kLdsBN) * 256];
+  const int64_t MT = (M + kLdsBM - 1) / kLdsBM;
+  const int64_t NT = (N + kLdsBN - 1) / kLdsBN;
+  // XCD-aware order, M tiles fastest within groups of 8
+  const int bid = blockIdx.x;
+  const int per_xcd = (int)(gridDim.x / 8);
+  const int t = (bid & 7) * per_xcd + (bid >> 3);
+  if (t >= MT * NT) return;
+  constexpr int GM = 8;
+  const int group = t / (GM * (int)NT);
+  const int first_m = group * GM;
+  const int gsz = min((int)MT - first_m, GM);
+  const int in = t - group * GM * (int)NT;
+  const int64_t m0 = (int64_t)(first_m + in % gsz) * kLdsBM;
+  const int64_t n0 = (int64_t)(in / gsz) * kLdsBN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int64_t KB = (K + 127) / 128;
+
+  // loader role: row r (0..127), half h (0..1): K [64 h, 64 h + 64) of the block
+  const int lr = tid >> 1, lh = tid & 1;
+  const bool xrow_ok = m0 + lr < M, wrow_ok = n0 + lr < N;
+  uint4 xc[2], wc[2];
+  uint32_t xsc = 0, wsc = 0;
+  auto gload = [&](int64_t kb) {
+    const int64_t k0 = kb * 128 + 64 * lh;
+    const bool kok = k0 < K;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      xc[i] = make_uint4(0, 0, 0, 0);
+      wc[i] = make_uint4(0, 0, 0, 0);
+    }
+    xsc = wsc = 0;
+    // K % 32 == 0: each 32-element quarter is wholly in or out of range
+    if (xrow_ok && kok) {
+      const uint8_t* p = xq + (m0 + lr) * (K / 2) + k0 / 2;
+      xc[0] = *(const uint4*)p;
+      if (k0 + 32 < K) xc[1] = *(const uint4*)(p + 16);
+      const uint8_t* s = xs + (m0 + lr) * (K / 16) + k0 / 16;
+      xsc = s[0] | (s[1] << 8);
+      if (k0 + 32 < K) xsc |= (s[2] << 16) | (s[3] << 24);
+    }
+    if (wrow_ok && kok) {
+      const uint8_t* p = wq + (n0 + lr) * (K / 2) + k0 / 2;
+      wc[0] = *(const uint4*)p;
+      if (k0 + 32 < K) wc[1] = *(const uint4*)(p + 16);
+      const uint8_t* s = ws + (n0 + lr) * (K / 16) + k0 / 16;
+      wsc = s[0] | (s[1] << 8);
+      if (k0 + 32 < K) wsc |= (s[2] << 16) | (s[3] << 24);
+    }
+  };
+  // dequantize this thread's 64 elements of each operand into LDS buffer b
+  auto dstore = [&](int b) {
+    uint8_t* sx = lds[b];
+    uint8_t* sw = lds[b] + kLdsBM * 256;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {          // chunk c: 8 values, group c / 2
+      const uint32_t xw = c < 4 ? (&xc[0].x)[c] : (&xc[1].x)[c - 4];
+      const uint32_t ww = c < 4 ? (&wc[0].x)[c] : (&wc[1].x)[c - 4];
+      const half8 hx = dequant8(xw, e4m3_to_f16((xsc >> (8 * (c >> 1))) & 0xffu));
+      const half8 hw = dequant8(ww, e4m3_to_f16((wsc >> (8 * (c >> 1))) & 0xffu));
+      const int chunk = lh * 8 + c;
+      const int phys = chunk ^ (lr & 15);
+      *(half8*)(sx + lr * 256 + phys * 16) = hx;
+      *(half8*)(sw + lr * 256 + phys * 16) = hw;
+    }
+  };
+
+  v4f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  gload(0);
+  dstore(0);
+  __syncthreads();
+  for (int64_t kb = 0; kb < KB; ++kb) {
+    const int b = (int)(kb & 1);
+    if (kb + 1 < KB) gload(kb + 1);
+    const uint8_t* sx = lds[b];
+    const uint8_t* sw = lds[b] + kLdsBM * 256;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {        // MFMA K step: chunks 4 ks + g4
+      half8 bx[4], aw[4];
+      const int chunk = 4 * ks + g4;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = wm * 64 + j * 16 + l16;
+        bx[j] = *(const half8*)(sx + r * 256 + ((chunk ^ (r & 15)) * 16));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = wn * 64 + i * 16 + l16;
+        aw[i] = *(const half8*)(sw + r * 256 + ((chunk ^ (r & 15)) * 16));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw[i], bx[j], acc[i][j], 0, 0, 0);
+    }
+    if (kb + 1 < KB) dstore(b ^ 1);
+    __syncthreads();
+  }
+
+  const float gg = (*xt) * (*wt);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t n = n0 + wn * 64 + i * 16 + 4 * g4;
+    if (n >= N) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t m = m0 + wm * 64 + j * 16 + l16;
+      if (m < M) store4_bf16(y, N, m, n, acc[i][j] * gg);
+    }
+  }
+}
+
+constexpr int64_t kStreamMaxM = 64;
+
+int fp4_splits(int64_t N, int64_t K) {
+  const int64_t KB = (K + 127) / 128;
+  const int64_t wg_n = (N + 16 * kStreamWaves - 1) / (16 * kStreamWaves);
+  int64_t want = (2048 + wg_n - 1) / wg_n;
+  int64_t max_by_depth = KB / 4;
+  int64_t s = want < max_by_depth ? want : max_by_depth;
+  if (s < 1) s = 1;
+  if (s > 64) s = 64;
+  return (int)s;
+}
+
+void fp4_split_plan(int64_t N, int64_t K, int* kbps, int* real) {
+  const int64_t KB = (K + 127) / 128;
+  const int s = fp4_splits(N, K);
+  *kbps = (int)((KB + s - 1) / s);
+  *real = (int)((KB + *kbps - 1) / *kbps);
+}
+
+}  // namespace fp4d
+using namespace fp4d;
+
+size_t fp4_quant_workspace_bytes(int64_t, int64_t) { return kAmaxBlocks * sizeof(float); }
+
+size_t fp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || M > kStreamMaxM) return 0;
+  int kbps, real;
+  fp4_split_plan(N, K, &kbps, &real);
+  return real > 1 ? (size_t)real * M * N * sizeof(float) : 0;
+}
+
+hipError_t launch_fp4_quant(const uint16_t* x, int64_t R, int64_t K, int dynamic, uint8_t* q4,
+                            uint8_t* gs, float* ts, void* ws, hipStream_t s) {
+  const int64_t n8 = R * K / 8;
+  const int64_t groups = R * K / 16;
+  float* part = nullptr;
+  int nparts = 0;
+  if (dynamic) {
+    part = (float*)ws;
+    int64_t nb = (n8 + 256 * 8 - 1) / (256 * 8);
+    if (nb > kAmaxBlocks) nb = kAmaxBlocks;
+    if (nb < 1) nb = 1;
+    nparts = (int)nb;
+    hipLaunchKernelGGL(fp4_amax_kernel, dim3(nparts), dim3(256), 0, s, x, n8, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  int64_t nb = (groups + 255) / 256;
+  if (nb > 8192) nb = 8192;
+  hipLaunchKernelGGL(fp4_quant_kernel, dim3((unsigned)nb), dim3(256), 0, s, x, groups, part,
+                     nparts, ts, q4, gs);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp4_gemm(const uint8_t* xq, const uint8_t* xs, const float* xt,
+                           const uint8_t* wq, const uint8_t* wsc, const float* wt, uint16_t* y,
+                           int64_t M, int64_t N, int64_t K, void* ws, size_t, hipStream_t s) {
+  if (M > kStreamMaxM) {
+    int64_t tiles = ((M + kLdsBM - 1) / kLdsBM) * ((N + kLdsBN - 1) / kLdsBN);
+    tiles = (tiles + 7) / 8 * 8;
+    hipLaunchKernelGGL(fp4_gemm_lds_kernel, dim3((unsigned)tiles), dim3(256), 0, s, xq, xs, xt,
+                       wq, wsc, wt, y, M, N, K);
+    return hipGetLastError();
+  }
+  int kbps, real;
+  fp4_split_plan(N, K, &kbps, &real);
+  float* part = real > 1 ? (float*)ws : nullptr;
+  dim3 grid((unsigned)((N + 16 * kStreamWaves - 1) / (16 * kStreamWaves)), real);
+  const int Mi = (int)M;
+#define BSFP8_FP4S(MT)                                                                          \
+  hipLaunchKernelGGL((fp4_gemm_stream_kernel<MT>), grid, dim3(64 * kStreamWaves), 0, s, xq, xs, \
+                     xt, wq, wsc, wt, y, part, Mi, N, K, kbps)
+  if (M <= 16) BSFP8_FP4S(1);
+  else if (M <= 32) BSFP8_FP4S(2);
+  else BSFP8_FP4S(4);
+#undef BSFP8_FP4S
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || part == nullptr) return e;
+  const int64_t MN = M * N;
+  hipLaunchKernelGGL(fp4_splitk_reduce, dim3((unsigned)((MN / 4 + 255) / 256)), dim3(256), 0, s,
+                     part, real, MN, N, y);
+  return hipGetLastError();
 }
 
 }  // namespace bsfp8
