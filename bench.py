@@ -1,61 +1,377 @@
-"""Benchmark of the block-scaled FP8 linear on one MI355X.
+"""Benchmark of the block-scaled FP8 / NVFP4-style linear path on one MI355X.
 
-Workload: the Llama-3-8B-shaped FP8 linears -- (K, N) in {(4096, 4096),
-(4096, 6144), (4096, 28672), (14336, 4096)} x M in {1, 16, 128, 2048, 8192}
-(20 runs), bf16 activations N(0, 1) with 0.1% outlier channels x50, weights
-N(0, 0.02), 1x128 dynamic act groups, 128x128 weight blocks, fp32 scales.
-
-One step = one FP8 linear forward for every run: dynamic activation
-quantization (fp8_quant_act) followed by the block-scaled GEMM
+Headline workload (``value``): the Llama-3-8B-shaped FP8 linears -- (K, N) in
+{(4096, 4096), (4096, 6144), (4096, 28672), (14336, 4096)} x M in
+{1, 16, 128, 2048, 8192} (20 runs), bf16 activations N(0, 1) with 0.1%
+outlier channels x50, weights N(0, 0.02), 1x128 dynamic act groups, 128x128
+weight blocks, fp32 scales.  One step = one FP8 linear forward for every run:
+dynamic activation quantization (fp8_quant_act) then the block-scaled GEMM
 (fp8_block_gemm).  Weights are quantized once before timing (load-time step)
-and two quantized copies are alternated step by step so that decode-sized
-runs read their weights from HBM, not from the 256 MB Infinity Cache.
+and two quantized copies alternate step by step, so decode-sized runs read
+their weights from HBM rather than from the 256 MB Infinity Cache.
+value = GEMM flops of the step / step time (TFLOP/s, act quant included).
 
-Printed: one JSON line on stdout (value = GEMM TFLOP/s including the act
-quantization, over the whole step), with the roofline of the dominant kernel
-(the large-M GEMM, timed with HIP events on the launch stream inside the
-timed region) and the CPU oracle's rate on a bounded sample.  Per-run
-details go to stderr and into the JSON ``detail`` field.
+The other rows of the path are timed in the same run and reported in
+``detail`` (not in ``value``): DeepSeek-V3-shaped linears with UE8M0 scales,
+the MoE grouped GEMMs (256 experts, Zipf-routed top-8), the NVFP4-style MLP
+(fp4_quant + fp4_group_gemm) with its FP8 attention projection, and weight
+quantization.
 
-    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+``roofline`` is for the dominant kernel, the large-M GEMM (gemm_lds_kernel):
+algorithmic flops over its launches / its summed duration from HIP events
+recorded on the launch stream inside the timed region.  ``traffic`` comes
+from the committed rocprofv3 PMC summary when that summary was taken on the
+current kernel source, else null.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--suites ...]
 """
 
 import argparse
+import hashlib
 import json
 import os
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "block-scaled FP8 GEMM TFLOP/s (incl. act quant) and % of FP8 MFMA/HBM roofline"
-SHAPES = [(4096, 4096), (4096, 6144), (4096, 28672), (14336, 4096)]   # (K, N)
-MS = [1, 16, 128, 2048, 8192]
-LARGE_M = 256            # runs with M above this use the LDS MFMA kernel
+LLAMA_SHAPES = [(4096, 4096), (4096, 6144), (4096, 28672), (14336, 4096)]   # (K, N)
+LLAMA_MS = [1, 16, 128, 2048, 8192]
+DEEPSEEK_SHAPES = [(7168, 1536), (1536, 24576), (7168, 18432), (18432, 7168)]
+DEEPSEEK_MS = [1, 64, 4096]
+LARGE_M = 256             # runs with M above this use the LDS MFMA kernel
 PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 MFMA
+PEAK_F16_TFLOPS = 2500.0  # MI355X dense fp16 / bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_lds_kernel_llama_traffic.txt")
+GEMM_SOURCE = os.path.join(ROOT, "block_scaled_precision_fp8_amd", "csrc", "gemm_fp8.hip")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def algo_bytes(M, N, K, sb=4):
-    """Bytes the linear must move: act quant (read bf16 X, write codes and
-    scales) plus GEMM (read codes and scales of X and W, write bf16 Y)."""
+def source_hash():
+    with open(GEMM_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """bytes per launch of the large-M GEMM from the committed PMC summary,
+    if it was measured on the current kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.lstrip().startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("gemm_fp8.hip sha256[:16]") != source_hash():
+        return None
+    try:
+        return float(kv["hbm bytes per launch (scaled)"])
+    except (KeyError, ValueError):
+        return None
+
+
+def act_bytes(M, K, sb):
+    G = -(-K // 128)
+    return 2 * M * K + M * K + sb * M * G
+
+
+def gemm_bytes(M, N, K, sb):
     G = -(-K // 128)
     NB = -(-N // 128)
-    quant = 2 * M * K + M * K + sb * M * G
-    gemm = M * K + N * K + sb * M * G + sb * NB * G + 2 * M * N
-    return quant, gemm
+    return M * K + N * K + sb * M * G + sb * NB * G + 2 * M * N
+
+
+class Timer:
+    """HIP events on the launch stream around every call in the timed loop."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+        self.ev = {}
+
+    def mark(self, key):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record(self.stream)
+        self.ev.setdefault(key, []).append(e)
+
+    def ms(self, a, b):
+        """mean ms between marks a and b (matched by occurrence)"""
+        ea, eb = self.ev[a], self.ev[b]
+        return sum(x.elapsed_time(y) for x, y in zip(ea, eb)) / len(ea)
+
+
+def run_linears(torch, L, synth, shapes, ms, fmt, workload, steps, warmup, dev, sp):
+    """act quant + block GEMM over a set of (K, N) x M runs; returns per-run
+    details, the step time, the step's flops and the large-M GEMM totals."""
+    sdt = torch.float32 if fmt == 0 else torch.uint8
+    weights = {}
+    for i, (K, N) in enumerate(shapes):
+        copies = []
+        for c in range(2):
+            sigma = 0.02 if workload == "llama" else 0.01
+            wb = synth.device_normal_bf16((N, K), sigma, workload, "w", index=10 * i + c)
+            wq = torch.empty((N, K), dtype=torch.uint8, device=dev)
+            ws = torch.empty((N // 128, K // 128), dtype=sdt, device=dev)
+            L.fp8_quant_weight(wb, wq, ws, scale_fmt=fmt)
+            del wb
+            copies.append((wq, ws))
+        weights[(K, N)] = copies
+    runs = []
+    for i, (K, N) in enumerate(shapes):
+        for M in ms:
+            if workload == "llama":
+                x = synth.device_llama_acts(M, K, index=100 * i + M)
+            else:
+                x = synth.device_deepseek_acts(M, K, index=100 * i + M)
+            need = L.workspace_size(L.OP_BLOCK_GEMM, M, N, K)
+            runs.append(dict(M=M, K=K, N=N, x=x,
+                             xq=torch.empty((M, K), dtype=torch.uint8, device=dev),
+                             xs=torch.empty((M, K // 128), dtype=sdt, device=dev),
+                             y=torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+                             ws=torch.empty(max(need, 16), dtype=torch.uint8, device=dev)))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def step(s, tm=None):
+        for j, r in enumerate(runs):
+            wq, wsc = weights[(r["K"], r["N"])][s & 1]
+            if tm:
+                tm.mark(("q", j))
+            L.fp8_quant_act(r["x"], r["xq"], r["xs"], scale_fmt=fmt, stream=sp)
+            if tm:
+                tm.mark(("g", j))
+            L.fp8_block_gemm(r["xq"], r["xs"], wq, wsc, r["y"], scale_fmt=fmt,
+                             workspace=r["ws"], stream=sp)
+            if tm:
+                tm.mark(("e", j))
+
+    for s in range(warmup):
+        step(s)
+    torch.cuda.synchronize()
+    tm = Timer(torch, stream)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for s in range(steps):
+        step(s, tm)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / steps
+    sb = 4 if fmt == 0 else 1
+    detail, big_flops, big_ms, n_big, flops = [], 0.0, 0.0, 0, 0.0
+    for j, r in enumerate(runs):
+        M, N, K = r["M"], r["N"], r["K"]
+        qm, gm = tm.ms(("q", j), ("g", j)), tm.ms(("g", j), ("e", j))
+        fl = 2.0 * M * N * K
+        flops += fl
+        qb, gb = act_bytes(M, K, sb), gemm_bytes(M, N, K, sb)
+        d = dict(M=M, K=K, N=N, quant_us=round(qm * 1e3, 2), gemm_us=round(gm * 1e3, 2),
+                 linear_tflops=round(fl / ((qm + gm) * 1e-3) / 1e12, 2),
+                 gemm_tflops=round(fl / (gm * 1e-3) / 1e12, 2),
+                 frac_fp8_peak=round(fl / (gm * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+                 quant_gbs=round(qb / (qm * 1e-3) / 1e9, 1),
+                 gemm_gbs=round(gb / (gm * 1e-3) / 1e9, 1),
+                 frac_hbm_gemm=round(gb / (gm * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
+        detail.append(d)
+        if M > LARGE_M:
+            big_flops += fl
+            big_ms += gm
+            n_big += 1
+        log(f"[{workload}] M={M:5d} K={K:5d} N={N:5d} quant {qm*1e3:8.1f} us "
+            f"({d['quant_gbs']:7.1f} GB/s)  gemm {gm*1e3:8.1f} us ({d['gemm_tflops']:7.1f} TF/s, "
+            f"{d['gemm_gbs']:7.1f} GB/s)  linear {d['linear_tflops']:7.1f} TF/s")
+    for r in runs:
+        r.clear()
+    weights.clear()
+    torch.cuda.empty_cache()
+    return dict(detail=detail, ms_step=ms_step, flops=flops, big_flops=big_flops,
+                big_ms=big_ms, n_big=n_big)
+
+
+def run_moe(torch, L, synth, steps, warmup, dev, sp):
+    """MoE grouped GEMMs: gate/up (256 x (7168 -> 4096)) on the routed token
+    rows, down (256 x (2048 -> 7168)) on synthetic expert activations."""
+    E, H, I, TOK, TOPK = 256, 7168, 2048, 4096, 8
+    tok, off = synth.moe_routing(TOK, E, TOPK)
+    T = len(tok)
+    seg = torch.from_numpy(off).to(dev)
+    x = synth.device_normal_bf16((TOK, H), 1.0, "moe", "x")[torch.from_numpy(tok).to(dev)]
+    h = synth.device_normal_bf16((T, I), 1.0, "moe", "h")
+    res = {}
+    counts = (off[1:] - off[:-1])
+    for name, xin, N, K in (("gate_up", x, 2 * I, H), ("down", h, H, I)):
+        wq = torch.empty((E, N, K), dtype=torch.uint8, device=dev)
+        ws = torch.empty((E, N // 128, K // 128), dtype=torch.float32, device=dev)
+        for e in range(E):
+            wb = synth.device_normal_bf16((N, K), 0.02, "moe", "w" if name == "gate_up" else "w2", e)
+            L.fp8_quant_weight(wb, wq[e], ws[e])
+            del wb
+        xq = torch.empty((T, K), dtype=torch.uint8, device=dev)
+        xs = torch.empty((T, K // 128), dtype=torch.float32, device=dev)
+        y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        for _ in range(warmup):
+            L.fp8_quant_act(xin, xq, xs, stream=sp)
+            L.fp8_grouped_gemm(xq, xs, wq, ws, seg, y, stream=sp)
+        torch.cuda.synchronize()
+        tm = Timer(torch, stream)
+        for _ in range(steps):
+            tm.mark("q")
+            L.fp8_quant_act(xin, xq, xs, stream=sp)
+            tm.mark("g")
+            L.fp8_grouped_gemm(xq, xs, wq, ws, seg, y, stream=sp)
+            tm.mark("e")
+        torch.cuda.synchronize()
+        qm, gm = tm.ms("q", "g"), tm.ms("g", "e")
+        fl = 2.0 * T * N * K
+        nb = int((counts > 0).sum())
+        wbytes = nb * (N * K + 4 * (N // 128) * (K // 128))
+        gb = wbytes + T * (K + 4 * (K // 128) + 2 * N)
+        res[name] = dict(T=T, N=N, K=K, experts=E, nonempty=nb, quant_us=round(qm * 1e3, 1),
+                         gemm_us=round(gm * 1e3, 1),
+                         gemm_tflops=round(fl / (gm * 1e-3) / 1e12, 1),
+                         gemm_gbs=round(gb / (gm * 1e-3) / 1e9, 1),
+                         frac_hbm=round(gb / (gm * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
+        log(f"[moe {name}] T={T} N={N} K={K}: quant {qm*1e3:.1f} us, grouped gemm {gm*1e3:.1f} us "
+            f"({res[name]['gemm_tflops']} TF/s, {res[name]['gemm_gbs']} GB/s)")
+        del wq, ws, xq, xs, y
+        torch.cuda.empty_cache()
+    res["rows_per_expert"] = dict(max=int(counts.max()), median=float(np.median(counts)),
+                                  min=int(counts.min()))
+    return res
+
+
+def run_nvfp4(torch, L, synth, steps, warmup, dev, sp):
+    """NVFP4-style MLP (gate/up 12288 -> 28672, down 28672 -> 12288; fp4_quant
+    of the activations + fp4_group_gemm) and the FP8 attention projection
+    (12288 x 12288, 1x128 / 128x128, fp32 scales) at M in {1, 32, 4096}."""
+    HID, INTER = 12288, 28672
+    out = []
+    mats = {}
+    for name, N, K in (("gate_up", INTER, HID), ("down", HID, INTER)):
+        copies = []
+        for c in range(2):
+            wb = synth.device_normal_bf16((N, K), 0.015, "nvfp4", "w", index=N + c)
+            q = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+            s = torch.empty((N, K // 16), dtype=torch.uint8, device=dev)
+            t = torch.empty((1,), dtype=torch.float32, device=dev)
+            L.fp4_quant(wb, q, s, t)
+            del wb
+            copies.append((q, s, t))
+        mats[name] = (N, K, copies)
+    attn = []
+    for c in range(2):
+        wb = synth.device_normal_bf16((HID, HID), 0.015, "nvfp4", "w", index=7 + c)
+        wq = torch.empty((HID, HID), dtype=torch.uint8, device=dev)
+        ws = torch.empty((HID // 128, HID // 128), dtype=torch.float32, device=dev)
+        L.fp8_quant_weight(wb, wq, ws)
+        del wb
+        attn.append((wq, ws))
+    stream = torch.cuda.current_stream()
+    for M in (1, 32, 4096):
+        for name in ("gate_up", "down", "attn_fp8"):
+            if name == "attn_fp8":
+                N, K = HID, HID
+            else:
+                N, K, copies = mats[name]
+            x = synth.device_normal_bf16((M, K), 1.0, "nvfp4", "x", index=M)
+            y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            if name == "attn_fp8":
+                need = L.workspace_size(L.OP_LINEAR, M, N, K)
+                wsp = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+
+                def call(s, tm=None):
+                    if tm:
+                        tm.mark("a")
+                    wq, wsc = attn[s & 1]
+                    L.fp8_linear(x, wq, wsc, y, workspace=wsp, stream=sp)
+                    if tm:
+                        tm.mark("b")
+                        tm.mark("c")
+            else:
+                qx = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+                sx = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
+                tx = torch.empty((1,), dtype=torch.float32, device=dev)
+                wqs = torch.empty(L.workspace_size(L.OP_FP4_QUANT, M, 0, K), dtype=torch.uint8,
+                                  device=dev)
+                need = L.workspace_size(L.OP_FP4_GEMM, M, N, K)
+                wsg = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+
+                def call(s, tm=None):
+                    q, sc, t = copies[s & 1]
+                    if tm:
+                        tm.mark("a")
+                    L.fp4_quant(x, qx, sx, tx, workspace=wqs, stream=sp)
+                    if tm:
+                        tm.mark("b")
+                    L.fp4_group_gemm(qx, sx, tx, q, sc, t, y, workspace=wsg, stream=sp)
+                    if tm:
+                        tm.mark("c")
+            for s in range(warmup):
+                call(s)
+            torch.cuda.synchronize()
+            tm = Timer(torch, stream)
+            for s in range(steps):
+                call(s, tm)
+            torch.cuda.synchronize()
+            qm, gm = tm.ms("a", "b"), tm.ms("b", "c")
+            fl = 2.0 * M * N * K
+            if name == "attn_fp8":
+                tot = qm
+                byt = act_bytes(M, K, 4) + gemm_bytes(M, N, K, 4)
+                d = dict(M=M, K=K, N=N, kind="fp8_linear", us=round(tot * 1e3, 2),
+                         tflops=round(fl / (tot * 1e-3) / 1e12, 2),
+                         gbs=round(byt / (tot * 1e-3) / 1e9, 1))
+            else:
+                wb = N * (K // 2 + K // 16)
+                gb = wb + M * (K // 2 + K // 16) + 2 * M * N
+                d = dict(M=M, K=K, N=N, kind=f"fp4_{name}", quant_us=round(qm * 1e3, 2),
+                         gemm_us=round(gm * 1e3, 2),
+                         gemm_tflops=round(fl / (gm * 1e-3) / 1e12, 2),
+                         frac_f16_peak=round(fl / (gm * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4),
+                         gemm_gbs=round(gb / (gm * 1e-3) / 1e9, 1),
+                         frac_hbm=round(gb / (gm * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
+            out.append(d)
+            log(f"[nvfp4] {d}")
+    return out
+
+
+def run_wquant(torch, L, synth, steps, warmup, dev, sp):
+    """Weight quantization (load-time step) of the 28672 x 4096 weight."""
+    N, K = 28672, 4096
+    wb = synth.device_normal_bf16((N, K), 0.02, "llama", "w", index=99)
+    wq = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    ws = torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        L.fp8_quant_weight(wb, wq, ws, stream=sp)
+    torch.cuda.synchronize()
+    tm = Timer(torch, stream)
+    for _ in range(steps):
+        tm.mark("a")
+        L.fp8_quant_weight(wb, wq, ws, stream=sp)
+        tm.mark("b")
+    torch.cuda.synchronize()
+    m = tm.ms("a", "b")
+    byt = 3 * N * K + 4 * (N // 128) * (K // 128)
+    return dict(N=N, K=K, us=round(m * 1e3, 1), gbs=round(byt / (m * 1e-3) / 1e9, 1),
+                frac_hbm=round(byt / (m * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
 
 
 def cpu_baseline(budget_s=12.0):
     """The oracle (numpy, fp64 accumulation) on a bounded sample: 256 tokens
-    against the first 2048 output features of each of the four shapes, act
-    quantization + block GEMM, repeated until the time budget is used."""
+    against the first 2048 output features of each of the four Llama shapes,
+    act quantization + block GEMM, repeated until the time budget is used."""
     import numpy as np
     from block_scaled_precision_fp8_amd import synth
     from oracle import quant as Q, gemm as G
@@ -66,7 +382,7 @@ def cpu_baseline(budget_s=12.0):
         blas_threads = os.cpu_count() or 1
     Ms, Ns = 256, 2048
     cases = []
-    for i, (K, N) in enumerate(SHAPES):
+    for i, (K, N) in enumerate(LLAMA_SHAPES):
         x = synth.llama_acts(Ms, K, seed=100 + i)
         w = synth.normal_bf16((Ns, K), 0.02, "llama", "w", index=i, seed=100)
         wq, ws = Q.quant_weight(w)            # load-time step, not timed
@@ -97,6 +413,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--suites", default="deepseek,moe,nvfp4,wquant",
+                    help="extra rows timed for `detail` (comma list, or 'none')")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (a known-size "
+                         "kernel for calibrating rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -104,108 +425,50 @@ def main():
               "part of this library (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
     from block_scaled_precision_fp8_amd import lib as L, synth
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     L.load()
+    sp = torch.cuda.current_stream().cuda_stream
+    if args.copy_calib_mib:
+        n = args.copy_calib_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
-    # ---- weights: quantized once (load-time), two copies per shape
-    weights = {}
-    for i, (K, N) in enumerate(SHAPES):
-        copies = []
-        for c in range(2):
-            wb = synth.device_normal_bf16((N, K), 0.02, "llama", "w", index=10 * i + c)
-            wq = torch.empty((N, K), dtype=torch.uint8, device=dev)
-            ws = torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev)
-            L.fp8_quant_weight(wb, wq, ws)
-            del wb
-            copies.append((wq, ws))
-        weights[(K, N)] = copies
-    # ---- activations and outputs per run
-    runs = []
-    for i, (K, N) in enumerate(SHAPES):
-        for M in MS:
-            x = synth.device_llama_acts(M, K, index=100 * i + M)
-            xq = torch.empty((M, K), dtype=torch.uint8, device=dev)
-            xs = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
-            y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-            need = L.workspace_size(L.OP_BLOCK_GEMM, M, N, K)
-            ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
-            runs.append(dict(M=M, K=K, N=N, x=x, xq=xq, xs=xs, y=y, ws=ws))
-    torch.cuda.synchronize()
-
-    stream = torch.cuda.current_stream()
-    sp = stream.cuda_stream
-
-    def step(s, evs=None):
-        for j, r in enumerate(runs):
-            wq, wsc = weights[(r["K"], r["N"])][s & 1]
-            if evs is not None:
-                evs[j][0].record(stream)
-            L.fp8_quant_act(r["x"], r["xq"], r["xs"], stream=sp)
-            if evs is not None:
-                evs[j][1].record(stream)
-            L.fp8_block_gemm(r["xq"], r["xs"], wq, wsc, r["y"], workspace=r["ws"], stream=sp)
-            if evs is not None:
-                evs[j][2].record(stream)
-
-    for s in range(args.warmup):
-        step(s)
-    torch.cuda.synchronize()
-
-    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in runs]
-           for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for s in range(args.steps):
-        step(s, evs[s])
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms_per_step = total_ms / args.steps
-
-    flops_step = sum(2.0 * r["M"] * r["N"] * r["K"] for r in runs)
-    value = flops_step / (ms_per_step * 1e-3) / 1e12
-
-    # ---- per-run and per-kernel times (HIP events on the launch stream)
-    detail = []
-    big_flops = big_ms = 0.0
-    for j, r in enumerate(runs):
-        q = np.array([evs[s][j][0].elapsed_time(evs[s][j][1]) for s in range(args.steps)])
-        g = np.array([evs[s][j][1].elapsed_time(evs[s][j][2]) for s in range(args.steps)])
-        M, N, K = r["M"], r["N"], r["K"]
-        fl = 2.0 * M * N * K
-        qb, gb = algo_bytes(M, N, K)
-        qm, gm = float(np.mean(q)), float(np.mean(g))
-        d = dict(M=M, K=K, N=N, quant_us=round(qm * 1e3, 2), gemm_us=round(gm * 1e3, 2),
-                 linear_tflops=round(fl / ((qm + gm) * 1e-3) / 1e12, 2),
-                 gemm_tflops=round(fl / (gm * 1e-3) / 1e12, 2),
-                 quant_gbs=round(qb / (qm * 1e-3) / 1e9, 1),
-                 gemm_gbs=round(gb / (gm * 1e-3) / 1e9, 1),
-                 linear_gbs=round((qb + gb) / ((qm + gm) * 1e-3) / 1e9, 1))
-        d["frac_fp8_peak"] = round(d["gemm_tflops"] / PEAK_FP8_TFLOPS, 4)
-        d["frac_hbm_gemm"] = round(d["gemm_gbs"] / PEAK_HBM_GBS, 4)
-        detail.append(d)
-        if M > LARGE_M:
-            big_flops += fl * args.steps
-            big_ms += float(np.sum(g))
-        log(f"M={M:5d} K={K:5d} N={N:5d}  quant {qm*1e3:8.1f} us ({d['quant_gbs']:7.1f} GB/s)"
-            f"  gemm {gm*1e3:8.1f} us ({d['gemm_tflops']:7.1f} TF/s, {d['gemm_gbs']:7.1f} GB/s)"
-            f"  linear {d['linear_tflops']:7.1f} TF/s")
-
-    achieved = big_flops / (big_ms * 1e-3) / 1e12
-    n_big = sum(1 for r in runs if r["M"] > LARGE_M)
+    r = run_linears(torch, L, synth, LLAMA_SHAPES, LLAMA_MS, 0, "llama", args.steps,
+                    args.warmup, dev, sp)
+    value = r["flops"] / (r["ms_step"] * 1e-3) / 1e12
+    achieved = r["big_flops"] / (r["big_ms"] * 1e-3) / 1e12
+    traffic = read_traffic()
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
-                "traffic": None,
-                "kernel": "gemm_lds_kernel (fp32 scales), the large-M block-scaled GEMM",
-                "launches_per_step": n_big,
-                "avg_launch_us": round(big_ms / (args.steps * n_big) * 1e3, 2)}
+                "traffic": traffic,
+                "kernel": "gemm_lds_kernel<0,2,4,64,64,false> (fp32 scales), large-M "
+                          "block-scaled GEMM",
+                "launches_per_step": r["n_big"],
+                "avg_launch_us": round(r["big_ms"] / r["n_big"] * 1e3, 2),
+                "algorithmic_gflop_per_launch": round(r["big_flops"] / r["n_big"] / 1e9, 2)}
+    detail = {"llama": r["detail"]}
+    suites = [] if args.suites == "none" else args.suites.split(",")
+    if "deepseek" in suites:
+        d = run_linears(torch, L, synth, DEEPSEEK_SHAPES, DEEPSEEK_MS, 1, "deepseek",
+                        max(5, args.steps // 2), 2, dev, sp)
+        detail["deepseek_ue8m0"] = d["detail"]
+        detail["deepseek_ue8m0_large_m_tflops"] = round(d["big_flops"] / (d["big_ms"] * 1e-3)
+                                                        / 1e12, 1)
+    if "moe" in suites:
+        detail["moe"] = run_moe(torch, L, synth, max(5, args.steps // 2), 2, dev, sp)
+    if "nvfp4" in suites:
+        detail["nvfp4_mlp_fp8_attn"] = run_nvfp4(torch, L, synth, max(5, args.steps // 2), 2,
+                                                 dev, sp)
+    if "wquant" in suites:
+        detail["weight_quant"] = run_wquant(torch, L, synth, 10, 2, dev, sp)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -214,14 +477,14 @@ def main():
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["ms_step"], 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp8_e4m3 (fp32 accumulate)", "data": "synthetic",
         "config": {"workload": "Llama-3-8B-shaped FP8 linears: (K,N) in {(4096,4096),"
                                "(4096,6144),(4096,28672),(14336,4096)} x M in "
                                "{1,16,128,2048,8192}; 1x128 act groups, 128x128 weight "
                                "blocks, fp32 scales, bf16 out",
-                   "runs_per_step": len(runs), "flops_per_step": flops_step},
+                   "runs_per_step": 20, "flops_per_step": r["flops"]},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "detail": detail,
