@@ -17,8 +17,9 @@ the MoE grouped GEMMs (256 experts, Zipf-routed top-8), the NVFP4-style MLP
 (fp4_quant + fp4_group_gemm) with its FP8 attention projection, and weight
 quantization.
 
-``roofline`` is for the dominant kernel, the large-M GEMM (gemm_lds_kernel):
-algorithmic flops over its launches / its summed duration from HIP events
+``roofline`` is for the dominant kernel, the large-M GEMM with 256 x 256 tiles
+(gemm_lds_kernel, every run the library sends to it; bsfp8_gemm_kernel says
+which): algorithmic flops over its launches / its summed duration from HIP events
 recorded on the launch stream inside the timed region.  ``traffic`` comes
 from the committed rocprofv3 PMC summary when that summary was taken on the
 current kernel source, else null.
@@ -44,7 +45,6 @@ LLAMA_SHAPES = [(4096, 4096), (4096, 6144), (4096, 28672), (14336, 4096)]   # (K
 LLAMA_MS = [1, 16, 128, 2048, 8192]
 DEEPSEEK_SHAPES = [(7168, 1536), (1536, 24576), (7168, 18432), (18432, 7168)]
 DEEPSEEK_MS = [1, 64, 4096]
-LARGE_M = 256             # runs with M above this use the LDS MFMA kernel
 PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 MFMA
 PEAK_F16_TFLOPS = 2500.0  # MI355X dense fp16 / bf16 MFMA
 PEAK_HBM_GBS = 8000.0
@@ -182,7 +182,7 @@ def run_linears(torch, L, synth, shapes, ms, fmt, workload, steps, warmup, dev, 
                  gemm_gbs=round(gb / (gm * 1e-3) / 1e9, 1),
                  frac_hbm_gemm=round(gb / (gm * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
         detail.append(d)
-        if M > LARGE_M:
+        if L.gemm_kernel(M, N) == L.GEMM_TILE_256x256:
             big_flops += fl
             big_ms += gm
             n_big += 1
@@ -449,8 +449,8 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
                 "traffic": traffic,
-                "kernel": "gemm_lds_kernel<0,2,4,64,64,false> (fp32 scales), large-M "
-                          "block-scaled GEMM",
+                "kernel": "gemm_lds_kernel<0,4,2,64,128,false> (fp32 scales, 256x256 "
+                          "tiles), large-M block-scaled GEMM",
                 "launches_per_step": r["n_big"],
                 "avg_launch_us": round(r["big_ms"] / r["n_big"] * 1e3, 2),
                 "algorithmic_gflop_per_launch": round(r["big_flops"] / r["n_big"] / 1e9, 2)}
@@ -460,7 +460,7 @@ def main():
         d = run_linears(torch, L, synth, DEEPSEEK_SHAPES, DEEPSEEK_MS, 1, "deepseek",
                         max(5, args.steps // 2), 2, dev, sp)
         detail["deepseek_ue8m0"] = d["detail"]
-        detail["deepseek_ue8m0_large_m_tflops"] = round(d["big_flops"] / (d["big_ms"] * 1e-3)
+        detail["deepseek_ue8m0_tile256_tflops"] = round(d["big_flops"] / (d["big_ms"] * 1e-3)
                                                         / 1e12, 1)
     if "moe" in suites:
         detail["moe"] = run_moe(torch, L, synth, max(5, args.steps // 2), 2, dev, sp)

@@ -93,6 +93,7 @@ struct GemmArgs {
 };
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int gemm_kind(int64_t M, int64_t N);   // a bsfp8_gemm_kind
 size_t linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
 size_t grouped_workspace_bytes(int64_t T, int64_t N, int64_t K, int E);
 hipError_t launch_block_gemm(const GemmArgs& a, hipStream_t s);

@@ -73,6 +73,14 @@ typedef enum {
   BSFP8_OP_FP4_GEMM = 4
 } bsfp8_op;
 
+/* Kernels fp8_block_gemm / fp8_linear choose between (bsfp8_gemm_kernel). */
+typedef enum {
+  BSFP8_GEMM_NONE = 0,          /* empty problem: nothing is launched          */
+  BSFP8_GEMM_STREAM = 1,        /* M <= 128: weight-streaming split-K kernel   */
+  BSFP8_GEMM_TILE_128x256 = 2,  /* LDS-staged MFMA kernel, 128 x 256 tiles     */
+  BSFP8_GEMM_TILE_256x256 = 3   /* LDS-staged MFMA kernel, 256 x 256 tiles     */
+} bsfp8_gemm_kind;
+
 /* Library version (major * 10000 + minor * 100 + patch). */
 BSFP8_API int32_t bsfp8_version(void);
 
@@ -238,6 +246,14 @@ BSFP8_API int32_t fp4_group_gemm(const void* xq4, const void* x_gscale,
  */
 BSFP8_API size_t bsfp8_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K,
                             int32_t E);
+
+/*
+ * Which kernel (a bsfp8_gemm_kind) fp8_block_gemm and fp8_linear launch for
+ * an M x N output; the choice depends on M and N only (the grouped GEMM
+ * always uses 128 x 256 tiles).  Host-only, touches no device.  Returns -1
+ * for negative sizes.
+ */
+BSFP8_API int32_t bsfp8_gemm_kernel(int64_t M, int64_t N);
 
 #ifdef __cplusplus
 }

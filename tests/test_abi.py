@@ -146,3 +146,21 @@ def test_fp4_argument_checks():
 def test_workspace_size_unknown_op():
     assert L.workspace_size(99, 1, 1, 16) == 2**64 - 1
     assert L.load().bsfp8_workspace_size(0, -1, 1, 16, 0) == 2**64 - 1
+
+
+def test_gemm_kernel_choice():
+    """Host-side kernel choice: split-K weight streaming up to M = 128, then
+    the 256 x 256 tile whenever it fills the CUs in fewer weighted rounds than
+    the 128 x 256 tile (256 CUs, per-tile time 4 : 3)."""
+    k = L.gemm_kernel
+    assert k(0, 256) == L.GEMM_NONE and k(5, 0) == L.GEMM_NONE
+    assert L.load().bsfp8_gemm_kernel(-1, 8) == -1
+    for M in (1, 16, 128):
+        assert k(M, 28672) == L.GEMM_STREAM
+    assert k(129, 256) == L.GEMM_TILE_128x256
+    assert k(2048, 4096) == L.GEMM_TILE_128x256      # 128 big tiles would idle half the CUs
+    assert k(4096, 1536) == L.GEMM_TILE_128x256
+    assert k(2048, 6144) == L.GEMM_TILE_256x256      # 192 big tiles: one round vs two
+    for N in (4096, 6144, 28672):
+        assert k(8192, N) == L.GEMM_TILE_256x256
+    assert k(4100, 4104) == L.GEMM_TILE_256x256      # the ragged big-tile parity case

@@ -44,9 +44,13 @@ def _gemm_dev(d, M, N, bias_bits=None, fmt=0):
     (64, 256, 2048, False), (128, 384, 640, True),
     (130, 520, 640, False), (300, 1000, 1040, True), (256, 256, 128, False),
     (513, 768, 2048, True), (1024, 1024, 1024, False),
+    (4100, 4104, 384, True),      # enough tiles for the 256 x 256 tile, ragged in M and N
 ])
 def test_block_gemm_parity(M, N, K, bias, fmt):
     say(f"block gemm M={M} N={N} K={K} bias={bias} fmt={fmt}")
+    if (M, N) == (4100, 4104):
+        from block_scaled_precision_fp8_amd import lib as L
+        assert L.gemm_kernel(M, N) == L.GEMM_TILE_256x256
     x = synth.deepseek_acts(M, K, seed=M) if fmt else synth.llama_acts(M, K, seed=M)
     w = synth.normal_bf16((N, K), 0.02, "llama", "w", seed=N)
     b = synth.normal_bf16((N,), 0.5, "llama", "bias", seed=N) if bias else None
@@ -64,6 +68,7 @@ def test_block_gemm_parity(M, N, K, bias, fmt):
     (2048, 4096, 28672, 0, "llama"), (16, 14336, 4096, 0, "llama"),
     (128, 4096, 6144, 0, "llama"), (4096, 7168, 18432, 1, "deepseek"),
     (1, 18432, 7168, 1, "deepseek"), (64, 1536, 24576, 1, "deepseek"),
+    (8192, 14336, 4096, 0, "llama"),
 ])
 def test_block_gemm_full_size_sampled(M, K, N, fmt, gen):
     """Full-size shapes in the launch configuration the bench uses; the
