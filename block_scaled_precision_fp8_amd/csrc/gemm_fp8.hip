@@ -342,21 +342,28 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
     v8i bx[MI];
 #pragma unroll
     for (int j = 0; j < MI; ++j) bx[j] = read_frag(sx + j * 16 * kRowBytes, ch0, ch1);
-    // W fragments: one 16-row subtile at a time, a group of NG subtiles
-    // between scheduling fences (bounds the live fragments)
-    constexpr int NG = (MI * NI >= 32) ? 2 : NI;
-    static_for<NI / NG>([&](auto gc) {
-      constexpr int g = decltype(gc)::value;
-      v8i aw[NG];
+    // W fragments in groups of NG 16-row subtiles, read one group ahead:
+    // group g + 1 is in flight while the MFMAs of group g run.  Scheduling
+    // fences keep that order (and bound the live fragments).
+    constexpr int NG = 2;
+    constexpr int NGR = NI / NG;
+    v8i aw[2][NG];
 #pragma unroll
-      for (int ii = 0; ii < NG; ++ii)
-        aw[ii] = read_frag(swl + (g * NG + ii) * 16 * kRowBytes, ch0, ch1);
+    for (int ii = 0; ii < NG; ++ii) aw[0][ii] = read_frag(swl + ii * 16 * kRowBytes, ch0, ch1);
+    static_for<NGR>([&](auto gc) {
+      constexpr int g = decltype(gc)::value;
+      if constexpr (g + 1 < NGR) {
+#pragma unroll
+        for (int ii = 0; ii < NG; ++ii)
+          aw[(g + 1) & 1][ii] = read_frag(swl + ((g + 1) * NG + ii) * 16 * kRowBytes, ch0, ch1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ii = 0; ii < NG; ++ii)
 #pragma unroll
         for (int j = 0; j < MI; ++j)
-          acc[g * NG + ii][j] = mfma_step<FMT>(acc[g * NG + ii][j], aw[ii], bx[j], sa[j], sw);
-      if constexpr (NG < NI) __builtin_amdgcn_sched_barrier(0);
+          acc[g * NG + ii][j] = mfma_step<FMT>(acc[g * NG + ii][j], aw[g & 1][ii], bx[j], sa[j], sw);
+      __builtin_amdgcn_sched_barrier(0);
     });
   };
 
