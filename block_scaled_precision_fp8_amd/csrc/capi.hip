@@ -55,12 +55,16 @@ int32_t hip_status(hipError_t e) {
 }
 
 // shared checks of the FP8 GEMM operand set
+// 32-bit in-tile byte offsets of the GEMM kernels (256 rows x K)
+constexpr int64_t kMaxGemmK = int64_t(1) << 22;
+
 int32_t check_gemm(const void* xq, const void* xs, const void* wq, const void* ws,
                    const void* bias, const void* y, int64_t M, int64_t N, int64_t K,
                    int32_t bn, int32_t bk, int32_t fmt) {
   if (M < 0 || N < 0 || K < 0) return BSFP8_EINVAL;
   if (!fits_i32(M) || !fits_i32(N) || !fits_i32(K)) return BSFP8_EINVAL;
   if (K % 16 != 0 || N % 8 != 0) return BSFP8_EINVAL;
+  if (K > kMaxGemmK) return BSFP8_ENOTSUP;
   if (!valid_fmt(fmt)) return BSFP8_EINVAL;
   int32_t r = check_blocks(bn, bk);
   if (r != BSFP8_OK) return r;

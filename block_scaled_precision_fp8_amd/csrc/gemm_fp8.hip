@@ -204,10 +204,10 @@ __device__ __forceinline__ v8i read_frag(const uint8_t* __restrict__ row, int ch
 // scale block).  Operands go global -> LDS directly (buffer_load ... lds,
 // 16 bytes per lane), double-buffered; in LDS every 128-byte row keeps
 // its eight 16-byte chunks XOR-swizzled by ((row >> 1) & 7).  The LDS has
-// 64 four-byte banks (two 128-byte rows per sweep) and a ds_read_b128 serves
-// 16 lanes at a time; a fragment read has 16 lanes on 16 consecutive rows
-// and one logical chunk, so (row parity, physical chunk) must be distinct
-// over any 16 consecutive rows -- which this swizzle gives.  Each wave
+// 64 four-byte banks (two 128-byte rows per sweep); a fragment read has 16
+// lanes on 16 consecutive rows and one logical chunk, so (row parity,
+// physical chunk) must be distinct over any 16 consecutive rows -- which
+// this swizzle gives.  Each wave
 // computes a WM (m) x WN (n) tile with 16x16x128 MFMAs: W is the A operand,
 // X the B operand.
 template <int FMT, int WAVES_M, int WAVES_N, int WM, int WN, bool GROUPED>
@@ -308,12 +308,17 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
     }
   };
 
-  // fragment: 16 rows x 128 codes; lane (l16, g4) takes row l16, bytes
-  // [32 g4, 32 g4 + 32) -- the same K split for both operands.  Fragment
-  // rows start at multiples of 16, so a row's swizzle ((row >> 1) & 7) is
-  // the lane's (l16 >> 1): two per-lane chunk offsets serve every fragment.
-  const int ch0 = ((2 * g4) ^ (l16 >> 1)) << 4;
-  const int ch1 = ((2 * g4 + 1) ^ (l16 >> 1)) << 4;
+  // fragment: 16 rows x 128 codes; lane (l16, g4) takes row l16 and the
+  // 16-byte chunks g4 and g4 + 4 of the K block as its 32 MFMA bytes.  The
+  // same permutation of K on both operands leaves every dot product the
+  // same, and all four 32-element scale sub-blocks of a row carry the one
+  // block scale.  With chunks {0,1,2,3} then {4,5,6,7} across the four
+  // lane groups the fragment reads have no LDS bank conflicts; chunks
+  // {0,2,4,6} conflict two ways.  Fragment rows start at multiples of 16,
+  // so a row's swizzle ((row >> 1) & 7) is the lane's (l16 >> 1): two
+  // per-lane chunk offsets serve every fragment.
+  const int ch0 = (g4 ^ (l16 >> 1)) << 4;
+  const int ch1 = ((g4 + 4) ^ (l16 >> 1)) << 4;
   auto frag = [&](const uint8_t* row) -> v8i {
     return join(*(const uint4*)(row + ch0), *(const uint4*)(row + ch1));
   };

@@ -153,8 +153,9 @@ BSFP8_API int32_t fp8_quant_weight(const void* w, int64_t N, int64_t K, int64_t 
  *                     bsfp8_workspace_size(BSFP8_OP_BLOCK_GEMM, M, N, K, 0)
  *                     bytes (may be NULL when that size is 0); contents on
  *                     entry are ignored, on exit undefined.
- * Errors: EINVAL (dims < 0, K % 16, null required pointers, bad enum,
- * misalignment); ENOTSUP (block sizes other than 128); ENOSPC.
+ * Errors: EINVAL (dims < 0, K % 16, N % 8, null required pointers, bad
+ * enum, misalignment); ENOTSUP (block sizes other than 128, K > 2^22);
+ * ENOSPC.  fp8_linear and fp8_grouped_gemm share these limits.
  */
 BSFP8_API int32_t fp8_block_gemm(const void* xq, const void* x_scale, const void* wq,
                        const void* w_scale_inv, const void* bias, void* y,

@@ -92,6 +92,7 @@ def _gemm(**kw):
     (dict(fmt=3), L.EINVAL), (dict(bn=64), L.ENOTSUP), (dict(bk=0), L.EINVAL),
     (dict(y=None), L.EINVAL), (dict(wq=None), L.EINVAL), (dict(b=MIS), L.EINVAL),
     (dict(M=0), L.OK), (dict(N=0), L.EINVAL), (dict(M=2**31), L.EINVAL),
+    (dict(K=2**22 + 16), L.ENOTSUP),
 ])
 def test_block_gemm_argument_checks(kw, code):
     assert _gemm(**kw) == code
