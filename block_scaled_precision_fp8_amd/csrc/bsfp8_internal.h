@@ -67,6 +67,40 @@ __device__ __forceinline__ int ue8m0_exp(float amax) {
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
+// Activation group codec (1 x 128 groups), one definition for every kernel
+// that quantizes activations so their codes and scales agree bit for bit.
+//   FLOAT: s = fl32(amax / 448) (1 for amax == 0), code = E4M3(fl32(x / s))
+//   UE8M0: e = ue8m0_exp(amax), code = E4M3(x * 2^-e) (exact scaling)
+__device__ __forceinline__ float act_scale_f32(float amax) {
+  return (amax == 0.0f) ? 1.0f : amax / kE4M3Max;
+}
+template <int FMT>
+__device__ __forceinline__ uint32_t act_encode4(float a, float b, float c, float d, float s,
+                                                int e) {
+  if (FMT == 0) return e4m3x4(a / s, b / s, c / s, d / s);
+  return e4m3x4(ldexpf(a, -e), ldexpf(b, -e), ldexpf(c, -e), ldexpf(d, -e));
+}
+
+// fl32(x / s) from r = fl32(1 / s) in three operations (Markstein's
+// correction step: q = RN(x r), the residual x - q s is exact with an FMA,
+// and RN(q + residual r) is the correctly rounded quotient when r is the
+// correctly rounded reciprocal and no intermediate underflows).  Quotients
+// small enough to underflow are far below the smallest E4M3 subnormal and
+// encode to a signed zero either way, so the codes equal those of x / s.
+__device__ __forceinline__ float div_by_rcp(float x, float s, float r) {
+  const float q = x * r;
+  const float res = fmaf(-q, s, x);
+  return fmaf(res, r, q);
+}
+template <int FMT>
+__device__ __forceinline__ uint32_t act_encode4_rcp(float a, float b, float c, float d,
+                                                    float s, float r, int e) {
+  if (FMT == 0)
+    return e4m3x4(div_by_rcp(a, s, r), div_by_rcp(b, s, r), div_by_rcp(c, s, r),
+                  div_by_rcp(d, s, r));
+  return e4m3x4(ldexpf(a, -e), ldexpf(b, -e), ldexpf(c, -e), ldexpf(d, -e));
+}
+
 // ---------------------------------------------------------------- host
 
 hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
@@ -95,6 +129,7 @@ struct GemmArgs {
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 int gemm_kind(int64_t M, int64_t N);   // a bsfp8_gemm_kind
 size_t linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
+bool linear_fused(int64_t M, int64_t N);   // fp8_linear quantizes inside the GEMM
 size_t grouped_workspace_bytes(int64_t T, int64_t N, int64_t K, int E);
 hipError_t launch_block_gemm(const GemmArgs& a, hipStream_t s);
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t s);

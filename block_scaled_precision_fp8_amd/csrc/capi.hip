@@ -188,6 +188,17 @@ int32_t fp8_linear(const void* x, int64_t ldx, const void* wq, const void* w_sca
   if (need && (!workspace || !al16(workspace))) return BSFP8_EINVAL;
   r = check_device(stream);
   if (r != BSFP8_OK) return r;
+  hipStream_t st = (hipStream_t)stream;
+  GemmArgs a{};
+  a.wq = (const uint8_t*)wq; a.ws = w_scale_inv;
+  a.bias = (const uint16_t*)bias; a.y = (uint16_t*)y; a.M = M; a.N = N; a.K = K;
+  a.fmt = scale_fmt;
+  if (linear_fused(M, N)) {
+    // one launch: the decode kernel quantizes the activations itself
+    if (!al16(x)) return BSFP8_EINVAL;
+    a.x_bf16 = (const uint16_t*)x; a.ldx = ldx;
+    return hip_status(launch_block_gemm(a, st));
+  }
   // workspace: [xq M*K][x_scale M*G*4][gemm workspace], 256-byte aligned parts
   const int64_t G = (K + 127) / 128;
   auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
@@ -195,13 +206,9 @@ int32_t fp8_linear(const void* x, int64_t ldx, const void* wq, const void* w_sca
   uint8_t* xq = ws;
   void* xs = ws + up((size_t)M * K);
   void* gw = ws + up((size_t)M * K) + up((size_t)M * G * 4);
-  hipStream_t st = (hipStream_t)stream;
   hipError_t e = launch_quant_act((const uint16_t*)x, M, K, ldx, scale_fmt, xq, xs, st);
   if (e != hipSuccess) return BSFP8_EHIP;
-  GemmArgs a{};
-  a.xq = xq; a.xs = xs; a.wq = (const uint8_t*)wq; a.ws = w_scale_inv;
-  a.bias = (const uint16_t*)bias; a.y = (uint16_t*)y; a.M = M; a.N = N; a.K = K;
-  a.fmt = scale_fmt; a.workspace = gw;
+  a.xq = xq; a.xs = xs; a.workspace = gw;
   a.workspace_bytes = workspace_bytes - (size_t)((uint8_t*)gw - ws);
   return hip_status(launch_block_gemm(a, st));
 }

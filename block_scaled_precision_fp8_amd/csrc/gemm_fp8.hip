@@ -507,6 +507,115 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   store_out4(y, N, m, n, v4f{s.x, s.y, s.z, s.w}, bias);
 }
 
+// ------------------------------------------------------------------------
+// Decode kernel (M <= 16): one workgroup owns 16 weight rows over the whole
+// K range and its kDecodeWaves waves take the K blocks round-robin.  Each
+// lane streams its 32 weight bytes per block straight from HBM with
+// kDecodeDepth blocks of loads in flight, the activation fragment (one
+// token row per lane column) comes from L2, and the waves' partial 16 x 16
+// tiles are summed through LDS: one launch, no workspace.  FUSED: the 1x128
+// activation quantization runs in the same launch -- each lane encodes its
+// 32 activations of the block with the group amax gathered from the four
+// lanes that share its row, to the codes fp8_quant_act writes (the fp32
+// division by the scale done as a multiply by the correctly rounded
+// reciprocal plus one exact correction).  Every workgroup quantizes all of
+// X, so the fused form is used up to kDecodeFusedMaxN outputs only.
+// ------------------------------------------------------------------------
+constexpr int kDecodeWaves = 8;
+constexpr int kDecodeDepth = 4;
+
+template <int FMT, bool FUSED>
+__global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
+    const uint8_t* __restrict__ xq, const void* __restrict__ xs,
+    const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ wq,
+    const void* __restrict__ wsc, const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
+    int M, int64_t N, int64_t K) {
+  __shared__ v4f red[kDecodeWaves][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int64_t nrow = n0 + l16;
+  const bool nvalid = nrow < N;
+  const bool mvalid = l16 < M;             // this lane's token row (B column)
+  const int KB = (int)((K + 127) / 128);
+  const int64_t nblk = n0 >> 7;
+  const uint8_t* wrow = wq + nrow * K;
+
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  for (int kb0 = wave; kb0 < KB; kb0 += kDecodeWaves * kDecodeDepth) {
+    uint4 wa[kDecodeDepth], wb[kDecodeDepth];
+#pragma unroll
+    for (int u = 0; u < kDecodeDepth; ++u) {
+      const int kb = kb0 + u * kDecodeWaves;
+      const int64_t k = (int64_t)kb * 128 + g4 * 32;
+      wa[u] = make_uint4(0, 0, 0, 0);
+      wb[u] = make_uint4(0, 0, 0, 0);
+      if (kb < KB && nvalid) {
+        if (k < K) wa[u] = ld_stream16(wrow + k);
+        if (k + 16 < K) wb[u] = ld_stream16(wrow + k + 16);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kDecodeDepth; ++u) {
+      const int kb = kb0 + u * kDecodeWaves;
+      if (kb >= KB) break;
+      const int64_t k = (int64_t)kb * 128 + g4 * 32;
+      v8i bx;
+      float sa;
+      if constexpr (FUSED) {
+        uint4 v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[i] = make_uint4(0, 0, 0, 0);
+          if (mvalid && k + 8 * i < K) v[i] = *(const uint4*)(x + (int64_t)l16 * ldx + k + 8 * i);
+        }
+        float f[32];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          f[8 * i + 0] = bf16_lo(v[i].x); f[8 * i + 1] = bf16_hi(v[i].x);
+          f[8 * i + 2] = bf16_lo(v[i].y); f[8 * i + 3] = bf16_hi(v[i].y);
+          f[8 * i + 4] = bf16_lo(v[i].z); f[8 * i + 5] = bf16_hi(v[i].z);
+          f[8 * i + 6] = bf16_lo(v[i].w); f[8 * i + 7] = bf16_hi(v[i].w);
+        }
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(f[i]));
+        amax = fmaxf(amax, __shfl_xor(amax, 16));
+        amax = fmaxf(amax, __shfl_xor(amax, 32));
+        const float s = FMT == 0 ? act_scale_f32(amax) : 0.0f;
+        const float r = FMT == 0 ? 1.0f / s : 0.0f;
+        const int e = FMT == 0 ? 0 : ue8m0_exp(amax);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          bx[i] = (int)act_encode4_rcp<FMT>(f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3], s,
+                                            r, e);
+        sa = FMT == 0 ? s : __int_as_float(e + 127);
+      } else {
+        uint4 xa = make_uint4(0, 0, 0, 0), xb = make_uint4(0, 0, 0, 0);
+        sa = (FMT == 0) ? 0.f : __int_as_float(127);
+        if (mvalid) {
+          if (k < K) xa = *(const uint4*)(xq + (int64_t)l16 * K + k);
+          if (k + 16 < K) xb = *(const uint4*)(xq + (int64_t)l16 * K + k + 16);
+          sa = load_scale<FMT>(xs, (int64_t)l16 * KB + kb);
+        }
+        bx = join(xa, xb);
+      }
+      const float sw = load_scale<FMT>(wsc, nblk * KB + kb);
+      acc = mfma_step<FMT>(acc, join(wa[u], wb[u]), bx, sa, sw);
+    }
+  }
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+  v4f sum = red[0][lane];
+#pragma unroll
+  for (int w = 1; w < kDecodeWaves; ++w) sum += red[w][lane];
+  // lane holds n = n0 + 4 g4 + {0..3} for token m = l16
+  const int64_t n = n0 + 4 * g4;
+  if (mvalid && n < N) store_out4(y, N, l16, n, sum, bias);
+}
+
 // Explicit instantiations of every tile configuration the dispatcher below
 // can launch (the host pass does not always emit launch stubs for kernel
 // templates that are only instantiated implicitly).
@@ -528,6 +637,8 @@ BSFP8_INST_ALL(1)
 // host side
 // ------------------------------------------------------------------------
 constexpr int64_t kStreamMaxM = 128;
+constexpr int64_t kDecodeMaxM = 16;
+constexpr int64_t kDecodeFusedMaxN = 8192;
 
 int stream_splits(int64_t M, int64_t N, int64_t K) {
   const int64_t KB = (K + 127) / 128;
@@ -619,7 +730,7 @@ hipError_t launch_lds(const GemmArgs& a, hipStream_t st) {
 using namespace detail;
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  if (M <= 0 || M > kStreamMaxM) return 0;
+  if (M <= kDecodeMaxM || M > kStreamMaxM) return 0;
   const int splits = stream_splits(M, N, K);
   const int64_t KB = (K + 127) / 128;
   const int kbps = (int)((KB + splits - 1) / splits);
@@ -627,8 +738,12 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return real > 1 ? (size_t)real * M * N * sizeof(float) : 0;
 }
 
+bool linear_fused(int64_t M, int64_t N) {
+  return M > 0 && M <= kDecodeMaxM && N <= kDecodeFusedMaxN;
+}
+
 size_t linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  if (M <= 0) return 0;
+  if (M <= 0 || linear_fused(M, N)) return 0;   // quantization inside the decode kernel
   const int64_t G = (K + 127) / 128;
   auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
   return up((size_t)M * K) + up((size_t)M * G * 4) + gemm_workspace_bytes(M, N, K);
@@ -638,11 +753,27 @@ size_t grouped_workspace_bytes(int64_t, int64_t, int64_t, int) { return 0; }
 
 int gemm_kind(int64_t M, int64_t N) {
   if (M <= 0 || N <= 0) return BSFP8_GEMM_NONE;
+  if (M <= kDecodeMaxM) return BSFP8_GEMM_DECODE;
   if (M <= kStreamMaxM) return BSFP8_GEMM_STREAM;
   return use_big_tile(M, N) ? BSFP8_GEMM_TILE_256x256 : BSFP8_GEMM_TILE_128x256;
 }
 
+template <int FMT>
+hipError_t launch_decode(const GemmArgs& a, hipStream_t st) {
+  const dim3 grid((unsigned)((a.N + 15) / 16));
+  if (a.x_bf16)
+    hipLaunchKernelGGL((gemm_decode_kernel<FMT, true>), grid, dim3(64 * kDecodeWaves), 0, st,
+                       nullptr, nullptr, a.x_bf16, a.ldx, a.wq, a.ws, a.bias, a.y, (int)a.M,
+                       a.N, a.K);
+  else
+    hipLaunchKernelGGL((gemm_decode_kernel<FMT, false>), grid, dim3(64 * kDecodeWaves), 0, st,
+                       a.xq, a.xs, nullptr, (int64_t)0, a.wq, a.ws, a.bias, a.y, (int)a.M, a.N,
+                       a.K);
+  return hipGetLastError();
+}
+
 hipError_t launch_block_gemm(const GemmArgs& a, hipStream_t st) {
+  if (a.M <= kDecodeMaxM) return a.fmt == 0 ? launch_decode<0>(a, st) : launch_decode<1>(a, st);
   if (a.M <= kStreamMaxM) return a.fmt == 0 ? launch_stream<0>(a, st) : launch_stream<1>(a, st);
   return a.fmt == 0 ? launch_lds<0, false>(a, st) : launch_lds<1, false>(a, st);
 }

@@ -45,21 +45,14 @@ __device__ __forceinline__ float amax8(const Unpacked& u) {
 // codes packed little-endian; writes the stored scale representation.
 template <int FMT>
 __device__ __forceinline__ uint2 encode8(const Unpacked& u, float amax, float* s_f32, int* s_exp) {
-  if (FMT == 0) {
-    const float s = (amax == 0.0f) ? 1.0f : amax / kE4M3Max;
-    *s_f32 = s;
-    uint2 r;
-    r.x = e4m3x4(u.f[0] / s, u.f[1] / s, u.f[2] / s, u.f[3] / s);
-    r.y = e4m3x4(u.f[4] / s, u.f[5] / s, u.f[6] / s, u.f[7] / s);
-    return r;
-  } else {
-    const int e = ue8m0_exp(amax);
-    *s_exp = e;
-    uint2 r;
-    r.x = e4m3x4(ldexpf(u.f[0], -e), ldexpf(u.f[1], -e), ldexpf(u.f[2], -e), ldexpf(u.f[3], -e));
-    r.y = e4m3x4(ldexpf(u.f[4], -e), ldexpf(u.f[5], -e), ldexpf(u.f[6], -e), ldexpf(u.f[7], -e));
-    return r;
-  }
+  const float s = FMT == 0 ? act_scale_f32(amax) : 0.0f;
+  const int e = FMT == 0 ? 0 : ue8m0_exp(amax);
+  *s_f32 = s;
+  *s_exp = e;
+  uint2 r;
+  r.x = act_encode4<FMT>(u.f[0], u.f[1], u.f[2], u.f[3], s, e);
+  r.y = act_encode4<FMT>(u.f[4], u.f[5], u.f[6], u.f[7], s, e);
+  return r;
 }
 
 // One 16-lane quarter-wave owns one 1x128 group of one row: each lane holds

@@ -18,7 +18,7 @@ OK, EINVAL, ENOTSUP, ENOSPC, EHIP = 0, 1, 2, 3, 4
 SCALE_FLOAT, SCALE_UE8M0 = 0, 1
 ACT_DYNAMIC, ACT_STATIC = 0, 1
 OP_BLOCK_GEMM, OP_LINEAR, OP_GROUPED_GEMM, OP_FP4_QUANT, OP_FP4_GEMM = 0, 1, 2, 3, 4
-GEMM_NONE, GEMM_STREAM, GEMM_TILE_128x256, GEMM_TILE_256x256 = 0, 1, 2, 3
+GEMM_NONE, GEMM_STREAM, GEMM_TILE_128x256, GEMM_TILE_256x256, GEMM_DECODE = 0, 1, 2, 3, 4
 
 EXPORTS = ("bsfp8_version", "bsfp8_status_string", "bsfp8_workspace_size", "bsfp8_gemm_kernel",
            "fp8_quant_act", "fp8_quant_weight", "fp8_block_gemm", "fp8_linear",

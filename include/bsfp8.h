@@ -76,9 +76,10 @@ typedef enum {
 /* Kernels fp8_block_gemm / fp8_linear choose between (bsfp8_gemm_kernel). */
 typedef enum {
   BSFP8_GEMM_NONE = 0,          /* empty problem: nothing is launched          */
-  BSFP8_GEMM_STREAM = 1,        /* M <= 128: weight-streaming split-K kernel   */
+  BSFP8_GEMM_STREAM = 1,        /* 16 < M <= 128: weight-streaming split-K     */
   BSFP8_GEMM_TILE_128x256 = 2,  /* LDS-staged MFMA kernel, 128 x 256 tiles     */
-  BSFP8_GEMM_TILE_256x256 = 3   /* LDS-staged MFMA kernel, 256 x 256 tiles     */
+  BSFP8_GEMM_TILE_256x256 = 3,  /* LDS-staged MFMA kernel, 256 x 256 tiles     */
+  BSFP8_GEMM_DECODE = 4         /* M <= 16: one-launch weight-streaming kernel */
 } bsfp8_gemm_kind;
 
 /* Library version (major * 10000 + minor * 100 + patch). */

@@ -99,10 +99,19 @@ def test_block_gemm_argument_checks(kw, code):
 
 
 def test_block_gemm_workspace_too_small():
-    need = L.workspace_size(L.OP_BLOCK_GEMM, 16, 4096, 4096)
+    need = L.workspace_size(L.OP_BLOCK_GEMM, 64, 4096, 4096)
     assert need > 0
-    assert _gemm(M=16, N=4096, K=4096, w=FAKE, wb=need - 1) == L.ENOSPC
-    assert _gemm(M=16, N=4096, K=4096, w=None, wb=need) == L.EINVAL
+    assert _gemm(M=64, N=4096, K=4096, w=FAKE, wb=need - 1) == L.ENOSPC
+    assert _gemm(M=64, N=4096, K=4096, w=None, wb=need) == L.EINVAL
+
+
+def test_decode_needs_no_workspace():
+    """M <= 16 runs in one launch with no workspace; fp8_linear fuses the
+    activation quantization there up to N = 8192 and stages it above."""
+    for M in (1, 16):
+        assert L.workspace_size(L.OP_BLOCK_GEMM, M, 28672, 4096) == 0
+        assert L.workspace_size(L.OP_LINEAR, M, 8192, 4096) == 0
+        assert L.workspace_size(L.OP_LINEAR, M, 8200, 4096) > 0
 
 
 def test_linear_argument_checks():
@@ -112,9 +121,9 @@ def test_linear_argument_checks():
              None) == L.ENOTSUP
     assert f(FAKE, 128, FAKE, FAKE, None, FAKE, 16, 256, 256, 128, 128, 0, 0, FAKE, 1 << 20,
              None) == L.EINVAL
-    need = L.workspace_size(L.OP_LINEAR, 16, 256, 256)
+    need = L.workspace_size(L.OP_LINEAR, 64, 256, 256)
     assert need > 0
-    assert f(FAKE, 256, FAKE, FAKE, None, FAKE, 16, 256, 256, 128, 128, 0, 0, FAKE, need - 1,
+    assert f(FAKE, 256, FAKE, FAKE, None, FAKE, 64, 256, 256, 128, 128, 0, 0, FAKE, need - 1,
              None) == L.ENOSPC
 
 
@@ -150,13 +159,16 @@ def test_workspace_size_unknown_op():
 
 
 def test_gemm_kernel_choice():
-    """Host-side kernel choice: split-K weight streaming up to M = 128, then
+    """Host-side kernel choice: the one-launch decode kernel up to M = 16,
+    split-K weight streaming up to M = 128, then
     the 256 x 256 tile whenever it fills the CUs in fewer weighted rounds than
     the 128 x 256 tile (256 CUs, per-tile time 4 : 3)."""
     k = L.gemm_kernel
     assert k(0, 256) == L.GEMM_NONE and k(5, 0) == L.GEMM_NONE
     assert L.load().bsfp8_gemm_kernel(-1, 8) == -1
-    for M in (1, 16, 128):
+    for M in (1, 16):
+        assert k(M, 28672) == L.GEMM_DECODE
+    for M in (17, 128):
         assert k(M, 28672) == L.GEMM_STREAM
     assert k(129, 256) == L.GEMM_TILE_128x256
     assert k(2048, 4096) == L.GEMM_TILE_128x256      # 128 big tiles would idle half the CUs

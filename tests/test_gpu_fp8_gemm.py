@@ -110,7 +110,38 @@ def test_block_gemm_full_size_sampled(M, K, N, fmt, gen):
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
-@pytest.mark.parametrize("M,N,K", [(1, 256, 256), (16, 520, 384), (200, 512, 1040)])
+def test_linear_fused_quant_every_bf16_pattern(fmt):
+    """The decode kernel's in-launch activation quantization against the
+    standalone quantizer: every finite bf16 bit pattern, in a seeded order,
+    as 16 tokens x 4096 channels; outputs must agree bit for bit."""
+    import torch
+    from block_scaled_precision_fp8_amd import lib as L
+    M, K, N = 16, 4096, 512
+    pats = np.arange(65536, dtype=np.uint32)
+    finite = ((pats >> 7) & 0xFF) != 0xFF
+    pats = np.where(finite, pats, 0).astype(np.uint16)
+    x = pats[np.random.default_rng(3).permutation(65536)].reshape(M, K)
+    assert L.workspace_size(L.OP_LINEAR, M, N, K) == 0          # the fused path
+    w = synth.normal_bf16((N, K), 0.02, "llama", "w", seed=8)
+    xd, wd = to_dev_bf16(x), to_dev_bf16(w)
+    sdt = torch.float32 if fmt == 0 else torch.uint8
+    xq = torch.empty((M, K), dtype=torch.uint8, device=xd.device)
+    xs = torch.empty((M, K // 128), dtype=sdt, device=xd.device)
+    wq = torch.empty((N, K), dtype=torch.uint8, device=xd.device)
+    ws = torch.empty((N // 128, K // 128), dtype=sdt, device=xd.device)
+    L.fp8_quant_act(xd, xq, xs, scale_fmt=fmt)
+    L.fp8_quant_weight(wd, wq, ws, scale_fmt=fmt)
+    y1 = torch.empty((M, N), dtype=torch.bfloat16, device=xd.device)
+    y2 = torch.empty_like(y1)
+    L.fp8_block_gemm(xq, xs, wq, ws, y1, scale_fmt=fmt)
+    L.fp8_linear(xd, wq, ws, y2, scale_fmt=fmt)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits(y1), bf16_bits(y2))
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("M,N,K", [(1, 256, 256), (16, 520, 384), (200, 512, 1040),
+                                   (1, 8200, 256), (5, 264, 4112)])
 def test_linear_matches_two_calls(M, N, K, fmt):
     import torch
     from block_scaled_precision_fp8_amd import lib as L
