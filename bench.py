@@ -10,6 +10,9 @@ dynamic activation quantization (fp8_quant_act) then the block-scaled GEMM
 and two quantized copies alternate step by step, so decode-sized runs read
 their weights from HBM rather than from the 256 MB Infinity Cache.
 value = GEMM flops of the step / step time (TFLOP/s, act quant included).
+Decode-sized runs (M <= 16) whose activation quantization the library fuses
+into the GEMM launch are one fp8_linear call; the others are fp8_quant_act
+then fp8_block_gemm, the two launches fp8_linear makes for them.
 
 The other rows of the path are timed in the same run and reported in
 ``detail`` (not in ``value``): DeepSeek-V3-shaped linears with UE8M0 scales,
@@ -133,7 +136,11 @@ def run_linears(torch, L, synth, shapes, ms, fmt, workload, steps, warmup, dev, 
             else:
                 x = synth.device_deepseek_acts(M, K, index=100 * i + M)
             need = L.workspace_size(L.OP_BLOCK_GEMM, M, N, K)
-            runs.append(dict(M=M, K=K, N=N, x=x,
+            # decode-sized runs whose quantization fp8_linear fuses into the
+            # GEMM launch go through fp8_linear (one launch)
+            fused = (L.gemm_kernel(M, N) == L.GEMM_DECODE
+                     and L.workspace_size(L.OP_LINEAR, M, N, K) == 0)
+            runs.append(dict(M=M, K=K, N=N, x=x, fused=fused,
                              xq=torch.empty((M, K), dtype=torch.uint8, device=dev),
                              xs=torch.empty((M, K // 128), dtype=sdt, device=dev),
                              y=torch.empty((M, N), dtype=torch.bfloat16, device=dev),
@@ -146,6 +153,12 @@ def run_linears(torch, L, synth, shapes, ms, fmt, workload, steps, warmup, dev, 
             wq, wsc = weights[(r["K"], r["N"])][s & 1]
             if tm:
                 tm.mark(("q", j))
+            if r["fused"]:
+                L.fp8_linear(r["x"], wq, wsc, r["y"], scale_fmt=fmt, stream=sp)
+                if tm:
+                    tm.mark(("g", j))
+                    tm.mark(("e", j))
+                continue
             L.fp8_quant_act(r["x"], r["xq"], r["xs"], scale_fmt=fmt, stream=sp)
             if tm:
                 tm.mark(("g", j))
@@ -168,11 +181,26 @@ def run_linears(torch, L, synth, shapes, ms, fmt, workload, steps, warmup, dev, 
     ms_step = t0.elapsed_time(t1) / steps
     sb = 4 if fmt == 0 else 1
     detail, big_flops, big_ms, n_big, flops = [], 0.0, 0.0, 0, 0.0
+    dec_bytes, dec_ms = 0.0, 0.0
     for j, r in enumerate(runs):
         M, N, K = r["M"], r["N"], r["K"]
         qm, gm = tm.ms(("q", j), ("g", j)), tm.ms(("g", j), ("e", j))
         fl = 2.0 * M * N * K
         flops += fl
+        if r["fused"]:
+            # one launch: bf16 activations in, weights + scales, bf16 out
+            lm = qm
+            lb = 2 * M * K + gemm_bytes(M, N, K, sb) - M * K - sb * M * (-(-K // 128))
+            d = dict(M=M, K=K, N=N, fused_quant=True, linear_us=round(lm * 1e3, 2),
+                     linear_tflops=round(fl / (lm * 1e-3) / 1e12, 2),
+                     linear_gbs=round(lb / (lm * 1e-3) / 1e9, 1),
+                     frac_hbm=round(lb / (lm * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
+            dec_bytes += lb
+            dec_ms += lm
+            log(f"[{workload}] M={M:5d} K={K:5d} N={N:5d} fused linear {lm*1e3:8.1f} us "
+                f"({d['linear_gbs']:7.1f} GB/s, {d['linear_tflops']:7.1f} TF/s)")
+            detail.append(d)
+            continue
         qb, gb = act_bytes(M, K, sb), gemm_bytes(M, N, K, sb)
         d = dict(M=M, K=K, N=N, quant_us=round(qm * 1e3, 2), gemm_us=round(gm * 1e3, 2),
                  linear_tflops=round(fl / ((qm + gm) * 1e-3) / 1e12, 2),
@@ -181,6 +209,9 @@ def run_linears(torch, L, synth, shapes, ms, fmt, workload, steps, warmup, dev, 
                  quant_gbs=round(qb / (qm * 1e-3) / 1e9, 1),
                  gemm_gbs=round(gb / (gm * 1e-3) / 1e9, 1),
                  frac_hbm_gemm=round(gb / (gm * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
+        if M <= 16:
+            dec_bytes += qb + gb
+            dec_ms += qm + gm
         detail.append(d)
         if L.gemm_kernel(M, N) == L.GEMM_TILE_256x256:
             big_flops += fl
@@ -189,12 +220,17 @@ def run_linears(torch, L, synth, shapes, ms, fmt, workload, steps, warmup, dev, 
         log(f"[{workload}] M={M:5d} K={K:5d} N={N:5d} quant {qm*1e3:8.1f} us "
             f"({d['quant_gbs']:7.1f} GB/s)  gemm {gm*1e3:8.1f} us ({d['gemm_tflops']:7.1f} TF/s, "
             f"{d['gemm_gbs']:7.1f} GB/s)  linear {d['linear_tflops']:7.1f} TF/s")
+    decode = None
+    if dec_ms > 0:
+        decode = dict(runs="M <= 16", bytes=dec_bytes, us=round(dec_ms * 1e3, 1),
+                      gbs=round(dec_bytes / (dec_ms * 1e-3) / 1e9, 1),
+                      frac_hbm=round(dec_bytes / (dec_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
     for r in runs:
         r.clear()
     weights.clear()
     torch.cuda.empty_cache()
     return dict(detail=detail, ms_step=ms_step, flops=flops, big_flops=big_flops,
-                big_ms=big_ms, n_big=n_big)
+                big_ms=big_ms, n_big=n_big, decode=decode)
 
 
 def run_moe(torch, L, synth, steps, warmup, dev, sp):
@@ -454,12 +490,13 @@ def main():
                 "launches_per_step": r["n_big"],
                 "avg_launch_us": round(r["big_ms"] / r["n_big"] * 1e3, 2),
                 "algorithmic_gflop_per_launch": round(r["big_flops"] / r["n_big"] / 1e9, 2)}
-    detail = {"llama": r["detail"]}
+    detail = {"llama": r["detail"], "llama_decode_hbm": r["decode"]}
     suites = [] if args.suites == "none" else args.suites.split(",")
     if "deepseek" in suites:
         d = run_linears(torch, L, synth, DEEPSEEK_SHAPES, DEEPSEEK_MS, 1, "deepseek",
                         max(5, args.steps // 2), 2, dev, sp)
         detail["deepseek_ue8m0"] = d["detail"]
+        detail["deepseek_decode_hbm"] = d["decode"]
         detail["deepseek_ue8m0_tile256_tflops"] = round(d["big_flops"] / (d["big_ms"] * 1e-3)
                                                         / 1e12, 1)
     if "moe" in suites:

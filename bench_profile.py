@@ -9,9 +9,11 @@ launches, each scaled by true bytes / counter reading of the plain copy
 kernel of N MiB that `bench.py --copy-calib-mib N` runs first; records the
 sha256 of the GEMM source so bench.py only uses it for the same kernel.
 `stats`: the kernel table of a --kernel-trace --stats run.
+`summary`: the text form of one bench.py JSON line.
 """
 
 import argparse
+import json
 import csv
 import hashlib
 import os
@@ -89,6 +91,25 @@ def stats(a):
     print("\n".join(lines))
 
 
+def summary(a):
+    """one bench.py JSON line -> the text summary kept under profiles/"""
+    with open(a.json) as f:
+        d = json.loads(f.read().strip().splitlines()[-1])
+    lines = [f"# bench.py (all suites) on one MI355X; command: {a.cmd}",
+             f"value ({d['config']['workload'][:60]}...): {d['value']} {d['unit']}, "
+             f"ms_per_step {d['ms_per_step']}",
+             "roofline: " + json.dumps(d["roofline"]),
+             "cpu_baseline: " + json.dumps(d["cpu_baseline"]),
+             "# per-run details"]
+    for key, val in d["detail"].items():
+        if isinstance(val, list):
+            lines += [f"{key}: " + json.dumps(r) for r in val]
+        else:
+            lines.append(f"{key}: " + json.dumps(val))
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -103,8 +124,12 @@ def main():
     s.add_argument("--cmd", required=True)
     s.add_argument("--out", required=True)
     s.add_argument("--top", type=int, default=12)
+    b = sub.add_parser("summary")
+    b.add_argument("--json", required=True)
+    b.add_argument("--cmd", required=True)
+    b.add_argument("--out", required=True)
     a = ap.parse_args()
-    traffic(a) if a.what == "traffic" else stats(a)
+    {"traffic": traffic, "stats": stats, "summary": summary}[a.what](a)
 
 
 if __name__ == "__main__":

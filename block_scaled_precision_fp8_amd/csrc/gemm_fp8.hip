@@ -521,8 +521,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 // reciprocal plus one exact correction).  Every workgroup quantizes all of
 // X, so the fused form is used up to kDecodeFusedMaxN outputs only.
 // ------------------------------------------------------------------------
-constexpr int kDecodeWaves = 8;
-constexpr int kDecodeDepth = 4;
+constexpr int kDecodeWaves = 16;
+constexpr int kDecodeDepth = 2;
 
 template <int FMT, bool FUSED>
 __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
