@@ -103,8 +103,14 @@ __device__ __forceinline__ uint32_t act_encode4_rcp(float a, float b, float c, f
 
 // ---------------------------------------------------------------- host
 
+// static_scale: null for dynamic 1x128 groups, else the device address of
+// one calibrated per-tensor scale (fp32, or the E8M0 byte).
 hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
-                            int fmt, uint8_t* xq, void* scale, hipStream_t s);
+                            int fmt, uint8_t* xq, void* scale, hipStream_t s,
+                            const void* static_scale = nullptr);
+hipError_t launch_dequant_weight(const uint8_t* wq, int64_t N, int64_t K, int fmt,
+                                 const void* scale, uint16_t* w, hipStream_t s);
+hipError_t launch_pow2_to_ue8m0(const float* in, int64_t n, uint8_t* out, hipStream_t s);
 hipError_t launch_quant_weight(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
                                int fmt, uint8_t* wq, void* scale, hipStream_t s);
 

@@ -119,7 +119,6 @@ int32_t fp8_quant_act(const void* x, int64_t M, int64_t K, int64_t ldx, int32_t 
   if (!valid_fmt(scale_fmt)) return BSFP8_EINVAL;
   if (group_k <= 0) return BSFP8_EINVAL;
   if (group_k != 128) return BSFP8_ENOTSUP;
-  if (act_scheme == BSFP8_ACT_STATIC) return BSFP8_ENOTSUP;
   if (M == 0) return BSFP8_OK;
   if (K == 0) return BSFP8_EINVAL;
   if (!x || !xq || !x_scale) return BSFP8_EINVAL;
@@ -127,8 +126,37 @@ int32_t fp8_quant_act(const void* x, int64_t M, int64_t K, int64_t ldx, int32_t 
   if (!fits_i32(M * ((K + 127) / 128))) return BSFP8_EINVAL;
   int32_t r = check_device(stream);
   if (r != BSFP8_OK) return r;
+  // STATIC: the calibrated scale sits in x_scale[0] on entry; every group's
+  // entry (x_scale[0] included) is set to that same value
   return hip_status(launch_quant_act((const uint16_t*)x, M, K, ldx, scale_fmt, (uint8_t*)xq,
-                                     x_scale, (hipStream_t)stream));
+                                     x_scale, (hipStream_t)stream,
+                                     act_scheme == BSFP8_ACT_STATIC ? x_scale : nullptr));
+}
+
+int32_t fp8_dequant_weight(const void* wq, int64_t N, int64_t K, int32_t block_n,
+                           int32_t block_k, int32_t scale_fmt, const void* w_scale_inv, void* w,
+                           void* stream) {
+  if (N < 0 || K < 0 || !fits_i32(N) || !fits_i32(K)) return BSFP8_EINVAL;
+  if (K % 16 != 0) return BSFP8_EINVAL;
+  if (!valid_fmt(scale_fmt)) return BSFP8_EINVAL;
+  int32_t r = check_blocks(block_n, block_k);
+  if (r != BSFP8_OK) return r;
+  if (N == 0 || K == 0) return BSFP8_OK;
+  if (!wq || !w_scale_inv || !w) return BSFP8_EINVAL;
+  if (!al16(wq) || !al16(w) || ((uintptr_t)w_scale_inv & 3u)) return BSFP8_EINVAL;
+  r = check_device(stream);
+  if (r != BSFP8_OK) return r;
+  return hip_status(launch_dequant_weight((const uint8_t*)wq, N, K, scale_fmt, w_scale_inv,
+                                          (uint16_t*)w, (hipStream_t)stream));
+}
+
+int32_t fp8_scale_to_ue8m0(const float* scale, int64_t n, void* out, void* stream) {
+  if (n < 0) return BSFP8_EINVAL;
+  if (n == 0) return BSFP8_OK;
+  if (!scale || !out || ((uintptr_t)scale & 3u)) return BSFP8_EINVAL;
+  int32_t r = check_device(stream);
+  if (r != BSFP8_OK) return r;
+  return hip_status(launch_pow2_to_ue8m0(scale, n, (uint8_t*)out, (hipStream_t)stream));
 }
 
 int32_t fp8_quant_weight(const void* w, int64_t N, int64_t K, int64_t ldw, int32_t block_n,

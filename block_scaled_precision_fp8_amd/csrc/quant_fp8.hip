@@ -59,10 +59,12 @@ __device__ __forceinline__ uint2 encode8(const Unpacked& u, float amax, float* s
 // eight consecutive bf16 values (one 16-byte load).  A workgroup of 16
 // quarters covers QG consecutive groups of RQ rows (QG * RQ = 16) and walks
 // kActRows such row sets, with kActUnroll loads issued before use.
-template <int FMT>
+// STATIC: one calibrated scale for the whole tensor, read from `sscale`
+// (fp32, or the E8M0 byte), replaces the group amax.
+template <int FMT, bool STATIC>
 __global__ __launch_bounds__(256) void quant_act_kernel(
     const uint16_t* __restrict__ x, int M, int K, int64_t ldx, int G, int qg_log2,
-    uint8_t* __restrict__ xq, void* __restrict__ scale) {
+    uint8_t* __restrict__ xq, void* __restrict__ scale, const void* sscale) {
   const int tid = threadIdx.x;
   const int l16 = tid & 15;
   const int q = tid >> 4;
@@ -88,14 +90,22 @@ __global__ __launch_bounds__(256) void quant_act_kernel(
     for (int u = 0; u < kActUnroll; ++u) {
       const int m = mbase + RQ * (jb + u);
       const Unpacked f = unpack8(v[u]);
-      float amax = amax8(f);
-      amax = fmaxf(amax, __shfl_xor(amax, 1, 16));
-      amax = fmaxf(amax, __shfl_xor(amax, 2, 16));
-      amax = fmaxf(amax, __shfl_xor(amax, 4, 16));
-      amax = fmaxf(amax, __shfl_xor(amax, 8, 16));
       float sf = 0.0f;
       int se = 0;
-      const uint2 codes = encode8<FMT>(f, amax, &sf, &se);
+      uint2 codes;
+      if constexpr (STATIC) {
+        if (FMT == 0) sf = *(const float*)sscale;
+        else se = (int)*(const uint8_t*)sscale - 127;
+        codes.x = act_encode4<FMT>(f.f[0], f.f[1], f.f[2], f.f[3], sf, se);
+        codes.y = act_encode4<FMT>(f.f[4], f.f[5], f.f[6], f.f[7], sf, se);
+      } else {
+        float amax = amax8(f);
+        amax = fmaxf(amax, __shfl_xor(amax, 1, 16));
+        amax = fmaxf(amax, __shfl_xor(amax, 2, 16));
+        amax = fmaxf(amax, __shfl_xor(amax, 4, 16));
+        amax = fmaxf(amax, __shfl_xor(amax, 8, 16));
+        codes = encode8<FMT>(f, amax, &sf, &se);
+      }
       if (m < M) {
         if (kvalid) *(uint2*)(xq + (int64_t)m * K + k0) = codes;
         if (gvalid && l16 == 0) {
@@ -156,7 +166,7 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(
 using namespace detail;
 
 hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int fmt,
-                            uint8_t* xq, void* scale, hipStream_t s) {
+                            uint8_t* xq, void* scale, hipStream_t s, const void* static_scale) {
   const int G = (int)((K + kBlock - 1) / kBlock);
   int qg_log2 = 0;
   while ((1 << qg_log2) < G && qg_log2 < 4) ++qg_log2;
@@ -164,12 +174,15 @@ hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx
   int64_t gy = (M + RQ * kActRows - 1) / (RQ * kActRows);
   if (gy > 65535) gy = 65535;
   dim3 grid((G + QG - 1) / QG, (unsigned)gy);
-  if (fmt == 0)
-    hipLaunchKernelGGL(quant_act_kernel<0>, grid, dim3(256), 0, s, x, (int)M, (int)K, ldx, G,
-                       qg_log2, xq, scale);
-  else
-    hipLaunchKernelGGL(quant_act_kernel<1>, grid, dim3(256), 0, s, x, (int)M, (int)K, ldx, G,
-                       qg_log2, xq, scale);
+#define BSFP8_ACT(F, S)                                                                      \
+  hipLaunchKernelGGL((quant_act_kernel<F, S>), grid, dim3(256), 0, s, x, (int)M, (int)K, ldx, \
+                     G, qg_log2, xq, scale, static_scale)
+  if (static_scale) {
+    if (fmt == 0) BSFP8_ACT(0, true); else BSFP8_ACT(1, true);
+  } else {
+    if (fmt == 0) BSFP8_ACT(0, false); else BSFP8_ACT(1, false);
+  }
+#undef BSFP8_ACT
   return hipGetLastError();
 }
 

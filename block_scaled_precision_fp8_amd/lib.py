@@ -22,7 +22,8 @@ GEMM_NONE, GEMM_STREAM, GEMM_TILE_128x256, GEMM_TILE_256x256, GEMM_DECODE = 0, 1
 
 EXPORTS = ("bsfp8_version", "bsfp8_status_string", "bsfp8_workspace_size", "bsfp8_gemm_kernel",
            "fp8_quant_act", "fp8_quant_weight", "fp8_block_gemm", "fp8_linear",
-           "fp8_grouped_gemm", "fp4_quant", "fp4_group_gemm")
+           "fp8_grouped_gemm", "fp4_quant", "fp4_group_gemm", "fp8_dequant_weight",
+           "fp8_scale_to_ue8m0")
 
 
 class BsFp8Error(RuntimeError):
@@ -43,6 +44,8 @@ _SIGS = {
     "bsfp8_status_string": (ctypes.c_char_p, [_I32]),
     "bsfp8_workspace_size": (_SZ, [_I32, _I64, _I64, _I64, _I32]),
     "bsfp8_gemm_kernel": (_I32, [_I64, _I64]),
+    "fp8_dequant_weight": (_I32, [_P, _I64, _I64, _I32, _I32, _I32, _P, _P, _P]),
+    "fp8_scale_to_ue8m0": (_I32, [_P, _I64, _P, _P]),
     "fp8_quant_act": (_I32, [_P, _I64, _I64, _I64, _I32, _I32, _I32, _P, _P, _P]),
     "fp8_quant_weight": (_I32, [_P, _I64, _I64, _I64, _I32, _I32, _I32, _P, _P, _P]),
     "fp8_block_gemm": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32,
@@ -121,6 +124,21 @@ def fp8_quant_act(x, xq, x_scale, group_k=128, act_scheme=ACT_DYNAMIC, scale_fmt
     _check("fp8_quant_act", load().fp8_quant_act(_ptr(x), M, K, ldx, group_k, act_scheme,
                                                  scale_fmt, _ptr(xq), _ptr(x_scale),
                                                  _stream(stream)))
+
+
+def fp8_dequant_weight(wq, w_scale_inv, w, block_n=128, block_k=128, scale_fmt=SCALE_FLOAT,
+                       stream=None):
+    """wq: uint8 (N, K) E4M3; w_scale_inv: (NB, KB); w: bf16 (N, K) out."""
+    N, K = wq.shape
+    _check("fp8_dequant_weight", load().fp8_dequant_weight(_ptr(wq), N, K, block_n, block_k,
+                                                           scale_fmt, _ptr(w_scale_inv),
+                                                           _ptr(w), _stream(stream)))
+
+
+def fp8_scale_to_ue8m0(scale, out, stream=None):
+    """scale: fp32 tensor; out: uint8 tensor of the same number of elements."""
+    _check("fp8_scale_to_ue8m0", load().fp8_scale_to_ue8m0(_ptr(scale), scale.numel(),
+                                                           _ptr(out), _stream(stream)))
 
 
 def fp8_quant_weight(w, wq, w_scale_inv, block_n=128, block_k=128, scale_fmt=SCALE_FLOAT,

@@ -89,15 +89,21 @@ BSFP8_API int32_t bsfp8_version(void);
 BSFP8_API const char* bsfp8_status_string(int32_t status);
 
 /*
- * fp8_quant_act -- per-token dynamic activation quantization in 1 x group_k
- * groups ([FG-FP8] §一, second bullet; [HF-PT] opening list).
+ * fp8_quant_act -- activation quantization in 1 x group_k groups: per-token
+ * dynamic scales ([FG-FP8] §一, second bullet; [HF-PT] opening list) or one
+ * static calibrated scale ([FG-FP8] §四: activation_scheme "static").
  *
  *   x        bf16 [M][ldx], read-only; only the first K columns are used.
  *   M, K     rows (tokens) and columns (input channels); K % 16 == 0.
  *   ldx      row stride of x in elements, ldx >= K, ldx % 8 == 0.
  *   group_k  group width; must equal the weight block's K size, 128
  *            ([FG-FP8] §一: the groups line up with the weight blocks).
- *   act_scheme  BSFP8_ACT_DYNAMIC (STATIC -> ENOTSUP).
+ *   act_scheme  BSFP8_ACT_DYNAMIC: the scales below, per group.
+ *               BSFP8_ACT_STATIC: x_scale[0] holds the calibrated
+ *               per-tensor scale on entry (fp32 s > 0, or the E8M0 byte
+ *               b, s = 2^(b-127)); codes = E4M3(fl32(x/s)) or
+ *               E4M3(x * 2^-(b-127)), and every entry of x_scale is set to
+ *               that scale, so fp8_block_gemm takes the result unchanged.
  *   scale_fmt   FLOAT: s = fl32(amax/448), codes = E4M3(fl32(x/s)).
  *               UE8M0: s = 2^e, e = ceil(log2(amax/448)) clamped to
  *               [-127,127] ([FG-FP8] §七 note: fp32 scales round *up* to
@@ -108,8 +114,7 @@ BSFP8_API const char* bsfp8_status_string(int32_t status);
  *   x_scale  out, [M][ceil(K/group_k)] fp32 (FLOAT) or uint8 (UE8M0); the
  *            dequantization multiplier of each group.
  * Errors: EINVAL (null pointers, M or K < 0, K % 16, ldx < K, ldx % 8,
- * group_k != 128 when positive, group_k <= 0, bad enum, misalignment);
- * ENOTSUP (static scheme; group_k other than 128).
+ * group_k <= 0, bad enum, misalignment); ENOTSUP (group_k other than 128).
  */
 BSFP8_API int32_t fp8_quant_act(const void* x, int64_t M, int64_t K, int64_t ldx,
                       int32_t group_k, int32_t act_scheme, int32_t scale_fmt,
@@ -239,6 +244,34 @@ BSFP8_API int32_t fp4_group_gemm(const void* xq4, const void* x_gscale,
                        const void* w_gscale, const float* w_tscale, void* y,
                        int64_t M, int64_t N, int64_t K, void* workspace,
                        size_t workspace_bytes, void* stream);
+
+/*
+ * fp8_dequant_weight -- fold the block scales back into the weights, the
+ * dequantize-on-load step for pre-quantized checkpoints ([FG-FP8] §五,
+ * Fp8Dequantize):  W[n][k] = bf16_rne(fl32(E4M3(wq[n][k]) * S_w[n/128][k/128])).
+ *
+ *   wq           E4M3 [N][K], K % 16 == 0.
+ *   w_scale_inv  [ceil(N/128)][ceil(K/128)] fp32 or UE8M0 bytes.
+ *   w            out, bf16 [N][K].
+ * Codes 0x7F / 0xFF (E4M3 NaN) and the E8M0 byte 0xFF are outside the
+ * contract.  Errors: EINVAL (sizes, null pointers, misalignment, bad enum);
+ * ENOTSUP (block sizes other than 128).
+ */
+BSFP8_API int32_t fp8_dequant_weight(const void* wq, int64_t N, int64_t K, int32_t block_n,
+                                     int32_t block_k, int32_t scale_fmt,
+                                     const void* w_scale_inv, void* w, void* stream);
+
+/*
+ * fp8_scale_to_ue8m0 -- power-of-two scales stored in float32 containers to
+ * the one-byte UE8M0 form the kernels read, exactly ([FG-FP8] §七: such
+ * checkpoints are converted on load).  scale[i] = 2^k with -127 <= k <= 127
+ * becomes the byte k + 127; any other value (not a power of two, <= 0,
+ * outside that range, Inf, NaN) becomes 0xFF, the E8M0 NaN encoding, which
+ * callers can test for.
+ *
+ *   scale  device fp32 [n];  out  device uint8 [n].
+ */
+BSFP8_API int32_t fp8_scale_to_ue8m0(const float* scale, int64_t n, void* out, void* stream);
 
 /*
  * Bytes of device workspace the given operation needs for this problem

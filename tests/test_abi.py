@@ -54,7 +54,8 @@ def _qa(**kw):
     (dict(M=-1), L.EINVAL), (dict(K=-16), L.EINVAL), (dict(K=200), L.EINVAL),
     (dict(ldx=128), L.EINVAL), (dict(ldx=260), L.EINVAL), (dict(fmt=2), L.EINVAL),
     (dict(sch=5), L.EINVAL), (dict(gk=0), L.EINVAL), (dict(gk=64), L.ENOTSUP),
-    (dict(sch=1), L.ENOTSUP), (dict(x=None), L.EINVAL), (dict(xq=None), L.EINVAL),
+    (dict(sch=1, M=0), L.OK), (dict(sch=1, xs=None), L.EINVAL),
+    (dict(x=None), L.EINVAL), (dict(xq=None), L.EINVAL),
     (dict(xs=None), L.EINVAL), (dict(x=MIS), L.EINVAL), (dict(M=0), L.OK),
     (dict(M=0, x=None), L.OK),
 ])
@@ -177,3 +178,19 @@ def test_gemm_kernel_choice():
     for N in (4096, 6144, 28672):
         assert k(8192, N) == L.GEMM_TILE_256x256
     assert k(4100, 4104) == L.GEMM_TILE_256x256      # the ragged big-tile parity case
+
+
+def test_dequant_and_ue8m0_argument_checks():
+    lib = L.load()
+    d = lib.fp8_dequant_weight
+    assert d(FAKE, -1, 256, 128, 128, 0, FAKE, FAKE, None) == L.EINVAL
+    assert d(FAKE, 256, 200, 128, 128, 0, FAKE, FAKE, None) == L.EINVAL
+    assert d(FAKE, 256, 256, 64, 128, 0, FAKE, FAKE, None) == L.ENOTSUP
+    assert d(FAKE, 256, 256, 128, 128, 3, FAKE, FAKE, None) == L.EINVAL
+    assert d(None, 256, 256, 128, 128, 0, FAKE, FAKE, None) == L.EINVAL
+    assert d(FAKE, 256, 256, 128, 128, 0, FAKE, MIS, None) == L.EINVAL
+    assert d(FAKE, 0, 256, 128, 128, 0, None, None, None) == L.OK
+    c = lib.fp8_scale_to_ue8m0
+    assert c(FAKE, -1, FAKE, None) == L.EINVAL
+    assert c(None, 4, FAKE, None) == L.EINVAL
+    assert c(FAKE, 0, None, None) == L.OK
