@@ -138,7 +138,7 @@ def run_linears(torch, L, synth, shapes, ms, fmt, workload, steps, warmup, dev, 
             need = L.workspace_size(L.OP_BLOCK_GEMM, M, N, K)
             # decode-sized runs whose quantization fp8_linear fuses into the
             # GEMM launch go through fp8_linear (one launch)
-            fused = (L.gemm_kernel(M, N) == L.GEMM_DECODE
+            fused = (L.gemm_kernel(M, N, K)[0] == L.GEMM_DECODE
                      and L.workspace_size(L.OP_LINEAR, M, N, K) == 0)
             runs.append(dict(M=M, K=K, N=N, x=x, fused=fused,
                              xq=torch.empty((M, K), dtype=torch.uint8, device=dev),
@@ -213,7 +213,7 @@ def run_linears(torch, L, synth, shapes, ms, fmt, workload, steps, warmup, dev, 
             dec_bytes += qb + gb
             dec_ms += qm + gm
         detail.append(d)
-        if L.gemm_kernel(M, N) == L.GEMM_TILE_256x256:
+        if L.gemm_kernel(M, N, K) == (L.GEMM_TILE_256x256, 1):
             big_flops += fl
             big_ms += gm
             n_big += 1

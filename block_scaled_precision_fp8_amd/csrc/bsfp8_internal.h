@@ -133,7 +133,7 @@ struct GemmArgs {
 };
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
-int gemm_kind(int64_t M, int64_t N);   // a bsfp8_gemm_kind
+int gemm_kind(int64_t M, int64_t N, int64_t K, int* splits);   // a bsfp8_gemm_kind
 size_t linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
 bool linear_fused(int64_t M, int64_t N);   // fp8_linear quantizes inside the GEMM
 size_t grouped_workspace_bytes(int64_t T, int64_t N, int64_t K, int E);

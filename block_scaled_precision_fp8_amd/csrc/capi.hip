@@ -105,9 +105,12 @@ size_t bsfp8_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int32_t
   }
 }
 
-int32_t bsfp8_gemm_kernel(int64_t M, int64_t N) {
-  if (M < 0 || N < 0) return -1;
-  return gemm_kind(M, N);
+int32_t bsfp8_gemm_kernel(int64_t M, int64_t N, int64_t K, int32_t* splits) {
+  if (M < 0 || N < 0 || K < 0) return -1;
+  int s = 1;
+  const int kind = gemm_kind(M, N, K, &s);
+  if (splits) *splits = s;
+  return kind;
 }
 
 int32_t fp8_quant_act(const void* x, int64_t M, int64_t K, int64_t ldx, int32_t group_k,

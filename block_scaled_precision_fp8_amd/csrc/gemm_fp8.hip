@@ -16,12 +16,13 @@
 //     place: no vector ALU work in the K loop at all.
 //
 // Kernels:
-//   gemm_lds_kernel     large M: workgroup tile BM x BN, operands staged in
+//   gemm_lds_kernel     M > 16: workgroup tile BM x BN, operands staged in
 //                       LDS (double-buffered, XOR-swizzled 16-byte chunks),
-//                       XCD-aware tile order.  Also serves the MoE grouped
-//                       GEMM through a device-built tile table.
-//   gemm_stream_kernel  small M (<= 128): weight-streaming split-K kernel,
-//                       W fragments loaded straight into registers.
+//                       XCD-aware tile order, optional split-K into fp32
+//                       partials.  Also serves the MoE grouped GEMM through
+//                       a device-built tile table.
+//   gemm_decode_kernel  M <= 16: weight-streaming kernel, one launch, with
+//                       the activation quantization fused for fp8_linear.
 //   splitk_reduce_kernel  fp32 partials -> bf16 (+ bias).
 #include <type_traits>
 
@@ -96,11 +97,12 @@ struct Tile {
   int64_t m0, mlim;   // rows [m0, min(m0 + BM, mlim))
   int64_t n0;
   int expert;
+  int split;          // K split (dense split-K launches), else 0
   bool valid;
 };
 
 template <int BM, int BN>
-__device__ __forceinline__ Tile dense_tile(int64_t M, int64_t N) {
+__device__ __forceinline__ Tile dense_tile(int64_t M, int64_t N, int splits) {
   const int MT = (int)((M + BM - 1) / BM), NT = (int)((N + BN - 1) / BN);
   const int T = MT * NT;
   // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so
@@ -109,8 +111,11 @@ __device__ __forceinline__ Tile dense_tile(int64_t M, int64_t N) {
   const int per_xcd = (int)(gridDim.x / 8);
   int t = (bid & 7) * per_xcd + (bid >> 3);
   Tile tl;
-  tl.valid = t < T;
+  tl.valid = t < T * splits;
   tl.expert = 0;
+  // K splits outermost: the tiles of one split run together
+  tl.split = t / T;
+  t -= tl.split * T;
   // grouped order: groups of 8 M tiles, M fastest, so 8 x k tiles that run
   // together share their X rows and W columns.
   constexpr int GM = 8;
@@ -152,6 +157,7 @@ __device__ __forceinline__ Tile grouped_tile(const int32_t* __restrict__ seg, in
     __syncthreads();
   }
   Tile tl;
+  tl.split = 0;
   const int t = blockIdx.x;
   const int total = s_pref[E] * NT;
   tl.valid = t < total;
@@ -214,7 +220,8 @@ template <int FMT, int WAVES_M, int WAVES_N, int WM, int WN, bool GROUPED>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
     const uint8_t* __restrict__ xq, const void* __restrict__ xs, const uint8_t* __restrict__ wq,
     const void* __restrict__ wsc, const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
-    int64_t M, int64_t N, int64_t K, const int32_t* __restrict__ seg, int E) {
+    int64_t M, int64_t N, int64_t K, const int32_t* __restrict__ seg, int E,
+    float* __restrict__ part, int kbps) {
   // The body exists only in the device pass; the host pass needs nothing
   // but the launch stub of each instantiation.
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -236,10 +243,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
 
   Tile tl;
   if (GROUPED) tl = grouped_tile<BM, BN, THREADS>(seg, E, N, s_pref);
-  else tl = dense_tile<BM, BN>(M, N);
+  else tl = dense_tile<BM, BN>(M, N, part ? (int)(((K + 127) / 128 + kbps - 1) / kbps) : 1);
   if (!tl.valid) return;
 
   const int KB = (int)((K + 127) / 128);
+  // this workgroup's K blocks [kb_begin, kb_end): all of K, or its split
+  const int kb_begin = part ? tl.split * kbps : 0;
+  const int kb_end = part ? min(KB, kb_begin + kbps) : KB;
   const int64_t NB = (N + 127) / 128;
   const uint8_t* wbase = wq + (int64_t)tl.expert * N * K;
   const uint8_t* wsb = (const uint8_t*)wsc + (int64_t)tl.expert * NB * KB * SB;
@@ -372,13 +382,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
     });
   };
 
-  // prologue: stage 0
-  issue(0, 0);
+  // prologue: the first stage
+  issue(kb_begin, 0);
 
   // Main loop, unrolled by two so every register / buffer index is static.
-  // Each step issues the next stage unconditionally (a stage past the end
-  // loads zeros: its offsets are out of range).
-  for (int kb0 = 0;; kb0 += 2) {
+  // Each step issues the next stage unconditionally (a stage past the end of
+  // K loads zeros: its offsets are out of range; past the end of a split it
+  // loads the next split's first block, which is never used).
+  for (int kb0 = kb_begin;; kb0 += 2) {
     bool last = false;
     static_for<2>([&](auto sc) {
       constexpr int s = decltype(sc)::value;
@@ -390,11 +401,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       step(std::integral_constant<int, s>{}, kb + 1);
-      last = kb + 1 >= KB;
+      last = kb + 1 >= kb_end;
     });
     if (last) break;
   }
-done:
   // drain: no DMA may land in LDS after this workgroup has finished
   wait_vmcnt<0>();
 
@@ -406,90 +416,17 @@ done:
 #pragma unroll
     for (int j = 0; j < MI; ++j) {
       const int64_t m = tl.m0 + wm * WM + j * 16 + l16;
-      if (m < tl.mlim) store_out4(y, N, m, n, acc[i][j], bias);
+      if (m >= tl.mlim) continue;
+      if (part) {
+        float* p = part + ((int64_t)tl.split * M + m) * N + n;
+        *(float4*)p = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+      } else {
+        store_out4(y, N, m, n, acc[i][j], bias);
+      }
     }
   }
 #endif
 
-}
-
-// ------------------------------------------------------------------------
-// Small-M weight-streaming kernel: each wave owns 16 weight rows and walks
-// the K blocks [kb0, kb1) of its split; W fragments go straight from HBM to
-// registers (each weight byte is used by exactly one wave), X fragments and
-// scales come from L2.  MT = number of 16-token column tiles.
-// ------------------------------------------------------------------------
-constexpr int kStreamWaves = 4;
-constexpr int kStreamUnroll = 4;
-
-template <int FMT, int MT>
-__global__ __launch_bounds__(64 * kStreamWaves) void gemm_stream_kernel(
-    const uint8_t* __restrict__ xq, const void* __restrict__ xs, const uint8_t* __restrict__ wq,
-    const void* __restrict__ wsc, const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
-    float* __restrict__ part, int M, int64_t N, int64_t K, int kb_per_split) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int l16 = lane & 15, g4 = lane >> 4;
-  const int64_t n0 = ((int64_t)blockIdx.x * kStreamWaves + wave) * 16;
-  if (n0 >= N) return;
-  const int64_t KB = (K + 127) / 128;
-  const int64_t kb0 = (int64_t)blockIdx.y * kb_per_split;
-  const int64_t kb1 = min(KB, kb0 + kb_per_split);
-  const int64_t nrow = n0 + l16;
-  const bool nvalid = nrow < N;
-  const int64_t nblk = n0 >> 7;
-
-  v4f acc[MT];
-#pragma unroll
-  for (int j = 0; j < MT; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  for (int64_t kb = kb0; kb < kb1; kb += kStreamUnroll) {
-    uint4 wa[kStreamUnroll], wb[kStreamUnroll];
-#pragma unroll
-    for (int u = 0; u < kStreamUnroll; ++u) {
-      const int64_t k = (kb + u) * 128 + g4 * 32;
-      wa[u] = make_uint4(0, 0, 0, 0);
-      wb[u] = make_uint4(0, 0, 0, 0);
-      if (kb + u < kb1 && nvalid) {
-        if (k < K) wa[u] = ld_stream16(wq + nrow * K + k);
-        if (k + 16 < K) wb[u] = ld_stream16(wq + nrow * K + k + 16);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kStreamUnroll; ++u) {
-      if (kb + u >= kb1) break;
-      const int64_t k = (kb + u) * 128 + g4 * 32;
-      const float sw = load_scale<FMT>(wsc, nblk * KB + kb + u);
-      const v8i aw = join(wa[u], wb[u]);
-#pragma unroll
-      for (int j = 0; j < MT; ++j) {
-        const int m = j * 16 + l16;
-        uint4 xa = make_uint4(0, 0, 0, 0), xb = make_uint4(0, 0, 0, 0);
-        float sa = (FMT == 0) ? 0.f : __int_as_float(127);
-        if (m < M) {
-          if (k < K) xa = *(const uint4*)(xq + (int64_t)m * K + k);
-          if (k + 16 < K) xb = *(const uint4*)(xq + (int64_t)m * K + k + 16);
-          sa = load_scale<FMT>(xs, (int64_t)m * KB + kb + u);
-        }
-        acc[j] = mfma_step<FMT>(acc[j], aw, join(xa, xb), sa, sw);
-      }
-    }
-  }
-
-  // lane holds n = n0 + 4 g4 + {0..3} for token m = 16 j + l16
-  const int64_t n = n0 + 4 * g4;
-  if (n >= N) return;
-#pragma unroll
-  for (int j = 0; j < MT; ++j) {
-    const int m = j * 16 + l16;
-    if (m >= M) continue;
-    if (part == nullptr) {
-      store_out4(y, N, m, n, acc[j], bias);
-    } else {
-      float* p = part + ((int64_t)blockIdx.y * M + m) * N + n;
-      *(float4*)p = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
-    }
-  }
 }
 
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
@@ -623,7 +560,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
   template __global__ void gemm_lds_kernel<FMT, WMN, WNN, WM, WN, G>(                        \
       const uint8_t* __restrict__, const void* __restrict__, const uint8_t* __restrict__,     \
       const void* __restrict__, const uint16_t* __restrict__, uint16_t* __restrict__, int64_t, \
-      int64_t, int64_t, const int32_t* __restrict__, int);
+      int64_t, int64_t, const int32_t* __restrict__, int, float* __restrict__, int);
 #define BSFP8_INST_ALL(FMT)             \
   BSFP8_INST(FMT, 4, 2, 64, 128, false) \
   BSFP8_INST(FMT, 2, 4, 64, 64, false)  \
@@ -636,46 +573,8 @@ BSFP8_INST_ALL(1)
 // ------------------------------------------------------------------------
 // host side
 // ------------------------------------------------------------------------
-constexpr int64_t kStreamMaxM = 128;
 constexpr int64_t kDecodeMaxM = 16;
 constexpr int64_t kDecodeFusedMaxN = 8192;
-
-int stream_splits(int64_t M, int64_t N, int64_t K) {
-  const int64_t KB = (K + 127) / 128;
-  const int64_t wg_n = (N + 16 * kStreamWaves - 1) / (16 * kStreamWaves);
-  int64_t want = (2048 + wg_n - 1) / wg_n;            // ~8 workgroups per CU
-  int64_t max_by_depth = KB / 4;                      // >= 4 K blocks per split
-  int64_t s = want < max_by_depth ? want : max_by_depth;
-  if (s < 1) s = 1;
-  if (s > 64) s = 64;
-  (void)M;
-  return (int)s;
-}
-
-template <int FMT>
-hipError_t launch_stream(const GemmArgs& a, hipStream_t st) {
-  const int splits = stream_splits(a.M, a.N, a.K);
-  const int64_t KB = (a.K + 127) / 128;
-  const int kbps = (int)((KB + splits - 1) / splits);
-  const int real_splits = (int)((KB + kbps - 1) / kbps);
-  float* part = real_splits > 1 ? (float*)a.workspace : nullptr;
-  dim3 grid((unsigned)((a.N + 16 * kStreamWaves - 1) / (16 * kStreamWaves)), real_splits);
-  const int M = (int)a.M;
-#define BSFP8_STREAM(MT)                                                                     \
-  hipLaunchKernelGGL((gemm_stream_kernel<FMT, MT>), grid, dim3(64 * kStreamWaves), 0, st,   \
-                     a.xq, a.xs, a.wq, a.ws, a.bias, a.y, part, M, a.N, a.K, kbps)
-  if (M <= 16) BSFP8_STREAM(1);
-  else if (M <= 32) BSFP8_STREAM(2);
-  else if (M <= 64) BSFP8_STREAM(4);
-  else BSFP8_STREAM(8);
-#undef BSFP8_STREAM
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || part == nullptr) return e;
-  const int64_t MN = a.M * a.N;
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((MN / 4 + 255) / 256)), dim3(256), 0,
-                     st, part, real_splits, MN, a.N, a.bias, a.y);
-  return hipGetLastError();
-}
 
 // Large-M tile configurations (WAVES_M x WAVES_N waves, wave tile WM x WN,
 // two LDS stages): BM = WM WAVES_M, BN = WN WAVES_N.
@@ -687,55 +586,87 @@ hipError_t launch_stream(const GemmArgs& a, hipStream_t st) {
 // Two stages wait for vmcnt(0) before each K block, which does not depend
 // on the completion order of the LDS-DMA loads and the scale loads.
 template <int FMT, int WMN, int WNN, int WM, int WN, bool GROUPED>
-hipError_t launch_cfg(const GemmArgs& a, hipStream_t st) {
+hipError_t launch_cfg(const GemmArgs& a, hipStream_t st, int splits, int kbps) {
   constexpr int BM = WMN * WM, BN = WNN * WN;
   const int64_t NT = (a.N + BN - 1) / BN;
   int64_t tiles;
   if (GROUPED) {
     tiles = ((a.M + BM - 1) / BM + a.E) * NT;   // every expert adds <= 1 partial M tile
   } else {
-    tiles = (a.M + BM - 1) / BM * NT;
+    tiles = (a.M + BM - 1) / BM * NT * splits;
     tiles = (tiles + 7) / 8 * 8;                 // whole rounds over the 8 XCDs
   }
+  float* part = splits > 1 ? (float*)a.workspace : nullptr;
   hipLaunchKernelGGL((gemm_lds_kernel<FMT, WMN, WNN, WM, WN, GROUPED>), dim3((unsigned)tiles),
                      dim3(64 * WMN * WNN), 0, st, a.xq, a.xs, a.wq, a.ws,
-                     GROUPED ? nullptr : a.bias, a.y, a.M, a.N, a.K, a.seg, a.E);
+                     GROUPED ? nullptr : a.bias, a.y, a.M, a.N, a.K, a.seg, a.E, part, kbps);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || part == nullptr) return e;
+  const int64_t MN = a.M * a.N;
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((MN / 4 + 255) / 256)), dim3(256), 0,
+                     st, part, splits, MN, a.N, a.bias, a.y);
   return hipGetLastError();
 }
 
-// Picks the big tile when its rounds over the CUs, weighted by the per-tile
-// time ratio (4 : 3 against the small tile), cost less than the small
-// tile's: a grid of few big tiles leaves CUs idle that small tiles fill.
-bool use_big_tile(int64_t M, int64_t N) {
-#ifdef BSFP8_SWEEP_CFG
-  return BSFP8_SWEEP_CFG == 5;
-#endif
+// Tile and K-split choice for a dense launch, from a cost model of one
+// round of workgroups over the 256 CUs: rounds x K blocks per split x the
+// measured time of one K block of one tile (2.15 us for 128 x 256 tiles,
+// 2.8 us for 256 x 256 tiles with fp32 scales; UE8M0 runs both about 1.3x
+// faster, which leaves the choice unchanged), plus, when K is split, one
+// reduction launch and the fp32 partial sums written and read back at
+// about 5 TB/s.  A grid of few tiles leaves CUs idle that smaller tiles or
+// K splits fill; splits pay for their partial sums.
+struct Plan {
+  int big;      // 256 x 256 tiles, else 128 x 256
+  int splits;   // K splits (1: no split, bf16 written directly)
+  int kbps;     // K blocks per split
+};
+
+Plan plan_dense(int64_t M, int64_t N, int64_t K) {
   constexpr int64_t kCUs = 256;                 // MI355X compute units
-  const int64_t nb = (N + 255) / 256;
-  const int64_t big = (M + 255) / 256 * nb, small = (M + 127) / 128 * nb;
-  return 4 * ((big + kCUs - 1) / kCUs) < 3 * ((small + kCUs - 1) / kCUs);
+  const double t_blk[2] = {2.15, 2.8};
+  const int64_t KB = (K + 127) / 128;
+  Plan best{0, 1, (int)KB};
+  double best_t = 1e300;
+  for (int big = 0; big < 2; ++big) {
+    const int64_t BM = big ? 256 : 128;
+    const int64_t tiles = (M + BM - 1) / BM * ((N + 255) / 256);
+    for (int64_t S = 1; S <= 32; S *= 2) {
+      if (S > 1 && KB < 2 * S) break;           // at least two K blocks per split
+      const int64_t kbps = (KB + S - 1) / S;
+      const int64_t real = (KB + kbps - 1) / kbps;
+      const int64_t rounds = (tiles * real + kCUs - 1) / kCUs;
+      double t = (double)rounds * (double)kbps * t_blk[big];
+      if (real > 1) t += 3.0 + (double)real * (double)M * (double)N * 8.0 / 5e6;
+      if (t < best_t) {
+        best_t = t;
+        best = Plan{big, (int)real, (int)kbps};
+      }
+    }
+  }
+  return best;
 }
 
 template <int FMT, bool GROUPED>
 hipError_t launch_lds(const GemmArgs& a, hipStream_t st) {
   // expert segments are mostly far shorter than 256 rows: grouped launches
-  // keep the small tile
-  if constexpr (!GROUPED) {
-    if (use_big_tile(a.M, a.N)) return launch_cfg<FMT, 4, 2, 64, 128, false>(a, st);
+  // keep the small tile and no split
+  if constexpr (GROUPED) {
+    return launch_cfg<FMT, 2, 4, 64, 64, true>(a, st, 1, (int)((a.K + 127) / 128));
+  } else {
+    const Plan p = plan_dense(a.M, a.N, a.K);
+    if (p.big) return launch_cfg<FMT, 4, 2, 64, 128, false>(a, st, p.splits, p.kbps);
+    return launch_cfg<FMT, 2, 4, 64, 64, false>(a, st, p.splits, p.kbps);
   }
-  return launch_cfg<FMT, 2, 4, 64, 64, GROUPED>(a, st);
 }
 
 }  // namespace detail
 using namespace detail;
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  if (M <= kDecodeMaxM || M > kStreamMaxM) return 0;
-  const int splits = stream_splits(M, N, K);
-  const int64_t KB = (K + 127) / 128;
-  const int kbps = (int)((KB + splits - 1) / splits);
-  const int real = (int)((KB + kbps - 1) / kbps);
-  return real > 1 ? (size_t)real * M * N * sizeof(float) : 0;
+  if (M <= kDecodeMaxM || N <= 0 || K <= 0) return 0;
+  const Plan p = plan_dense(M, N, K);
+  return p.splits > 1 ? (size_t)p.splits * M * N * sizeof(float) : 0;
 }
 
 bool linear_fused(int64_t M, int64_t N) {
@@ -751,11 +682,13 @@ size_t linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 
 size_t grouped_workspace_bytes(int64_t, int64_t, int64_t, int) { return 0; }
 
-int gemm_kind(int64_t M, int64_t N) {
-  if (M <= 0 || N <= 0) return BSFP8_GEMM_NONE;
+int gemm_kind(int64_t M, int64_t N, int64_t K, int* splits) {
+  if (splits) *splits = 1;
+  if (M <= 0 || N <= 0 || K <= 0) return BSFP8_GEMM_NONE;
   if (M <= kDecodeMaxM) return BSFP8_GEMM_DECODE;
-  if (M <= kStreamMaxM) return BSFP8_GEMM_STREAM;
-  return use_big_tile(M, N) ? BSFP8_GEMM_TILE_256x256 : BSFP8_GEMM_TILE_128x256;
+  const Plan p = plan_dense(M, N, K);
+  if (splits) *splits = p.splits;
+  return p.big ? BSFP8_GEMM_TILE_256x256 : BSFP8_GEMM_TILE_128x256;
 }
 
 template <int FMT>
@@ -774,7 +707,6 @@ hipError_t launch_decode(const GemmArgs& a, hipStream_t st) {
 
 hipError_t launch_block_gemm(const GemmArgs& a, hipStream_t st) {
   if (a.M <= kDecodeMaxM) return a.fmt == 0 ? launch_decode<0>(a, st) : launch_decode<1>(a, st);
-  if (a.M <= kStreamMaxM) return a.fmt == 0 ? launch_stream<0>(a, st) : launch_stream<1>(a, st);
   return a.fmt == 0 ? launch_lds<0, false>(a, st) : launch_lds<1, false>(a, st);
 }
 

@@ -18,7 +18,7 @@ OK, EINVAL, ENOTSUP, ENOSPC, EHIP = 0, 1, 2, 3, 4
 SCALE_FLOAT, SCALE_UE8M0 = 0, 1
 ACT_DYNAMIC, ACT_STATIC = 0, 1
 OP_BLOCK_GEMM, OP_LINEAR, OP_GROUPED_GEMM, OP_FP4_QUANT, OP_FP4_GEMM = 0, 1, 2, 3, 4
-GEMM_NONE, GEMM_STREAM, GEMM_TILE_128x256, GEMM_TILE_256x256, GEMM_DECODE = 0, 1, 2, 3, 4
+GEMM_NONE, GEMM_TILE_128x256, GEMM_TILE_256x256, GEMM_DECODE = 0, 2, 3, 4
 
 EXPORTS = ("bsfp8_version", "bsfp8_status_string", "bsfp8_workspace_size", "bsfp8_gemm_kernel",
            "fp8_quant_act", "fp8_quant_weight", "fp8_block_gemm", "fp8_linear",
@@ -43,7 +43,7 @@ _SIGS = {
     "bsfp8_version": (_I32, []),
     "bsfp8_status_string": (ctypes.c_char_p, [_I32]),
     "bsfp8_workspace_size": (_SZ, [_I32, _I64, _I64, _I64, _I32]),
-    "bsfp8_gemm_kernel": (_I32, [_I64, _I64]),
+    "bsfp8_gemm_kernel": (_I32, [_I64, _I64, _I64, _P]),
     "fp8_dequant_weight": (_I32, [_P, _I64, _I64, _I32, _I32, _I32, _P, _P, _P]),
     "fp8_scale_to_ue8m0": (_I32, [_P, _I64, _P, _P]),
     "fp8_quant_act": (_I32, [_P, _I64, _I64, _I64, _I32, _I32, _I32, _P, _P, _P]),
@@ -103,9 +103,11 @@ def workspace_size(op, M, N, K, E=0):
     return int(load().bsfp8_workspace_size(op, M, N, K, E))
 
 
-def gemm_kernel(M, N):
-    """GEMM_* kind fp8_block_gemm / fp8_linear launch for an M x N output."""
-    return int(load().bsfp8_gemm_kernel(M, N))
+def gemm_kernel(M, N, K):
+    """(GEMM_* kind, K splits) that fp8_block_gemm / fp8_linear use for M x N x K."""
+    sp = ctypes.c_int32(0)
+    kind = int(load().bsfp8_gemm_kernel(M, N, K, ctypes.byref(sp)))
+    return kind, int(sp.value)
 
 
 def _workspace(op, M, N, K, E, ws, device):

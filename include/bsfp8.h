@@ -76,7 +76,7 @@ typedef enum {
 /* Kernels fp8_block_gemm / fp8_linear choose between (bsfp8_gemm_kernel). */
 typedef enum {
   BSFP8_GEMM_NONE = 0,          /* empty problem: nothing is launched          */
-  BSFP8_GEMM_STREAM = 1,        /* 16 < M <= 128: weight-streaming split-K     */
+  BSFP8_GEMM_RESERVED = 1,      /* not returned                                */
   BSFP8_GEMM_TILE_128x256 = 2,  /* LDS-staged MFMA kernel, 128 x 256 tiles     */
   BSFP8_GEMM_TILE_256x256 = 3,  /* LDS-staged MFMA kernel, 256 x 256 tiles     */
   BSFP8_GEMM_DECODE = 4         /* M <= 16: one-launch weight-streaming kernel */
@@ -284,11 +284,13 @@ BSFP8_API size_t bsfp8_workspace_size(int32_t op, int64_t M, int64_t N, int64_t 
 
 /*
  * Which kernel (a bsfp8_gemm_kind) fp8_block_gemm and fp8_linear launch for
- * an M x N output; the choice depends on M and N only (the grouped GEMM
- * always uses 128 x 256 tiles).  Host-only, touches no device.  Returns -1
- * for negative sizes.
+ * an M x N x K problem, and into how many K splits it cuts K (*splits, may
+ * be NULL; 1 when K is not split: splits above 1 write fp32 partial sums to
+ * the workspace and add one reduction launch).  The grouped GEMM always
+ * uses 128 x 256 tiles without splits.  Host-only, touches no device.
+ * Returns -1 for negative sizes.
  */
-BSFP8_API int32_t bsfp8_gemm_kernel(int64_t M, int64_t N);
+BSFP8_API int32_t bsfp8_gemm_kernel(int64_t M, int64_t N, int64_t K, int32_t* splits);
 
 #ifdef __cplusplus
 }

@@ -161,23 +161,28 @@ def test_workspace_size_unknown_op():
 
 def test_gemm_kernel_choice():
     """Host-side kernel choice: the one-launch decode kernel up to M = 16,
-    split-K weight streaming up to M = 128, then
-    the 256 x 256 tile whenever it fills the CUs in fewer weighted rounds than
-    the 128 x 256 tile (256 CUs, per-tile time 4 : 3)."""
+    then the LDS MFMA kernel with the tile and K split picked by the cost
+    model (rounds of workgroups over 256 CUs x per-K-block tile time, plus
+    the partial sums of a split)."""
     k = L.gemm_kernel
-    assert k(0, 256) == L.GEMM_NONE and k(5, 0) == L.GEMM_NONE
-    assert L.load().bsfp8_gemm_kernel(-1, 8) == -1
+    assert k(0, 256, 256)[0] == L.GEMM_NONE and k(5, 0, 256)[0] == L.GEMM_NONE
+    assert L.load().bsfp8_gemm_kernel(-1, 8, 128, None) == -1
     for M in (1, 16):
-        assert k(M, 28672) == L.GEMM_DECODE
-    for M in (17, 128):
-        assert k(M, 28672) == L.GEMM_STREAM
-    assert k(129, 256) == L.GEMM_TILE_128x256
-    assert k(2048, 4096) == L.GEMM_TILE_128x256      # 128 big tiles would idle half the CUs
-    assert k(4096, 1536) == L.GEMM_TILE_128x256
-    assert k(2048, 6144) == L.GEMM_TILE_256x256      # 192 big tiles: one round vs two
+        assert k(M, 28672, 4096) == (L.GEMM_DECODE, 1)
+    # few output tiles: K is split so the grid covers the CUs
+    kind, s = k(128, 4096, 4096)
+    assert kind == L.GEMM_TILE_128x256 and s == 8
+    kind, s = k(128, 28672, 4096)
+    assert kind == L.GEMM_TILE_128x256 and s == 2
+    # large problems: no split; 256 x 256 tiles once they fill the CUs
+    assert k(2048, 4096, 4096) == (L.GEMM_TILE_128x256, 1)
+    assert k(2048, 6144, 4096) == (L.GEMM_TILE_256x256, 1)
     for N in (4096, 6144, 28672):
-        assert k(8192, N) == L.GEMM_TILE_256x256
-    assert k(4100, 4104) == L.GEMM_TILE_256x256      # the ragged big-tile parity case
+        assert k(8192, N, 4096) == (L.GEMM_TILE_256x256, 1)
+    assert k(4100, 4104, 384)[0] == L.GEMM_TILE_256x256     # the ragged big-tile parity case
+    # the workspace is the partial sums of a split
+    assert L.workspace_size(L.OP_BLOCK_GEMM, 128, 4096, 4096) == 8 * 128 * 4096 * 4
+    assert L.workspace_size(L.OP_BLOCK_GEMM, 8192, 4096, 4096) == 0
 
 
 def test_dequant_and_ue8m0_argument_checks():

@@ -50,7 +50,7 @@ def test_block_gemm_parity(M, N, K, bias, fmt):
     say(f"block gemm M={M} N={N} K={K} bias={bias} fmt={fmt}")
     if (M, N) == (4100, 4104):
         from block_scaled_precision_fp8_amd import lib as L
-        assert L.gemm_kernel(M, N) == L.GEMM_TILE_256x256
+        assert L.gemm_kernel(M, N, K)[0] == L.GEMM_TILE_256x256
     x = synth.deepseek_acts(M, K, seed=M) if fmt else synth.llama_acts(M, K, seed=M)
     w = synth.normal_bf16((N, K), 0.02, "llama", "w", seed=N)
     b = synth.normal_bf16((N,), 0.5, "llama", "bias", seed=N) if bias else None
