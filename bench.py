@@ -21,8 +21,9 @@ the MoE grouped GEMMs (256 experts, Zipf-routed top-8), the NVFP4-style MLP
 quantization.
 
 ``roofline`` is for the dominant kernel, the large-M GEMM with 256 x 256 tiles
-(gemm_lds_kernel, every run the library sends to it; bsfp8_gemm_kernel says
-which): algorithmic flops over its launches / its summed duration from HIP events
+(gemm_lds_kernel, every run the library sends to it, split-K ones included
+with their whole 2MNK; bsfp8_gemm_kernel says which): algorithmic flops over
+its launches / its summed duration from HIP events
 recorded on the launch stream inside the timed region.  ``traffic`` comes
 from the committed rocprofv3 PMC summary when that summary was taken on the
 current kernel source, else null.
@@ -213,7 +214,7 @@ def run_linears(torch, L, synth, shapes, ms, fmt, workload, steps, warmup, dev, 
             dec_bytes += qb + gb
             dec_ms += qm + gm
         detail.append(d)
-        if L.gemm_kernel(M, N, K) == (L.GEMM_TILE_256x256, 1):
+        if L.gemm_kernel(M, N, K)[0] == L.GEMM_TILE_256x256:
             big_flops += fl
             big_ms += gm
             n_big += 1
