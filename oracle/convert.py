@@ -10,13 +10,13 @@ What the pages fix ([FG-FP8] §四, §五, §七):
   exactly to the float8_e8m0fnu dtype the kernels read.
 
 Readings where the pages are silent (each also listed in the design doc):
- 14. static: one calibrated per-tensor activation scale supplied by the
+ 12. static: one calibrated per-tensor activation scale supplied by the
      caller; float: codes = E4M3(fl32(x / s)); ue8m0: the scale is the byte b
      (s = 2^(b-127)) and codes = E4M3(x * 2^-(b-127)); every 1 x 128 group's
      stored scale is that one scale, so the GEMM is unchanged;
- 15. dequantized weight = bf16_rne(fl32(dec(code) * scale)) -- the float32
+ 13. dequantized weight = bf16_rne(fl32(dec(code) * scale)) -- the float32
      product, then one round-to-nearest-even into bf16;
- 16. fp32 -> UE8M0: an exact power of two 2^k with -127 <= k <= 127 becomes
+ 14. fp32 -> UE8M0: an exact power of two 2^k with -127 <= k <= 127 becomes
      the byte k + 127; every other value (not a power of two, <= 0, out of
      range, Inf, NaN) becomes 0xFF, the E8M0 NaN encoding.
 """
@@ -57,7 +57,7 @@ def dequant_weight_bf16(wq, w_scale, block_n=128, block_k=128, fmt=SCALE_FLOAT):
 
 
 def pow2_to_ue8m0(scale_f32):
-    """float32 array -> uint8 E8M0 bytes (see reading 16)."""
+    """float32 array -> uint8 E8M0 bytes (see reading 14)."""
     s = np.asarray(scale_f32, dtype=np.float32).astype(np.float64)
     out = np.full(s.shape, 255, dtype=np.uint8)
     with np.errstate(divide="ignore", invalid="ignore"):
