@@ -24,6 +24,7 @@
 //   gemm_decode_kernel  M <= 16: weight-streaming kernel, one launch, with
 //                       the activation quantization fused for fp8_linear.
 //   splitk_reduce_kernel  fp32 partials -> bf16 (+ bias).
+#include <algorithm>
 #include <type_traits>
 
 #include "bsfp8.h"
@@ -135,14 +136,19 @@ __device__ __forceinline__ Tile dense_tile(int64_t M, int64_t N, int splits) {
 // segment offsets: expert e owns mt_e = ceil(rows_e / BM) M tiles and all NT
 // N tiles; tiles are numbered expert by expert, then N tile, then M tile
 // (M fastest, so the M tiles of one expert's weight tile run together).
+// gsel picks the experts a launch covers: 0 all, 1 those with more than
+// kSmallSegment rows, 2 the others (each class runs on its own tile shape).
+constexpr int kSmallSegment = 128;
+
 template <int BM, int BN, int THREADS>
 __device__ __forceinline__ Tile grouped_tile(const int32_t* __restrict__ seg, int E, int64_t N,
-                                             int* s_pref) {
+                                             int* s_pref, int gsel) {
   const int NT = (int)((N + BN - 1) / BN);
   // per-expert M-tile counts, then an inclusive scan (Hillis-Steele).
   for (int e = threadIdx.x; e < E; e += THREADS) {
     const int rows = seg[e + 1] - seg[e];
-    s_pref[e + 1] = (rows + BM - 1) / BM;
+    const bool take = gsel == 0 || ((rows > kSmallSegment) == (gsel == 1));
+    s_pref[e + 1] = take ? (rows + BM - 1) / BM : 0;
   }
   if (threadIdx.x == 0) s_pref[0] = 0;
   __syncthreads();
@@ -220,7 +226,7 @@ template <int FMT, int WAVES_M, int WAVES_N, int WM, int WN, bool GROUPED>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
     const uint8_t* __restrict__ xq, const void* __restrict__ xs, const uint8_t* __restrict__ wq,
     const void* __restrict__ wsc, const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
-    int64_t M, int64_t N, int64_t K, const int32_t* __restrict__ seg, int E,
+    int64_t M, int64_t N, int64_t K, const int32_t* __restrict__ seg, int E, int gsel,
     float* __restrict__ part, int kbps) {
   // The body exists only in the device pass; the host pass needs nothing
   // but the launch stub of each instantiation.
@@ -242,7 +248,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
   __shared__ int s_pref[GROUPED ? 1025 : 1];
 
   Tile tl;
-  if (GROUPED) tl = grouped_tile<BM, BN, THREADS>(seg, E, N, s_pref);
+  if (GROUPED) tl = grouped_tile<BM, BN, THREADS>(seg, E, N, s_pref, gsel);
   else tl = dense_tile<BM, BN>(M, N, part ? (int)(((K + 127) / 128 + kbps - 1) / kbps) : 1);
   if (!tl.valid) return;
 
@@ -560,11 +566,12 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
   template __global__ void gemm_lds_kernel<FMT, WMN, WNN, WM, WN, G>(                        \
       const uint8_t* __restrict__, const void* __restrict__, const uint8_t* __restrict__,     \
       const void* __restrict__, const uint16_t* __restrict__, uint16_t* __restrict__, int64_t, \
-      int64_t, int64_t, const int32_t* __restrict__, int, float* __restrict__, int);
+      int64_t, int64_t, const int32_t* __restrict__, int, int, float* __restrict__, int);
 #define BSFP8_INST_ALL(FMT)             \
   BSFP8_INST(FMT, 4, 2, 64, 128, false) \
   BSFP8_INST(FMT, 2, 4, 64, 64, false)  \
-  BSFP8_INST(FMT, 2, 4, 64, 64, true)
+  BSFP8_INST(FMT, 2, 4, 64, 64, true)   \
+  BSFP8_INST(FMT, 4, 2, 64, 128, true)
 BSFP8_INST_ALL(0)
 BSFP8_INST_ALL(1)
 #undef BSFP8_INST_ALL
@@ -586,12 +593,17 @@ constexpr int64_t kDecodeFusedMaxN = 8192;
 // Two stages wait for vmcnt(0) before each K block, which does not depend
 // on the completion order of the LDS-DMA loads and the scale loads.
 template <int FMT, int WMN, int WNN, int WM, int WN, bool GROUPED>
-hipError_t launch_cfg(const GemmArgs& a, hipStream_t st, int splits, int kbps) {
+hipError_t launch_cfg(const GemmArgs& a, hipStream_t st, int splits, int kbps, int gsel = 0) {
   constexpr int BM = WMN * WM, BN = WNN * WN;
   const int64_t NT = (a.N + BN - 1) / BN;
   int64_t tiles;
   if (GROUPED) {
-    tiles = ((a.M + BM - 1) / BM + a.E) * NT;   // every expert adds <= 1 partial M tile
+    // upper bound on the class's M tiles: every expert adds <= 1 partial
+    // tile; more than kSmallSegment rows each bounds the count of big ones
+    const int64_t full = (a.M + BM - 1) / BM;
+    const int64_t parts = gsel == 1 ? std::min<int64_t>(a.E, a.M / (kSmallSegment + 1) + 1)
+                                    : (int64_t)a.E;
+    tiles = (gsel == 2 ? (int64_t)a.E : full + parts) * NT;
   } else {
     tiles = (a.M + BM - 1) / BM * NT * splits;
     tiles = (tiles + 7) / 8 * 8;                 // whole rounds over the 8 XCDs
@@ -599,7 +611,8 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t st, int splits, int kbps) {
   float* part = splits > 1 ? (float*)a.workspace : nullptr;
   hipLaunchKernelGGL((gemm_lds_kernel<FMT, WMN, WNN, WM, WN, GROUPED>), dim3((unsigned)tiles),
                      dim3(64 * WMN * WNN), 0, st, a.xq, a.xs, a.wq, a.ws,
-                     GROUPED ? nullptr : a.bias, a.y, a.M, a.N, a.K, a.seg, a.E, part, kbps);
+                     GROUPED ? nullptr : a.bias, a.y, a.M, a.N, a.K, a.seg, a.E, gsel, part,
+                     kbps);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || part == nullptr) return e;
   const int64_t MN = a.M * a.N;
@@ -649,10 +662,14 @@ Plan plan_dense(int64_t M, int64_t N, int64_t K) {
 
 template <int FMT, bool GROUPED>
 hipError_t launch_lds(const GemmArgs& a, hipStream_t st) {
-  // expert segments are mostly far shorter than 256 rows: grouped launches
-  // keep the small tile and no split
   if constexpr (GROUPED) {
-    return launch_cfg<FMT, 2, 4, 64, 64, true>(a, st, 1, (int)((a.K + 127) / 128));
+    // experts with many rows on 256 x 256 tiles, the short segments (most
+    // of them under skewed routing) on 128 x 256 tiles: two launches over
+    // disjoint experts, each with its own device-built tile table
+    const int kb = (int)((a.K + 127) / 128);
+    hipError_t e = launch_cfg<FMT, 4, 2, 64, 128, true>(a, st, 1, kb, 1);
+    if (e != hipSuccess) return e;
+    return launch_cfg<FMT, 2, 4, 64, 64, true>(a, st, 1, kb, 2);
   } else {
     const Plan p = plan_dense(a.M, a.N, a.K);
     if (p.big) return launch_cfg<FMT, 4, 2, 64, 128, false>(a, st, p.splits, p.kbps);
