@@ -245,12 +245,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
   constexpr int SB = FMT == 0 ? 4 : 1;      // bytes per scale
   constexpr int LOADS = XJ + WJ + MI + 1;   // vector-memory ops per stage per lane
   __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES * STAGE];
-  __shared__ int s_pref[GROUPED ? 1025 : 1];
+  static_assert(!GROUPED || STAGES * STAGE >= 1025 * 4, "tile table fits the stage buffers");
 
   Tile tl;
-  if (GROUPED) tl = grouped_tile<BM, BN, THREADS>(seg, E, N, s_pref, gsel);
+  // the grouped tile table lives in the stage buffers until the tile is known
+  if (GROUPED) tl = grouped_tile<BM, BN, THREADS>(seg, E, N, (int*)lds, gsel);
   else tl = dense_tile<BM, BN>(M, N, part ? (int)(((K + 127) / 128 + kbps - 1) / kbps) : 1);
   if (!tl.valid) return;
+  if (GROUPED) __syncthreads();            // every lookup done before the first DMA
 
   const int KB = (int)((K + 127) / 128);
   // this workgroup's K blocks [kb_begin, kb_end): all of K, or its split
@@ -570,7 +572,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
 #define BSFP8_INST_ALL(FMT)             \
   BSFP8_INST(FMT, 4, 2, 64, 128, false) \
   BSFP8_INST(FMT, 2, 4, 64, 64, false)  \
-  BSFP8_INST(FMT, 2, 4, 64, 64, true)   \
+  BSFP8_INST(FMT, 1, 4, 64, 64, true)   \
   BSFP8_INST(FMT, 4, 2, 64, 128, true)
 BSFP8_INST_ALL(0)
 BSFP8_INST_ALL(1)
@@ -586,6 +588,8 @@ constexpr int64_t kDecodeFusedMaxN = 8192;
 // Large-M tile configurations (WAVES_M x WAVES_N waves, wave tile WM x WN,
 // two LDS stages): BM = WM WAVES_M, BN = WN WAVES_N.
 //   small: 128 x 256, 8 waves of 64 x 64 (two per SIMD)
+//   short: 64 x 256, 4 waves of 64 x 64, two workgroups per CU (MoE
+//          segments of at most 128 rows)
 //   big:   256 x 256, 8 waves of 64 x 128 (two per SIMD); per flop a third
 //          fewer operand bytes through L2 and the texture path and a quarter
 //          fewer LDS fragment reads than the small tile, so it runs about
@@ -603,7 +607,7 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t st, int splits, int kbps, i
     const int64_t full = (a.M + BM - 1) / BM;
     const int64_t parts = gsel == 1 ? std::min<int64_t>(a.E, a.M / (kSmallSegment + 1) + 1)
                                     : (int64_t)a.E;
-    tiles = (gsel == 2 ? (int64_t)a.E : full + parts) * NT;
+    tiles = (gsel == 2 ? (int64_t)a.E * ((kSmallSegment + BM - 1) / BM) : full + parts) * NT;
   } else {
     tiles = (a.M + BM - 1) / BM * NT * splits;
     tiles = (tiles + 7) / 8 * 8;                 // whole rounds over the 8 XCDs
@@ -664,12 +668,14 @@ template <int FMT, bool GROUPED>
 hipError_t launch_lds(const GemmArgs& a, hipStream_t st) {
   if constexpr (GROUPED) {
     // experts with many rows on 256 x 256 tiles, the short segments (most
-    // of them under skewed routing) on 128 x 256 tiles: two launches over
-    // disjoint experts, each with its own device-built tile table
+    // of them under skewed routing) on 64 x 256 tiles of four waves (two
+    // workgroups per CU), which pad a 42-row median segment to 64 rather
+    // than 128: two launches over disjoint experts, each with its own
+    // device-built tile table
     const int kb = (int)((a.K + 127) / 128);
     hipError_t e = launch_cfg<FMT, 4, 2, 64, 128, true>(a, st, 1, kb, 1);
     if (e != hipSuccess) return e;
-    return launch_cfg<FMT, 2, 4, 64, 64, true>(a, st, 1, kb, 2);
+    return launch_cfg<FMT, 1, 4, 64, 64, true>(a, st, 1, kb, 2);
   } else {
     const Plan p = plan_dense(a.M, a.N, a.K);
     if (p.big) return launch_cfg<FMT, 4, 2, 64, 128, false>(a, st, p.splits, p.kbps);

@@ -288,7 +288,7 @@ BSFP8_API size_t bsfp8_workspace_size(int32_t op, int64_t M, int64_t N, int64_t 
  * be NULL; 1 when K is not split: splits above 1 write fp32 partial sums to
  * the workspace and add one reduction launch).  The grouped GEMM does not
  * split K: experts with more than 128 rows run on 256 x 256 tiles and the
- * others on 128 x 256 tiles, in two launches.  Host-only, touches no device.
+ * others on 64 x 256 tiles, in two launches.  Host-only, touches no device.
  * Returns -1 for negative sizes.
  */
 BSFP8_API int32_t bsfp8_gemm_kernel(int64_t M, int64_t N, int64_t K, int32_t* splits);
