@@ -111,6 +111,8 @@ hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx
 hipError_t launch_dequant_weight(const uint8_t* wq, int64_t N, int64_t K, int fmt,
                                  const void* scale, uint16_t* w, hipStream_t s);
 hipError_t launch_pow2_to_ue8m0(const float* in, int64_t n, uint8_t* out, hipStream_t s);
+hipError_t launch_mxfp4_quant_weight(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
+                                     uint8_t* wq4, uint8_t* scale, hipStream_t s);
 hipError_t launch_quant_weight(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
                                int fmt, uint8_t* wq, void* scale, hipStream_t s);
 
@@ -130,9 +132,12 @@ struct GemmArgs {
   // fused act quant (fp8_linear decode path): bf16 input, else null
   const uint16_t* x_bf16;
   int64_t ldx;
+  // MXFP4 weights: wq (N, K/2) E2M1 codes, ws (N, K/32) E8M0 bytes
+  bool w4;
 };
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+size_t fp8_fp4_workspace_bytes(int64_t M, int64_t N, int64_t K);
 int gemm_kind(int64_t M, int64_t N, int64_t K, int* splits);   // a bsfp8_gemm_kind
 size_t linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
 bool linear_fused(int64_t M, int64_t N);   // fp8_linear quantizes inside the GEMM

@@ -101,6 +101,7 @@ size_t bsfp8_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int32_t
     case BSFP8_OP_GROUPED_GEMM: return grouped_workspace_bytes(M, N, K, E);
     case BSFP8_OP_FP4_QUANT: return fp4_quant_workspace_bytes(M, K);
     case BSFP8_OP_FP4_GEMM: return fp4_gemm_workspace_bytes(M, N, K);
+    case BSFP8_OP_FP8_FP4_GEMM: return fp8_fp4_workspace_bytes(M, N, K);
     default: return (size_t)-1;
   }
 }
@@ -160,6 +161,40 @@ int32_t fp8_scale_to_ue8m0(const float* scale, int64_t n, void* out, void* strea
   int32_t r = check_device(stream);
   if (r != BSFP8_OK) return r;
   return hip_status(launch_pow2_to_ue8m0(scale, n, (uint8_t*)out, (hipStream_t)stream));
+}
+
+int32_t mxfp4_quant_weight(const void* w, int64_t N, int64_t K, int64_t ldw, void* wq4,
+                           void* w_scale, void* stream) {
+  if (N < 0 || K < 0 || !fits_i32(N) || !fits_i32(K)) return BSFP8_EINVAL;
+  if (K % 32 != 0 || ldw < K || ldw % 8 != 0) return BSFP8_EINVAL;
+  if (N == 0 || K == 0) return BSFP8_OK;
+  if (!w || !wq4 || !w_scale) return BSFP8_EINVAL;
+  if (!al16(w) || !al16(wq4)) return BSFP8_EINVAL;
+  int32_t r = check_device(stream);
+  if (r != BSFP8_OK) return r;
+  return hip_status(launch_mxfp4_quant_weight((const uint16_t*)w, N, K, ldw, (uint8_t*)wq4,
+                                              (uint8_t*)w_scale, (hipStream_t)stream));
+}
+
+int32_t fp8_fp4_gemm(const void* xq, const void* x_scale, const void* wq4, const void* w_scale,
+                     const void* bias, void* y, int64_t M, int64_t N, int64_t K,
+                     int32_t scale_fmt, void* workspace, size_t workspace_bytes, void* stream) {
+  int32_t r = check_gemm(xq, x_scale, wq4, w_scale, bias, y, M, N, K, 128, 128, scale_fmt);
+  if (r != BSFP8_OK) return r;
+  if (K % 32 != 0) return BSFP8_EINVAL;
+  if (M == 0) return BSFP8_OK;
+  const size_t need = fp8_fp4_workspace_bytes(M, N, K);
+  if (workspace_bytes < need) return BSFP8_ENOSPC;
+  if (need && (!workspace || !al16(workspace))) return BSFP8_EINVAL;
+  if (!fits_i32(M * ((K + 127) / 128))) return BSFP8_EINVAL;
+  r = check_device(stream);
+  if (r != BSFP8_OK) return r;
+  GemmArgs a{};
+  a.xq = (const uint8_t*)xq; a.xs = x_scale; a.wq = (const uint8_t*)wq4; a.ws = w_scale;
+  a.bias = (const uint16_t*)bias; a.y = (uint16_t*)y; a.M = M; a.N = N; a.K = K;
+  a.fmt = scale_fmt; a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+  a.w4 = true;
+  return hip_status(launch_block_gemm(a, (hipStream_t)stream));
 }
 
 int32_t fp8_quant_weight(const void* w, int64_t N, int64_t K, int64_t ldw, int32_t block_n,

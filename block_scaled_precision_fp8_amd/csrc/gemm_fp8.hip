@@ -77,6 +77,26 @@ __device__ __forceinline__ v4f mfma_step(v4f acc, const v8i& a, const v8i& b, fl
   }
 }
 
+// MFMA step with an MXFP4 weight fragment (A operand, format E2M1: 16
+// bytes per lane in the low half of the register block) and its lane's
+// E8M0 block scale (the 32 weights this lane carries); X stays FP8.
+template <int FMT>
+__device__ __forceinline__ v4f mfma_step_w4(v4f acc, const v8i& a, const v8i& b, float sa,
+                                            int sw4) {
+  if (FMT == 0) {
+    const v4f zero = {0.f, 0.f, 0.f, 0.f};
+    v4f t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 4, 0, 0, sw4, 0, 127);
+    acc[0] = fmaf(t[0], sa, acc[0]);
+    acc[1] = fmaf(t[1], sa, acc[1]);
+    acc[2] = fmaf(t[2], sa, acc[2]);
+    acc[3] = fmaf(t[3], sa, acc[3]);
+    return acc;
+  } else {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 4, 0, 0, sw4, 0,
+                                                            __float_as_int(sa));
+  }
+}
+
 // bf16 epilogue for four consecutive n of one row m.
 __device__ __forceinline__ void store_out4(uint16_t* y, int64_t N, int64_t m, int64_t n, v4f v,
                                            const uint16_t* bias) {
@@ -222,7 +242,14 @@ __device__ __forceinline__ v8i read_frag(const uint8_t* __restrict__ row, int ch
 // this swizzle gives.  Each wave
 // computes a WM (m) x WN (n) tile with 16x16x128 MFMAs: W is the A operand,
 // X the B operand.
-template <int FMT, int WAVES_M, int WAVES_N, int WM, int WN, bool GROUPED>
+//
+// W4: W holds MXFP4 codes (N, K/2) with one E8M0 scale per 1 x 32 group
+// (N, K/32).  A W row is then 64 bytes per K block, four 16-byte chunks
+// swizzled by ((row >> 2) & 3) (four rows per bank sweep); lane (l16, g4)
+// takes chunk g4, the weights K 32 g4 .. 32 g4 + 31, which the MFMA pairs
+// with the X chunks g4 and g4 + 4 of the FP8 operand (the lane layout of
+// the FP4 x FP8 form, checked on the GPU), and passes its own group's scale.
+template <int FMT, int WAVES_M, int WAVES_N, int WM, int WN, bool GROUPED, bool W4 = false>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
     const uint8_t* __restrict__ xq, const void* __restrict__ xs, const uint8_t* __restrict__ wq,
     const void* __restrict__ wsc, const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
@@ -237,11 +264,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
   constexpr int BM = WAVES_M * WM, BN = WAVES_N * WN;
   constexpr int MI = WM / 16, NI = WN / 16;
   static_assert(WN == 64 || WN == 128, "a wave's N range lies inside one weight block");
+  static_assert(!(W4 && GROUPED), "MXFP4 weights: dense launches");
+  constexpr int kWRow = W4 ? 64 : kRowBytes;   // W bytes per row per K block
   constexpr int XJ = BM * 8 / THREADS;      // DMA loads per lane per stage (X)
-  constexpr int WJ = BN * 8 / THREADS;      // (W)
-  static_assert(XJ * THREADS == BM * 8 && WJ * THREADS == BN * 8, "tile / thread mismatch");
+  constexpr int WJ = BN * (kWRow / 16) / THREADS;   // (W)
+  static_assert(XJ * THREADS == BM * 8 && WJ * THREADS == BN * (kWRow / 16), "tile / thread mismatch");
   constexpr int XBYTES = BM * kRowBytes;
-  constexpr int STAGE = (BM + BN) * kRowBytes;
+  constexpr int STAGE = BM * kRowBytes + BN * kWRow;
   constexpr int SB = FMT == 0 ? 4 : 1;      // bytes per scale
   constexpr int LOADS = XJ + WJ + MI + 1;   // vector-memory ops per stage per lane
   __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES * STAGE];
@@ -270,7 +299,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
   const int64_t mrows = min((int64_t)BM, tl.mlim - tl.m0);
   const int64_t nrows = min((int64_t)BN, N - tl.n0);
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(xq + tl.m0 * K, mrows * K);
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(wbase + tl.n0 * K, nrows * K);
+  const int64_t KW = W4 ? K / 2 : K;         // W bytes per row
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(wbase + tl.n0 * KW, nrows * KW);
   const __amdgpu_buffer_rsrc_t rsa = make_rsrc((const uint8_t*)xs + tl.m0 * KB * SB,
                                                mrows * KB * SB);
   const __amdgpu_buffer_rsrc_t rsw = make_rsrc(wsb, NB * KB * SB);
@@ -282,6 +312,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
     const uint32_t kc = kbyte + c * 16;
     return (row < rows && kc < (uint32_t)K) ? (uint32_t)(row * K) + kc : kOOB;
   };
+  // the same for a 64-byte MXFP4 W row: four chunks, swizzle (row >> 2) & 3
+  auto dma_src4 = [&](int q, int64_t rows, int kb) -> uint32_t {
+    const int row = q >> 2, c = (q & 3) ^ ((row >> 2) & 3);
+    const uint32_t kc = (uint32_t)kb * 64 + c * 16;
+    return (row < rows && kc < (uint32_t)KW) ? (uint32_t)(row * KW) + kc : kOOB;
+  };
+  // MXFP4 weight scales: lane row of each 16-row subtile, group 4 kb + g4
+  const int64_t G32 = K / 32;
+  const __amdgpu_buffer_rsrc_t rsw4 = make_rsrc((const uint8_t*)wsc + tl.n0 * G32,
+                                                W4 ? nrows * G32 : 0);
   // scale sources: this lane's token rows, and this wave's weight block
   uint32_t saoff[MI];
 #pragma unroll
@@ -294,6 +334,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
 
   float sa_reg[STAGES][MI];
   float sw_reg[STAGES];
+  int sw4_reg[STAGES][W4 ? NI : 1];
 
   // issue one stage: X and W tiles into LDS buffer `buf`, scales into
   // registers; exactly LOADS vector-memory ops per lane, in this order.
@@ -310,8 +351,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
 #pragma unroll
     for (int j = 0; j < WJ; ++j) {
       const int q = (j * WAVES + wave) * 64 + lane;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, BSFP8_LDS(sw + (j * WAVES + wave) * 1024),
-                                               16, dma_src(q, nrows, kbyte), 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rw, BSFP8_LDS(sw + (j * WAVES + wave) * 1024), 16,
+          W4 ? dma_src4(q, nrows, kb) : dma_src(q, nrows, kbyte), 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
@@ -319,7 +361,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
       if (FMT == 0) sa_reg[buf][i] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsa, off, 0, 0));
       else sa_reg[buf][i] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b8(rsa, off, 0, 0));
     }
-    {
+    if constexpr (W4) {
+#pragma unroll
+      for (int ii = 0; ii < NI; ++ii) {
+        const int r = wn * WN + ii * 16 + l16;
+        const int64_t gi = (int64_t)kb * 4 + g4;
+        const uint32_t off = (r < nrows && gi < G32) ? (uint32_t)(r * G32 + gi) : kOOB;
+        sw4_reg[buf][ii] = (int)__builtin_amdgcn_raw_buffer_load_b8(rsw4, off, 0, 0);
+      }
+    } else {
       const uint32_t off = swoff == kOOB ? kOOB : swoff + kb * SB;
       if (FMT == 0) sw_reg[buf] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsw, off, 0, 0));
       else sw_reg[buf] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b8(rsw, off, 0, 0));
@@ -337,8 +387,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
   // per-lane chunk offsets serve every fragment.
   const int ch0 = (g4 ^ (l16 >> 1)) << 4;
   const int ch1 = ((g4 + 4) ^ (l16 >> 1)) << 4;
-  auto frag = [&](const uint8_t* row) -> v8i {
-    return join(*(const uint4*)(row + ch0), *(const uint4*)(row + ch1));
+  const int chw = (g4 ^ ((l16 >> 2) & 3)) << 4;   // MXFP4 W rows: chunk g4
+  // a W fragment: FP8 rows as X, MXFP4 rows one 16-byte chunk per lane
+  auto wfrag = [&](const uint8_t* row) -> v8i {
+    if constexpr (W4) return join(*(const uint4*)(row + chw), make_uint4(0, 0, 0, 0));
+    else return read_frag(row, ch0, ch1);
   };
 
   v4f acc[NI][MI];
@@ -352,11 +405,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
   auto step = [&](auto buf_c, int kb_next) {
     constexpr int buf = decltype(buf_c)::value;
     const uint8_t* sx = lds + buf * STAGE + (wm * WM + l16) * kRowBytes;
-    const uint8_t* swl = lds + buf * STAGE + XBYTES + (wn * WN + l16) * kRowBytes;
+    const uint8_t* swl = lds + buf * STAGE + XBYTES + (wn * WN + l16) * kWRow;
     issue(kb_next, buf ^ 1);
     float sa[MI];
-    float sw = sw_reg[buf];
+    float sw = W4 ? 0.0f : sw_reg[buf];
     if (FMT == 1) sw = __int_as_float(__float_as_int(sw) & 0xff);
+    int sw4[W4 ? NI : 1];
+    if constexpr (W4) {
+#pragma unroll
+      for (int ii = 0; ii < NI; ++ii) sw4[ii] = sw4_reg[buf][ii] & 0xff;
+    }
 #pragma unroll
     for (int j = 0; j < MI; ++j) {
       sa[j] = sa_reg[buf][j];
@@ -372,20 +430,25 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
     constexpr int NGR = NI / NG;
     v8i aw[2][NG];
 #pragma unroll
-    for (int ii = 0; ii < NG; ++ii) aw[0][ii] = read_frag(swl + ii * 16 * kRowBytes, ch0, ch1);
+    for (int ii = 0; ii < NG; ++ii) aw[0][ii] = wfrag(swl + ii * 16 * kWRow);
     static_for<NGR>([&](auto gc) {
       constexpr int g = decltype(gc)::value;
       if constexpr (g + 1 < NGR) {
 #pragma unroll
         for (int ii = 0; ii < NG; ++ii)
-          aw[(g + 1) & 1][ii] = read_frag(swl + ((g + 1) * NG + ii) * 16 * kRowBytes, ch0, ch1);
+          aw[(g + 1) & 1][ii] = wfrag(swl + ((g + 1) * NG + ii) * 16 * kWRow);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ii = 0; ii < NG; ++ii)
 #pragma unroll
-        for (int j = 0; j < MI; ++j)
-          acc[g * NG + ii][j] = mfma_step<FMT>(acc[g * NG + ii][j], aw[g & 1][ii], bx[j], sa[j], sw);
+        for (int j = 0; j < MI; ++j) {
+          if constexpr (W4)
+            acc[g * NG + ii][j] = mfma_step_w4<FMT>(acc[g * NG + ii][j], aw[g & 1][ii], bx[j], sa[j],
+                                                    sw4[g * NG + ii]);
+          else
+            acc[g * NG + ii][j] = mfma_step<FMT>(acc[g * NG + ii][j], aw[g & 1][ii], bx[j], sa[j], sw);
+        }
       __builtin_amdgcn_sched_barrier(0);
     });
   };
@@ -469,7 +532,10 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 constexpr int kDecodeWaves = 16;
 constexpr int kDecodeDepth = 2;
 
-template <int FMT, bool FUSED>
+// W4: W holds MXFP4 codes (N, K/2) with E8M0 scales per 1 x 32 group
+// (N, K/32): each lane streams 16 weight bytes per block and takes the X
+// chunks g4 and g4 + 4 (the FP4 x FP8 lane pairing of the scaled MFMA).
+template <int FMT, bool FUSED, bool W4 = false>
 __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
     const uint8_t* __restrict__ xq, const void* __restrict__ xs,
     const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ wq,
@@ -485,7 +551,12 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
   const bool mvalid = l16 < M;             // this lane's token row (B column)
   const int KB = (int)((K + 127) / 128);
   const int64_t nblk = n0 >> 7;
-  const uint8_t* wrow = wq + nrow * K;
+  const int64_t KW = W4 ? K / 2 : K;       // W bytes per row
+  const int64_t G32 = K / 32;
+  const uint8_t* wrow = wq + nrow * KW;
+  // this lane's X elements of a block: two runs of 16 starting at kx0, kx1
+  const int kx0 = W4 ? 16 * g4 : 32 * g4;
+  const int kx1 = W4 ? 64 + 16 * g4 : 32 * g4 + 16;
 
   v4f acc = {0.f, 0.f, 0.f, 0.f};
   for (int kb0 = wave; kb0 < KB; kb0 += kDecodeWaves * kDecodeDepth) {
@@ -493,27 +564,33 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
 #pragma unroll
     for (int u = 0; u < kDecodeDepth; ++u) {
       const int kb = kb0 + u * kDecodeWaves;
-      const int64_t k = (int64_t)kb * 128 + g4 * 32;
       wa[u] = make_uint4(0, 0, 0, 0);
       wb[u] = make_uint4(0, 0, 0, 0);
       if (kb < KB && nvalid) {
-        if (k < K) wa[u] = ld_stream16(wrow + k);
-        if (k + 16 < K) wb[u] = ld_stream16(wrow + k + 16);
+        if constexpr (W4) {
+          const int64_t kw = (int64_t)kb * 64 + g4 * 16;
+          if (kw < KW) wa[u] = ld_stream16(wrow + kw);
+        } else {
+          const int64_t k = (int64_t)kb * 128 + g4 * 32;
+          if (k < K) wa[u] = ld_stream16(wrow + k);
+          if (k + 16 < K) wb[u] = ld_stream16(wrow + k + 16);
+        }
       }
     }
 #pragma unroll
     for (int u = 0; u < kDecodeDepth; ++u) {
       const int kb = kb0 + u * kDecodeWaves;
       if (kb >= KB) break;
-      const int64_t k = (int64_t)kb * 128 + g4 * 32;
+      const int64_t k0 = (int64_t)kb * 128 + kx0, k1 = (int64_t)kb * 128 + kx1;
       v8i bx;
       float sa;
       if constexpr (FUSED) {
         uint4 v[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+          const int64_t k = (i < 2 ? k0 : k1) + 8 * (i & 1);
           v[i] = make_uint4(0, 0, 0, 0);
-          if (mvalid && k + 8 * i < K) v[i] = *(const uint4*)(x + (int64_t)l16 * ldx + k + 8 * i);
+          if (mvalid && k < K) v[i] = *(const uint4*)(x + (int64_t)l16 * ldx + k);
         }
         float f[32];
 #pragma unroll
@@ -540,14 +617,20 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
         uint4 xa = make_uint4(0, 0, 0, 0), xb = make_uint4(0, 0, 0, 0);
         sa = (FMT == 0) ? 0.f : __int_as_float(127);
         if (mvalid) {
-          if (k < K) xa = *(const uint4*)(xq + (int64_t)l16 * K + k);
-          if (k + 16 < K) xb = *(const uint4*)(xq + (int64_t)l16 * K + k + 16);
+          if (k0 < K) xa = *(const uint4*)(xq + (int64_t)l16 * K + k0);
+          if (k1 < K) xb = *(const uint4*)(xq + (int64_t)l16 * K + k1);
           sa = load_scale<FMT>(xs, (int64_t)l16 * KB + kb);
         }
         bx = join(xa, xb);
       }
-      const float sw = load_scale<FMT>(wsc, nblk * KB + kb);
-      acc = mfma_step<FMT>(acc, join(wa[u], wb[u]), bx, sa, sw);
+      if constexpr (W4) {
+        const int64_t gi = (int64_t)kb * 4 + g4;
+        const int sw4 = (nvalid && gi < G32) ? (int)((const uint8_t*)wsc)[nrow * G32 + gi] : 127;
+        acc = mfma_step_w4<FMT>(acc, join(wa[u], wb[u]), bx, sa, sw4);
+      } else {
+        const float sw = load_scale<FMT>(wsc, nblk * KB + kb);
+        acc = mfma_step<FMT>(acc, join(wa[u], wb[u]), bx, sa, sw);
+      }
     }
   }
   red[wave][lane] = acc;
@@ -564,16 +647,17 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
 // Explicit instantiations of every tile configuration the dispatcher below
 // can launch (the host pass does not always emit launch stubs for kernel
 // templates that are only instantiated implicitly).
-#define BSFP8_INST(FMT, WMN, WNN, WM, WN, G)                                                  \
-  template __global__ void gemm_lds_kernel<FMT, WMN, WNN, WM, WN, G>(                        \
+#define BSFP8_INST(FMT, WMN, WNN, WM, WN, G, W4)                                              \
+  template __global__ void gemm_lds_kernel<FMT, WMN, WNN, WM, WN, G, W4>(                    \
       const uint8_t* __restrict__, const void* __restrict__, const uint8_t* __restrict__,     \
       const void* __restrict__, const uint16_t* __restrict__, uint16_t* __restrict__, int64_t, \
       int64_t, int64_t, const int32_t* __restrict__, int, int, float* __restrict__, int);
-#define BSFP8_INST_ALL(FMT)             \
-  BSFP8_INST(FMT, 4, 2, 64, 128, false) \
-  BSFP8_INST(FMT, 2, 4, 64, 64, false)  \
-  BSFP8_INST(FMT, 1, 4, 64, 64, true)   \
-  BSFP8_INST(FMT, 4, 2, 64, 128, true)
+#define BSFP8_INST_ALL(FMT)                   \
+  BSFP8_INST(FMT, 4, 2, 64, 128, false, false) \
+  BSFP8_INST(FMT, 2, 4, 64, 64, false, false)  \
+  BSFP8_INST(FMT, 2, 4, 64, 64, false, true)   \
+  BSFP8_INST(FMT, 1, 4, 64, 64, true, false)   \
+  BSFP8_INST(FMT, 4, 2, 64, 128, true, false)
 BSFP8_INST_ALL(0)
 BSFP8_INST_ALL(1)
 #undef BSFP8_INST_ALL
@@ -596,7 +680,7 @@ constexpr int64_t kDecodeFusedMaxN = 8192;
 //          1.5x faster per CU once every CU has a tile of its own.
 // Two stages wait for vmcnt(0) before each K block, which does not depend
 // on the completion order of the LDS-DMA loads and the scale loads.
-template <int FMT, int WMN, int WNN, int WM, int WN, bool GROUPED>
+template <int FMT, int WMN, int WNN, int WM, int WN, bool GROUPED, bool W4 = false>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t st, int splits, int kbps, int gsel = 0) {
   constexpr int BM = WMN * WM, BN = WNN * WN;
   const int64_t NT = (a.N + BN - 1) / BN;
@@ -613,7 +697,7 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t st, int splits, int kbps, i
     tiles = (tiles + 7) / 8 * 8;                 // whole rounds over the 8 XCDs
   }
   float* part = splits > 1 ? (float*)a.workspace : nullptr;
-  hipLaunchKernelGGL((gemm_lds_kernel<FMT, WMN, WNN, WM, WN, GROUPED>), dim3((unsigned)tiles),
+  hipLaunchKernelGGL((gemm_lds_kernel<FMT, WMN, WNN, WM, WN, GROUPED, W4>), dim3((unsigned)tiles),
                      dim3(64 * WMN * WNN), 0, st, a.xq, a.xs, a.wq, a.ws,
                      GROUPED ? nullptr : a.bias, a.y, a.M, a.N, a.K, a.seg, a.E, gsel, part,
                      kbps);
@@ -639,13 +723,13 @@ struct Plan {
   int kbps;     // K blocks per split
 };
 
-Plan plan_dense(int64_t M, int64_t N, int64_t K) {
+Plan plan_dense(int64_t M, int64_t N, int64_t K, bool allow_big = true) {
   constexpr int64_t kCUs = 256;                 // MI355X compute units
   const double t_blk[2] = {2.15, 2.8};
   const int64_t KB = (K + 127) / 128;
   Plan best{0, 1, (int)KB};
   double best_t = 1e300;
-  for (int big = 0; big < 2; ++big) {
+  for (int big = 0; big < (allow_big ? 2 : 1); ++big) {
     const int64_t BM = big ? 256 : 128;
     const int64_t tiles = (M + BM - 1) / BM * ((N + 255) / 256);
     for (int64_t S = 1; S <= 32; S *= 2) {
@@ -677,6 +761,12 @@ hipError_t launch_lds(const GemmArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
     return launch_cfg<FMT, 1, 4, 64, 64, true>(a, st, 1, kb, 2);
   } else {
+    if (a.w4) {
+      // MXFP4 weights: 128 x 256 tiles (the scale registers of the 256 x 256
+      // tile would not fit beside its accumulators)
+      const Plan p = plan_dense(a.M, a.N, a.K, false);
+      return launch_cfg<FMT, 2, 4, 64, 64, false, true>(a, st, p.splits, p.kbps);
+    }
     const Plan p = plan_dense(a.M, a.N, a.K);
     if (p.big) return launch_cfg<FMT, 4, 2, 64, 128, false>(a, st, p.splits, p.kbps);
     return launch_cfg<FMT, 2, 4, 64, 64, false>(a, st, p.splits, p.kbps);
@@ -685,6 +775,12 @@ hipError_t launch_lds(const GemmArgs& a, hipStream_t st) {
 
 }  // namespace detail
 using namespace detail;
+
+size_t fp8_fp4_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= kDecodeMaxM || N <= 0 || K <= 0) return 0;
+  const Plan p = plan_dense(M, N, K, false);
+  return p.splits > 1 ? (size_t)p.splits * M * N * sizeof(float) : 0;
+}
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M <= kDecodeMaxM || N <= 0 || K <= 0) return 0;
@@ -717,14 +813,16 @@ int gemm_kind(int64_t M, int64_t N, int64_t K, int* splits) {
 template <int FMT>
 hipError_t launch_decode(const GemmArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)((a.N + 15) / 16));
+  const dim3 block(64 * kDecodeWaves);
   if (a.x_bf16)
-    hipLaunchKernelGGL((gemm_decode_kernel<FMT, true>), grid, dim3(64 * kDecodeWaves), 0, st,
-                       nullptr, nullptr, a.x_bf16, a.ldx, a.wq, a.ws, a.bias, a.y, (int)a.M,
-                       a.N, a.K);
+    hipLaunchKernelGGL((gemm_decode_kernel<FMT, true>), grid, block, 0, st, nullptr, nullptr,
+                       a.x_bf16, a.ldx, a.wq, a.ws, a.bias, a.y, (int)a.M, a.N, a.K);
+  else if (a.w4)
+    hipLaunchKernelGGL((gemm_decode_kernel<FMT, false, true>), grid, block, 0, st, a.xq, a.xs,
+                       nullptr, (int64_t)0, a.wq, a.ws, a.bias, a.y, (int)a.M, a.N, a.K);
   else
-    hipLaunchKernelGGL((gemm_decode_kernel<FMT, false>), grid, dim3(64 * kDecodeWaves), 0, st,
-                       a.xq, a.xs, nullptr, (int64_t)0, a.wq, a.ws, a.bias, a.y, (int)a.M, a.N,
-                       a.K);
+    hipLaunchKernelGGL((gemm_decode_kernel<FMT, false>), grid, block, 0, st, a.xq, a.xs, nullptr,
+                       (int64_t)0, a.wq, a.ws, a.bias, a.y, (int)a.M, a.N, a.K);
   return hipGetLastError();
 }
 

@@ -17,13 +17,14 @@ LIB_PATH = os.path.join(_HERE, "libbsfp8.so")
 OK, EINVAL, ENOTSUP, ENOSPC, EHIP = 0, 1, 2, 3, 4
 SCALE_FLOAT, SCALE_UE8M0 = 0, 1
 ACT_DYNAMIC, ACT_STATIC = 0, 1
-OP_BLOCK_GEMM, OP_LINEAR, OP_GROUPED_GEMM, OP_FP4_QUANT, OP_FP4_GEMM = 0, 1, 2, 3, 4
+OP_BLOCK_GEMM, OP_LINEAR, OP_GROUPED_GEMM, OP_FP4_QUANT, OP_FP4_GEMM, OP_FP8_FP4_GEMM = \
+    0, 1, 2, 3, 4, 5
 GEMM_NONE, GEMM_TILE_128x256, GEMM_TILE_256x256, GEMM_DECODE = 0, 2, 3, 4
 
 EXPORTS = ("bsfp8_version", "bsfp8_status_string", "bsfp8_workspace_size", "bsfp8_gemm_kernel",
            "fp8_quant_act", "fp8_quant_weight", "fp8_block_gemm", "fp8_linear",
            "fp8_grouped_gemm", "fp4_quant", "fp4_group_gemm", "fp8_dequant_weight",
-           "fp8_scale_to_ue8m0")
+           "fp8_scale_to_ue8m0", "mxfp4_quant_weight", "fp8_fp4_gemm")
 
 
 class BsFp8Error(RuntimeError):
@@ -46,6 +47,8 @@ _SIGS = {
     "bsfp8_gemm_kernel": (_I32, [_I64, _I64, _I64, _P]),
     "fp8_dequant_weight": (_I32, [_P, _I64, _I64, _I32, _I32, _I32, _P, _P, _P]),
     "fp8_scale_to_ue8m0": (_I32, [_P, _I64, _P, _P]),
+    "mxfp4_quant_weight": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P]),
+    "fp8_fp4_gemm": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _SZ, _P]),
     "fp8_quant_act": (_I32, [_P, _I64, _I64, _I64, _I32, _I32, _I32, _P, _P, _P]),
     "fp8_quant_weight": (_I32, [_P, _I64, _I64, _I64, _I32, _I32, _I32, _P, _P, _P]),
     "fp8_block_gemm": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32,
@@ -141,6 +144,25 @@ def fp8_scale_to_ue8m0(scale, out, stream=None):
     """scale: fp32 tensor; out: uint8 tensor of the same number of elements."""
     _check("fp8_scale_to_ue8m0", load().fp8_scale_to_ue8m0(_ptr(scale), scale.numel(),
                                                            _ptr(out), _stream(stream)))
+
+
+def mxfp4_quant_weight(w, wq4, w_scale, stream=None):
+    """w: bf16 (N, >=K); wq4: uint8 (N, K/2); w_scale: uint8 (N, K/32)."""
+    N, K = wq4.shape[0], wq4.shape[1] * 2
+    ldw = w.stride(0) if w.dim() == 2 else K
+    _check("mxfp4_quant_weight", load().mxfp4_quant_weight(_ptr(w), N, K, ldw, _ptr(wq4),
+                                                           _ptr(w_scale), _stream(stream)))
+
+
+def fp8_fp4_gemm(xq, x_scale, wq4, w_scale, y, bias=None, scale_fmt=SCALE_FLOAT,
+                 workspace=None, stream=None):
+    """xq: uint8 (M, K) E4M3; x_scale (M, K/128); wq4 (N, K/2); w_scale (N, K/32)."""
+    M, K = xq.shape
+    N = wq4.shape[0]
+    ws, wsb = _workspace(OP_FP8_FP4_GEMM, M, N, K, 0, workspace, xq.device)
+    _check("fp8_fp4_gemm", load().fp8_fp4_gemm(_ptr(xq), _ptr(x_scale), _ptr(wq4), _ptr(w_scale),
+                                               _ptr(bias), _ptr(y), M, N, K, scale_fmt, _ptr(ws), wsb,
+                                               _stream(stream)))
 
 
 def fp8_quant_weight(w, wq, w_scale_inv, block_n=128, block_k=128, scale_fmt=SCALE_FLOAT,

@@ -70,7 +70,8 @@ typedef enum {
   BSFP8_OP_LINEAR = 1,
   BSFP8_OP_GROUPED_GEMM = 2,
   BSFP8_OP_FP4_QUANT = 3,
-  BSFP8_OP_FP4_GEMM = 4
+  BSFP8_OP_FP4_GEMM = 4,
+  BSFP8_OP_FP8_FP4_GEMM = 5
 } bsfp8_op;
 
 /* Kernels fp8_block_gemm / fp8_linear choose between (bsfp8_gemm_kernel). */
@@ -244,6 +245,45 @@ BSFP8_API int32_t fp4_group_gemm(const void* xq4, const void* x_gscale,
                        const void* w_gscale, const float* w_tscale, void* y,
                        int64_t M, int64_t N, int64_t K, void* workspace,
                        size_t workspace_bytes, void* stream);
+
+/*
+ * mxfp4_quant_weight -- FP4-packed weights with UE8M0 block scales, the
+ * V4-style expert weights the pages' FP8-activation x FP4-weight linear
+ * consumes ([FG-FP8] §一 FP4-packed experts, §6.1 deepgemm_fp8_fp4_linear;
+ * UE8M0 scales §七).  Per 1 x 32 group along K of each row:
+ *   e = ceil(log2(amax/6)) clamped to [-127,127] (0 for amax = 0), stored
+ *   as the byte e+127;  codes = E2M1(w * 2^-e), round to nearest even.
+ *
+ *   w        bf16 [N][ldw], K % 32 == 0, ldw >= K, ldw % 8 == 0.
+ *   wq4      out, uint8 [N][K/2]: element 2i in the low nibble of byte i.
+ *   w_scale  out, E8M0 bytes [N][K/32].
+ * Errors: EINVAL (sizes, null pointers, misalignment).
+ */
+BSFP8_API int32_t mxfp4_quant_weight(const void* w, int64_t N, int64_t K, int64_t ldw,
+                                     void* wq4, void* w_scale, void* stream);
+
+/*
+ * fp8_fp4_gemm -- FP8 activations x MXFP4 weights ([FG-FP8] §6.1, the
+ * FP8 x FP4 linear), on gfx950's scaled MFMA with the weights as its FP4
+ * operand and their E8M0 group scales as its block scales:
+ *
+ *   Y[m][n] = bf16( sum_k E4M3(xq[m][k]) S_a[m][k/128]
+ *                         * E2M1(wq4[n][k]) 2^(w_scale[n][k/32]-127) + bias[n] )
+ *
+ *   xq, x_scale  as written by fp8_quant_act (1 x 128 groups; scale_fmt
+ *                FLOAT or UE8M0).
+ *   wq4, w_scale as written by mxfp4_quant_weight (N rows).
+ *   bias         bf16 [N] or NULL;  y out, bf16 [M][N].
+ *   K % 32 == 0, N % 8 == 0, K <= 2^22.
+ *   workspace    >= bsfp8_workspace_size(BSFP8_OP_FP8_FP4_GEMM, M, N, K, 0).
+ * M <= 16 streams the weights in one launch (half the bytes of FP8);
+ * larger M runs the LDS MFMA kernel on 128 x 256 tiles, K split as for
+ * fp8_block_gemm.  Errors as fp8_block_gemm (block sizes are fixed here).
+ */
+BSFP8_API int32_t fp8_fp4_gemm(const void* xq, const void* x_scale, const void* wq4,
+                               const void* w_scale, const void* bias, void* y, int64_t M,
+                               int64_t N, int64_t K, int32_t scale_fmt, void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 /*
  * fp8_dequant_weight -- fold the block scales back into the weights, the

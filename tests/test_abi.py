@@ -199,3 +199,28 @@ def test_dequant_and_ue8m0_argument_checks():
     assert c(FAKE, -1, FAKE, None) == L.EINVAL
     assert c(None, 4, FAKE, None) == L.EINVAL
     assert c(FAKE, 0, None, None) == L.OK
+
+
+def test_mxfp4_argument_checks():
+    lib = L.load()
+    q = lib.mxfp4_quant_weight
+    assert q(FAKE, 4, 48, 48, FAKE, FAKE, None) == L.EINVAL          # K % 32
+    assert q(FAKE, 4, 64, 60, FAKE, FAKE, None) == L.EINVAL          # ldw < K
+    assert q(FAKE, 4, 64, 68, FAKE, FAKE, None) == L.EINVAL          # ldw % 8
+    assert q(None, 4, 64, 64, FAKE, FAKE, None) == L.EINVAL
+    assert q(MIS, 4, 64, 64, FAKE, FAKE, None) == L.EINVAL
+    assert q(FAKE, -1, 64, 64, FAKE, FAKE, None) == L.EINVAL
+    assert q(None, 0, 64, 64, None, None, None) == L.OK
+    g = lib.fp8_fp4_gemm
+    args = [FAKE, FAKE, FAKE, FAKE, None, FAKE, 16, 256, 256, 0, None, 0, None]
+    for i, v, code in [(8, 48, L.EINVAL), (8, 2**22 + 32, L.ENOTSUP), (7, 12, L.EINVAL),
+                       (9, 2, L.EINVAL), (2, None, L.EINVAL), (3, MIS, L.EINVAL),
+                       (6, 0, L.OK), (6, -3, L.EINVAL)]:
+        a = list(args); a[i] = v
+        assert g(*a) == code, (i, v)
+    # M > 16 may split K: the workspace is checked like the FP8 GEMM's
+    need = L.workspace_size(L.OP_FP8_FP4_GEMM, 128, 4096, 4096)
+    assert need > 0
+    assert L.workspace_size(L.OP_FP8_FP4_GEMM, 16, 28672, 4096) == 0
+    a = list(args); a[6:9] = [128, 4096, 4096]; a[10] = FAKE; a[11] = need - 1
+    assert g(*a) == L.ENOSPC

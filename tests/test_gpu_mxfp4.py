@@ -1,0 +1,121 @@
+"""GPU parity of the MXFP4 weight quantizer (codes and UE8M0 group scales
+bit-exact) and of the FP8 x FP4 GEMM (within 2e-3 relative Frobenius error
+of the oracle's fp64 product of the dequantized operands)."""
+
+import numpy as np
+import pytest
+
+from block_scaled_precision_fp8_amd import synth
+from oracle import formats as F
+from oracle import mxfp4 as X
+from oracle import quant as Q
+
+from gpu_util import to_dev, to_dev_bf16, bf16_bits, u8, rel_fro, say
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+def _quant_dev(w_bits):
+    import torch
+    from block_scaled_precision_fp8_amd import lib as L
+    N, K = w_bits.shape
+    wd = to_dev_bf16(w_bits)
+    q = torch.full((N, K // 2), 0xEE, dtype=torch.uint8, device=wd.device)
+    s = torch.full((N, K // 32), 0xEE, dtype=torch.uint8, device=wd.device)
+    L.mxfp4_quant_weight(wd, q, s)
+    torch.cuda.synchronize()
+    return u8(q), u8(s)
+
+
+@pytest.mark.parametrize("N,K,sigma,seed", [(1, 32, 0.015, 0), (37, 4096, 0.015, 1),
+                                            (300, 1056, 1.0, 2), (8, 28672, 0.015, 3)])
+def test_mxfp4_quant_parity(N, K, sigma, seed):
+    say(f"mxfp4 quant N={N} K={K}")
+    w = synth.normal_bf16((N, K), sigma, "nvfp4", "w", seed=seed)
+    q, s = _quant_dev(w)
+    rq, rs = X.quant_weight_mxfp4(w)
+    assert np.array_equal(s, rs), f"{np.count_nonzero(s != rs)} scale mismatches"
+    assert np.array_equal(q, rq), f"{np.count_nonzero(q != rq)} code-byte mismatches"
+
+
+def test_mxfp4_quant_edges():
+    w = synth.normal_bf16((4, 128), 0.015, "nvfp4", "w", seed=4)
+    w[0, :32] = 0                                             # zero group
+    w[0, 32:64] = 0x8000                                      # negative zeros
+    w[1, :32] = np.arange(1, 33, dtype=np.uint16)             # bf16 subnormals
+    w[1, 32:64] = synth.f32_to_bf16_bits(np.float32([3e38, -1e38] * 16))
+    w[2, :32] = synth.f32_to_bf16_bits(np.float32([6.0, -0.25, 0.75, 2.5] * 8))   # ties at e = 0
+    q, s = _quant_dev(w)
+    rq, rs = X.quant_weight_mxfp4(w)
+    assert np.array_equal(s, rs) and np.array_equal(q, rq)
+
+
+def _gemm(M, N, K, fmt, bias=False, seed=0):
+    import torch
+    from block_scaled_precision_fp8_amd import lib as L
+    x = synth.deepseek_acts(M, K, seed=seed) if fmt else synth.llama_acts(M, K, seed=seed)
+    w = synth.normal_bf16((N, K), 0.015, "nvfp4", "w", seed=seed + 1)
+    b = synth.normal_bf16((N,), 0.5, "llama", "bias", seed=seed) if bias else None
+    xq, xs = Q.quant_act(x, 128, fmt)
+    wq, ws = X.quant_weight_mxfp4(w)
+    yf = torch.full((M * N + 64,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    y = yf[:M * N].view(M, N)
+    L.fp8_fp4_gemm(to_dev(xq), to_dev(xs), to_dev(wq), to_dev(ws), y,
+                   bias=None if b is None else to_dev_bf16(b), scale_fmt=fmt)
+    torch.cuda.synchronize()
+    assert torch.isnan(yf[M * N:].float()).all(), "wrote past the output"
+    got = F.bf16_decode(bf16_bits(y))
+    ref = X.fp8_fp4_gemm(xq, xs, wq, ws, bias=None if b is None else F.bf16_decode(b), fmt=fmt)
+    return got, ref
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("M,N,K,bias", [
+    (1, 256, 256, False), (5, 264, 288, True), (16, 1000, 1024, False), (17, 520, 4128, True),
+    (64, 256, 2048, False), (130, 520, 640, True), (300, 1000, 1056, False), (1024, 1024, 1024, True),
+])
+def test_fp8_fp4_gemm_parity(M, N, K, bias, fmt):
+    say(f"fp8 x fp4 gemm M={M} N={N} K={K} fmt={fmt}")
+    got, ref = _gemm(M, N, K, fmt, bias, seed=M + N)
+    assert np.isfinite(got).all(), "unwritten outputs"
+    err = rel_fro(got, ref)
+    say(f"  rel fro {err:.3e}  vs bf16(ref) {rel_fro(got, F.bf16_round(ref)):.3e}")
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("M,K,N,fmt", [(1, 7168, 18432, 1), (16, 4096, 28672, 0), (4096, 7168, 4096, 1)])
+def test_fp8_fp4_gemm_full_size_sampled(M, K, N, fmt):
+    """Full-size shapes; the oracle recomputes 2048 sampled outputs."""
+    import torch
+    from block_scaled_precision_fp8_amd import lib as L
+    say(f"fp8 x fp4 full-size M={M} K={K} N={N} fmt={fmt}")
+    x = synth.deepseek_acts(M, K, seed=2) if fmt else synth.llama_acts(M, K, seed=2)
+    wdev = synth.device_normal_bf16((N, K), 0.015, "nvfp4", "w", index=N)
+    xd = to_dev_bf16(x)
+    sdt = torch.float32 if fmt == 0 else torch.uint8
+    xq = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    xs = torch.empty((M, K // 128), dtype=sdt, device="cuda")
+    wq = torch.empty((N, K // 2), dtype=torch.uint8, device="cuda")
+    ws = torch.empty((N, K // 32), dtype=torch.uint8, device="cuda")
+    L.fp8_quant_act(xd, xq, xs, scale_fmt=fmt)
+    L.mxfp4_quant_weight(wdev, wq, ws)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    L.fp8_fp4_gemm(xq, xs, wq, ws, y, scale_fmt=fmt)
+    torch.cuda.synchronize()
+    g = np.random.default_rng(M + N)
+    rows, cols = g.integers(0, M, 2048), g.integers(0, N, 2048)
+    ur, uc = np.unique(rows), np.unique(cols)
+    hx, hxs = Q.quant_act(x[ur], 128, fmt)
+    hw, hws = X.quant_weight_mxfp4(bf16_bits(wdev)[uc])
+    from oracle import gemm as G
+    A = G.dequant_act(hx, hxs, 128, fmt)
+    B = X.dequant_mxfp4(hw, hws)
+    ref = np.einsum("ik,ik->i", A[np.searchsorted(ur, rows)], B[np.searchsorted(uc, cols)])
+    got = F.bf16_decode(bf16_bits(y))[rows, cols]
+    err = rel_fro(got, ref)
+    say(f"  sampled rel fro {err:.3e}")
+    assert err <= TOL
+    # the device-quantized weights of the sampled rows equal the oracle's
+    assert np.array_equal(u8(wq)[uc], hw) and np.array_equal(u8(ws)[uc], hws)
