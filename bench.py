@@ -17,7 +17,8 @@ then fp8_block_gemm, the two launches fp8_linear makes for them.
 The other rows of the path are timed in the same run and reported in
 ``detail`` (not in ``value``): DeepSeek-V3-shaped linears with UE8M0 scales,
 the MoE grouped GEMMs (256 experts, Zipf-routed top-8), the NVFP4-style MLP
-(fp4_quant + fp4_group_gemm) with its FP8 attention projection, and weight
+(fp4_quant + fp4_group_gemm) with its FP8 attention projection, the FP8
+activation x MXFP4 weight linear at DeepSeek-V3 expert shapes, and weight
 quantization.
 
 ``roofline`` is for the dominant kernel, the large-M GEMM with 256 x 256 tiles
@@ -383,6 +384,65 @@ def run_nvfp4(torch, L, synth, steps, warmup, dev, sp):
     return out
 
 
+def run_mxfp4(torch, L, synth, steps, warmup, dev, sp):
+    """FP8 activations (1x128 groups, UE8M0 scales) x MXFP4 weights (E2M1 in
+    1x32 groups with UE8M0 scales) at the DeepSeek-V3 expert-sized shapes
+    (7168 -> 18432, 18432 -> 7168), M in {1, 64, 4096}: act quant then
+    fp8_fp4_gemm.  Two weight copies alternate so decode reads HBM."""
+    out = []
+    stream = torch.cuda.current_stream()
+    for K, N in ((7168, 18432), (18432, 7168)):
+        copies = []
+        for c in range(2):
+            wb = synth.device_normal_bf16((N, K), 0.01, "deepseek", "w", index=N + 17 * c)
+            q = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+            s = torch.empty((N, K // 32), dtype=torch.uint8, device=dev)
+            L.mxfp4_quant_weight(wb, q, s, stream=sp)
+            del wb
+            copies.append((q, s))
+        for M in (1, 64, 4096):
+            x = synth.device_deepseek_acts(M, K, index=M)
+            xq = torch.empty((M, K), dtype=torch.uint8, device=dev)
+            xs = torch.empty((M, K // 128), dtype=torch.uint8, device=dev)
+            y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            need = L.workspace_size(L.OP_FP8_FP4_GEMM, M, N, K)
+            wsp = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+
+            def call(i, tm=None):
+                q, sc = copies[i & 1]
+                if tm:
+                    tm.mark("a")
+                L.fp8_quant_act(x, xq, xs, scale_fmt=L.SCALE_UE8M0, stream=sp)
+                if tm:
+                    tm.mark("b")
+                L.fp8_fp4_gemm(xq, xs, q, sc, y, scale_fmt=L.SCALE_UE8M0, workspace=wsp,
+                               stream=sp)
+                if tm:
+                    tm.mark("c")
+            for i in range(warmup):
+                call(i)
+            torch.cuda.synchronize()
+            tm = Timer(torch, stream)
+            for i in range(steps):
+                call(i, tm)
+            torch.cuda.synchronize()
+            qm, gm = tm.ms("a", "b"), tm.ms("b", "c")
+            fl = 2.0 * M * N * K
+            gb = N * (K // 2 + K // 32) + M * (K + K // 128) + 2 * M * N
+            d = dict(M=M, K=K, N=N, quant_us=round(qm * 1e3, 2), gemm_us=round(gm * 1e3, 2),
+                     tflops_incl_quant=round(fl / ((qm + gm) * 1e-3) / 1e12, 1),
+                     gemm_tflops=round(fl / (gm * 1e-3) / 1e12, 1),
+                     frac_fp8_peak=round(fl / (gm * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+                     gemm_gbs=round(gb / (gm * 1e-3) / 1e9, 1),
+                     frac_hbm=round(gb / (gm * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
+            out.append(d)
+            log(f"[mxfp4] {d}")
+            del x, xq, xs, y, wsp
+        del copies
+        torch.cuda.empty_cache()
+    return out
+
+
 def run_wquant(torch, L, synth, steps, warmup, dev, sp):
     """Weight quantization (load-time step) of the 28672 x 4096 weight."""
     N, K = 28672, 4096
@@ -450,7 +510,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--suites", default="deepseek,moe,nvfp4,wquant",
+    ap.add_argument("--suites", default="deepseek,moe,nvfp4,mxfp4,wquant",
                     help="extra rows timed for `detail` (comma list, or 'none')")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a known-size "
@@ -505,6 +565,9 @@ def main():
     if "nvfp4" in suites:
         detail["nvfp4_mlp_fp8_attn"] = run_nvfp4(torch, L, synth, max(5, args.steps // 2), 2,
                                                  dev, sp)
+    if "mxfp4" in suites:
+        detail["fp8_x_mxfp4_ue8m0"] = run_mxfp4(torch, L, synth, max(5, args.steps // 2), 2,
+                                                dev, sp)
     if "wquant" in suites:
         detail["weight_quant"] = run_wquant(torch, L, synth, 10, 2, dev, sp)
 

@@ -519,8 +519,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 // Decode kernel (M <= 16): one workgroup owns 16 weight rows over the whole
 // K range and its kDecodeWaves waves take the K blocks round-robin.  Each
 // lane streams its 32 weight bytes per block straight from HBM with
-// kDecodeDepth blocks of loads in flight, the activation fragment (one
-// token row per lane column) comes from L2, and the waves' partial 16 x 16
+// kDecodeDepth blocks of loads in flight, the quantized activation
+// fragment (one token row per lane column) and both block scales are
+// fetched together with those weights, and the waves' partial 16 x 16
 // tiles are summed through LDS: one launch, no workspace.  FUSED: the 1x128
 // activation quantization runs in the same launch -- each lane encodes its
 // 32 activations of the block with the group amax gathered from the four
@@ -533,8 +534,10 @@ constexpr int kDecodeWaves = 16;
 constexpr int kDecodeDepth = 2;
 
 // W4: W holds MXFP4 codes (N, K/2) with E8M0 scales per 1 x 32 group
-// (N, K/32): each lane streams 16 weight bytes per block and takes the X
-// chunks g4 and g4 + 4 (the FP4 x FP8 lane pairing of the scaled MFMA).
+// (N, K/32): each lane streams 16 weight bytes and one scale byte per block
+// and takes the X chunks g4 and g4 + 4 (the FP4 x FP8 lane pairing of the
+// scaled MFMA).  The kernel is bound by the latency of each workgroup's one
+// round of loads, not by bytes, so MXFP4 rows run at about the FP8 time.
 template <int FMT, bool FUSED, bool W4 = false>
 __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
     const uint8_t* __restrict__ xq, const void* __restrict__ xs,
@@ -558,27 +561,55 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
   const int kx0 = W4 ? 16 * g4 : 32 * g4;
   const int kx1 = W4 ? 64 + 16 * g4 : 32 * g4 + 16;
 
+  constexpr int DEPTH = kDecodeDepth;
+  constexpr int XD = FUSED ? 1 : DEPTH;    // X fragments prefetched with W
   v4f acc = {0.f, 0.f, 0.f, 0.f};
-  for (int kb0 = wave; kb0 < KB; kb0 += kDecodeWaves * kDecodeDepth) {
-    uint4 wa[kDecodeDepth], wb[kDecodeDepth];
+  for (int kb0 = wave; kb0 < KB; kb0 += kDecodeWaves * DEPTH) {
+    uint4 wa[DEPTH], wb[DEPTH];
+    int sw4[DEPTH];
+    float swb[DEPTH];
+    uint4 xa[XD], xb[XD];
+    float sx[XD];
 #pragma unroll
-    for (int u = 0; u < kDecodeDepth; ++u) {
+    for (int u = 0; u < DEPTH; ++u) {
       const int kb = kb0 + u * kDecodeWaves;
       wa[u] = make_uint4(0, 0, 0, 0);
       wb[u] = make_uint4(0, 0, 0, 0);
+      sw4[u] = 127;
+      // the weight block scale: with fp32 scales it multiplies this lane's
+      // OUTPUT column (token l16), so every lane needs it, whatever its row
+      swb[u] = (FMT == 0) ? 0.f : __int_as_float(127);
+      if (!W4 && kb < KB) swb[u] = load_scale<FMT>(wsc, nblk * KB + kb);
       if (kb < KB && nvalid) {
         if constexpr (W4) {
+          // this lane's 32 weights (group 4 kb + g4) and their scale byte
           const int64_t kw = (int64_t)kb * 64 + g4 * 16;
-          if (kw < KW) wa[u] = ld_stream16(wrow + kw);
+          if (kw < KW) {
+            wa[u] = ld_stream16(wrow + kw);
+            sw4[u] = (int)((const uint8_t*)wsc)[nrow * G32 + (int64_t)kb * 4 + g4];
+          }
         } else {
           const int64_t k = (int64_t)kb * 128 + g4 * 32;
           if (k < K) wa[u] = ld_stream16(wrow + k);
           if (k + 16 < K) wb[u] = ld_stream16(wrow + k + 16);
         }
       }
+      if constexpr (!FUSED) {
+        // the quantized X fragment and its scale (L2-resident), issued with
+        // the weight loads so their latencies overlap
+        xa[u] = make_uint4(0, 0, 0, 0);
+        xb[u] = make_uint4(0, 0, 0, 0);
+        sx[u] = (FMT == 0) ? 0.f : __int_as_float(127);
+        if (kb < KB && mvalid) {
+          const int64_t k0 = (int64_t)kb * 128 + kx0, k1 = (int64_t)kb * 128 + kx1;
+          if (k0 < K) xa[u] = *(const uint4*)(xq + (int64_t)l16 * K + k0);
+          if (k1 < K) xb[u] = *(const uint4*)(xq + (int64_t)l16 * K + k1);
+          sx[u] = load_scale<FMT>(xs, (int64_t)l16 * KB + kb);
+        }
+      }
     }
 #pragma unroll
-    for (int u = 0; u < kDecodeDepth; ++u) {
+    for (int u = 0; u < DEPTH; ++u) {
       const int kb = kb0 + u * kDecodeWaves;
       if (kb >= KB) break;
       const int64_t k0 = (int64_t)kb * 128 + kx0, k1 = (int64_t)kb * 128 + kx1;
@@ -614,23 +645,13 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
                                             r, e);
         sa = FMT == 0 ? s : __int_as_float(e + 127);
       } else {
-        uint4 xa = make_uint4(0, 0, 0, 0), xb = make_uint4(0, 0, 0, 0);
-        sa = (FMT == 0) ? 0.f : __int_as_float(127);
-        if (mvalid) {
-          if (k0 < K) xa = *(const uint4*)(xq + (int64_t)l16 * K + k0);
-          if (k1 < K) xb = *(const uint4*)(xq + (int64_t)l16 * K + k1);
-          sa = load_scale<FMT>(xs, (int64_t)l16 * KB + kb);
-        }
-        bx = join(xa, xb);
+        sa = sx[u < XD ? u : 0];
+        bx = join(xa[u < XD ? u : 0], xb[u < XD ? u : 0]);
       }
-      if constexpr (W4) {
-        const int64_t gi = (int64_t)kb * 4 + g4;
-        const int sw4 = (nvalid && gi < G32) ? (int)((const uint8_t*)wsc)[nrow * G32 + gi] : 127;
-        acc = mfma_step_w4<FMT>(acc, join(wa[u], wb[u]), bx, sa, sw4);
-      } else {
-        const float sw = load_scale<FMT>(wsc, nblk * KB + kb);
-        acc = mfma_step<FMT>(acc, join(wa[u], wb[u]), bx, sa, sw);
-      }
+      if constexpr (W4)
+        acc = mfma_step_w4<FMT>(acc, join(wa[u], make_uint4(0, 0, 0, 0)), bx, sa, sw4[u]);
+      else
+        acc = mfma_step<FMT>(acc, join(wa[u], wb[u]), bx, sa, swb[u]);
     }
   }
   red[wave][lane] = acc;
@@ -656,6 +677,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
   BSFP8_INST(FMT, 4, 2, 64, 128, false, false) \
   BSFP8_INST(FMT, 2, 4, 64, 64, false, false)  \
   BSFP8_INST(FMT, 2, 4, 64, 64, false, true)   \
+  BSFP8_INST(FMT, 4, 2, 64, 128, false, true)  \
   BSFP8_INST(FMT, 1, 4, 64, 64, true, false)   \
   BSFP8_INST(FMT, 4, 2, 64, 128, true, false)
 BSFP8_INST_ALL(0)
@@ -762,9 +784,8 @@ hipError_t launch_lds(const GemmArgs& a, hipStream_t st) {
     return launch_cfg<FMT, 1, 4, 64, 64, true>(a, st, 1, kb, 2);
   } else {
     if (a.w4) {
-      // MXFP4 weights: 128 x 256 tiles (the scale registers of the 256 x 256
-      // tile would not fit beside its accumulators)
-      const Plan p = plan_dense(a.M, a.N, a.K, false);
+      const Plan p = plan_dense(a.M, a.N, a.K);
+      if (p.big) return launch_cfg<FMT, 4, 2, 64, 128, false, true>(a, st, p.splits, p.kbps);
       return launch_cfg<FMT, 2, 4, 64, 64, false, true>(a, st, p.splits, p.kbps);
     }
     const Plan p = plan_dense(a.M, a.N, a.K);
@@ -778,7 +799,7 @@ using namespace detail;
 
 size_t fp8_fp4_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M <= kDecodeMaxM || N <= 0 || K <= 0) return 0;
-  const Plan p = plan_dense(M, N, K, false);
+  const Plan p = plan_dense(M, N, K);
   return p.splits > 1 ? (size_t)p.splits * M * N * sizeof(float) : 0;
 }
 
