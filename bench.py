@@ -16,10 +16,11 @@ then fp8_block_gemm, the two launches fp8_linear makes for them.
 
 The other rows of the path are timed in the same run and reported in
 ``detail`` (not in ``value``): DeepSeek-V3-shaped linears with UE8M0 scales,
-the MoE grouped GEMMs (256 experts, Zipf-routed top-8), the NVFP4-style MLP
-(fp4_quant + fp4_group_gemm) with its FP8 attention projection, the FP8
-activation x MXFP4 weight linear at DeepSeek-V3 expert shapes, and weight
-quantization.
+the MoE expert MLP (256 experts, Zipf-routed top-8: gate/up grouped GEMM,
+the same with the fused SiLU-mul requant, the down GEMM on its output), the
+NVFP4-style MLP (fp4_quant + fp4_group_gemm) with its FP8 attention
+projection, the FP8 activation x MXFP4 weight linear at DeepSeek-V3 expert
+shapes, and weight quantization.
 
 ``roofline`` is for the dominant kernel, the large-M GEMM with 256 x 256 tiles
 (gemm_lds_kernel, every run the library sends to it, split-K ones included
@@ -236,54 +237,72 @@ def run_linears(torch, L, synth, shapes, ms, fmt, workload, steps, warmup, dev, 
 
 
 def run_moe(torch, L, synth, steps, warmup, dev, sp):
-    """MoE grouped GEMMs: gate/up (256 x (7168 -> 4096)) on the routed token
-    rows, down (256 x (2048 -> 7168)) on synthetic expert activations."""
+    """MoE expert MLP (256 experts, hidden 7168, intermediate 2048, 4096
+    tokens routed top-8 by Zipf popularity): the gate/up grouped GEMM
+    (7168 -> 2 x 2048) alone and with the fused SiLU-mul + 1x128 requant
+    epilogue, and the down grouped GEMM (2048 -> 7168) on that epilogue's
+    FP8 output; ``ffn_us`` is act quant + fused gate/up + down."""
     E, H, I, TOK, TOPK = 256, 7168, 2048, 4096, 8
     tok, off = synth.moe_routing(TOK, E, TOPK)
     T = len(tok)
     seg = torch.from_numpy(off).to(dev)
     x = synth.device_normal_bf16((TOK, H), 1.0, "moe", "x")[torch.from_numpy(tok).to(dev)]
-    h = synth.device_normal_bf16((T, I), 1.0, "moe", "h")
-    res = {}
     counts = (off[1:] - off[:-1])
-    for name, xin, N, K in (("gate_up", x, 2 * I, H), ("down", h, H, I)):
+    nb = int((counts > 0).sum())
+    W = {}
+    for name, N, K in (("gate_up", 2 * I, H), ("down", H, I)):
         wq = torch.empty((E, N, K), dtype=torch.uint8, device=dev)
         ws = torch.empty((E, N // 128, K // 128), dtype=torch.float32, device=dev)
         for e in range(E):
             wb = synth.device_normal_bf16((N, K), 0.02, "moe", "w" if name == "gate_up" else "w2", e)
             L.fp8_quant_weight(wb, wq[e], ws[e])
             del wb
-        xq = torch.empty((T, K), dtype=torch.uint8, device=dev)
-        xs = torch.empty((T, K // 128), dtype=torch.float32, device=dev)
-        y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
-        torch.cuda.synchronize()
-        stream = torch.cuda.current_stream()
-        for _ in range(warmup):
-            L.fp8_quant_act(xin, xq, xs, stream=sp)
-            L.fp8_grouped_gemm(xq, xs, wq, ws, seg, y, stream=sp)
-        torch.cuda.synchronize()
-        tm = Timer(torch, stream)
-        for _ in range(steps):
-            tm.mark("q")
-            L.fp8_quant_act(xin, xq, xs, stream=sp)
-            tm.mark("g")
-            L.fp8_grouped_gemm(xq, xs, wq, ws, seg, y, stream=sp)
-            tm.mark("e")
-        torch.cuda.synchronize()
-        qm, gm = tm.ms("q", "g"), tm.ms("g", "e")
+        W[name] = (wq, ws)
+    xq = torch.empty((T, H), dtype=torch.uint8, device=dev)
+    xs = torch.empty((T, H // 128), dtype=torch.float32, device=dev)
+    y1 = torch.empty((T, 2 * I), dtype=torch.bfloat16, device=dev)
+    hq = torch.empty((T, I), dtype=torch.uint8, device=dev)
+    hs = torch.empty((T, I // 128), dtype=torch.float32, device=dev)
+    y2 = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(tm=None):
+        mark = tm.mark if tm else (lambda k: None)
+        mark("q")
+        L.fp8_quant_act(x, xq, xs, stream=sp)
+        mark("g")
+        L.fp8_grouped_gemm(xq, xs, W["gate_up"][0], W["gate_up"][1], seg, y1, stream=sp)
+        mark("f")
+        L.fp8_grouped_gemm_silu_mul_quant(xq, xs, W["gate_up"][0], W["gate_up"][1], seg, hq, hs,
+                                          stream=sp)
+        mark("d")
+        L.fp8_grouped_gemm(hq, hs, W["down"][0], W["down"][1], seg, y2, stream=sp)
+        mark("e")
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    tm = Timer(torch, stream)
+    for _ in range(steps):
+        step(tm)
+    torch.cuda.synchronize()
+    qm, gm, fm, dm = tm.ms("q", "g"), tm.ms("g", "f"), tm.ms("f", "d"), tm.ms("d", "e")
+
+    def row(ms, N, K, out_bytes):
         fl = 2.0 * T * N * K
-        nb = int((counts > 0).sum())
-        wbytes = nb * (N * K + 4 * (N // 128) * (K // 128))
-        gb = wbytes + T * (K + 4 * (K // 128) + 2 * N)
-        res[name] = dict(T=T, N=N, K=K, experts=E, nonempty=nb, quant_us=round(qm * 1e3, 1),
-                         gemm_us=round(gm * 1e3, 1),
-                         gemm_tflops=round(fl / (gm * 1e-3) / 1e12, 1),
-                         gemm_gbs=round(gb / (gm * 1e-3) / 1e9, 1),
-                         frac_hbm=round(gb / (gm * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
-        log(f"[moe {name}] T={T} N={N} K={K}: quant {qm*1e3:.1f} us, grouped gemm {gm*1e3:.1f} us "
-            f"({res[name]['gemm_tflops']} TF/s, {res[name]['gemm_gbs']} GB/s)")
-        del wq, ws, xq, xs, y
-        torch.cuda.empty_cache()
+        gb = nb * (N * K + 4 * (N // 128) * (K // 128)) + T * (K + 4 * (K // 128)) + out_bytes
+        return dict(T=T, N=N, K=K, experts=E, nonempty=nb, us=round(ms * 1e3, 1),
+                    tflops=round(fl / (ms * 1e-3) / 1e12, 1),
+                    gbs=round(gb / (ms * 1e-3) / 1e9, 1),
+                    frac_hbm=round(gb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
+    res = {"act_quant_us": round(qm * 1e3, 1),
+           "gate_up": row(gm, 2 * I, H, 2 * T * 2 * I),
+           "gate_up_silu_mul_quant": row(fm, 2 * I, H, T * I + 4 * T * (I // 128)),
+           "down": row(dm, H, I, 2 * T * H),
+           "ffn_us": round((qm + fm + dm) * 1e3, 1)}
+    log(f"[moe] T={T}: act quant {qm*1e3:.1f} us, gate/up {gm*1e3:.1f} us, fused gate/up + "
+        f"silu-mul quant {fm*1e3:.1f} us, down {dm*1e3:.1f} us, ffn {res['ffn_us']} us")
+    del W, xq, xs, y1, hq, hs, y2
+    torch.cuda.empty_cache()
     res["rows_per_expert"] = dict(max=int(counts.max()), median=float(np.median(counts)),
                                   min=int(counts.min()))
     return res

@@ -134,6 +134,10 @@ struct GemmArgs {
   int64_t ldx;
   // MXFP4 weights: wq (N, K/2) E2M1 codes, ws (N, K/32) E8M0 bytes
   bool w4;
+  // grouped gate/up GEMM with the SiLU-mul requant epilogue: h codes
+  // (M, N/2) and scales (M, N/256); y is then the optional bf16 h
+  uint8_t* hq;
+  void* hs;
 };
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
@@ -144,6 +148,7 @@ bool linear_fused(int64_t M, int64_t N);   // fp8_linear quantizes inside the GE
 size_t grouped_workspace_bytes(int64_t T, int64_t N, int64_t K, int E);
 hipError_t launch_block_gemm(const GemmArgs& a, hipStream_t s);
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t s);
+hipError_t launch_grouped_silu_mul_quant(const GemmArgs& a, hipStream_t s);
 
 size_t fp4_quant_workspace_bytes(int64_t R, int64_t K);
 size_t fp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);

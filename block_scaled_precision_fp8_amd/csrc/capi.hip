@@ -304,6 +304,31 @@ int32_t fp8_grouped_gemm(const void* xq, const void* x_scale, const void* wq,
   return hip_status(launch_grouped_gemm(a, (hipStream_t)stream));
 }
 
+int32_t fp8_grouped_gemm_silu_mul_quant(const void* xq, const void* x_scale, const void* wq,
+                                        const void* w_scale_inv, const int32_t* seg_offsets,
+                                        int32_t E, void* hq, void* h_scale, void* h_bf16,
+                                        int64_t T, int64_t I, int64_t K, int32_t scale_fmt,
+                                        void* stream) {
+  if (E < 1 || E > 1024) return BSFP8_EINVAL;
+  if (I <= 0 || I % 128 != 0 || !fits_i32(2 * I)) return BSFP8_EINVAL;
+  int32_t r = check_gemm(xq, x_scale, wq, w_scale_inv, nullptr, hq, T, 2 * I, K, 128, 128,
+                         scale_fmt);
+  if (r != BSFP8_OK) return r;
+  if (T == 0) return BSFP8_OK;
+  if (!seg_offsets || ((uintptr_t)seg_offsets & 3u)) return BSFP8_EINVAL;
+  if (!h_scale || ((uintptr_t)h_scale & 3u)) return BSFP8_EINVAL;
+  if (h_bf16 && !al16(h_bf16)) return BSFP8_EINVAL;
+  if (!fits_i32(((T + 127) / 128 + E) * (I / 128))) return BSFP8_EINVAL;
+  r = check_device(stream);
+  if (r != BSFP8_OK) return r;
+  GemmArgs a{};
+  a.xq = (const uint8_t*)xq; a.xs = x_scale; a.wq = (const uint8_t*)wq; a.ws = w_scale_inv;
+  a.bias = nullptr; a.y = (uint16_t*)h_bf16; a.M = T; a.N = 2 * I; a.K = K; a.fmt = scale_fmt;
+  a.seg = seg_offsets; a.E = E;
+  a.hq = (uint8_t*)hq; a.hs = h_scale;
+  return hip_status(launch_grouped_silu_mul_quant(a, (hipStream_t)stream));
+}
+
 int32_t fp4_quant(const void* x, int64_t R, int64_t K, int32_t dynamic_tscale, void* q4,
                   void* gscale, float* tscale, void* workspace, size_t workspace_bytes,
                   void* stream) {

@@ -232,6 +232,113 @@ __device__ __forceinline__ v8i read_frag(const uint8_t* __restrict__ row, int ch
   return join(*(const uint4*)(row + ch0), *(const uint4*)(row + ch1));
 }
 
+// SiLU(gate) * up with the 1 x 128 requantization, for a gate/up tile of
+// the grouped GEMM (the step between an MoE expert's gate/up and down
+// GEMMs).  Waves wn < WAVES_N / 2 hold the gate values of h columns
+// c0 + (wn WN .. wn WN + WN), wave wn + WAVES_N / 2 the up values of the same
+// columns in the same lane layout: the up waves hand their accumulators over
+// through the (drained) LDS stage buffers, each gate lane forms
+// h = silu(g) u in fp32 and rounds it to bf16, and the 128 columns of a token
+// row -- one activation group -- are quantized with the activation codec:
+// amax over the lanes (and waves) that share the row, then the scale and the
+// codes fp8_quant_act would write for that bf16 row.  h_bf16 (nullable)
+// receives the rounded h.
+template <int FMT, int WAVES_M, int WAVES_N, int WM, int WN>
+__device__ __forceinline__ void swiglu_epilogue(v4f (&acc)[WN / 16][WM / 16], uint8_t* lds,
+                                                const Tile& tl, int wm, int wn, int lane,
+                                                int64_t I, int64_t c0, uint16_t* h_bf16,
+                                                uint8_t* hq, void* hs) {
+  constexpr int NI = WN / 16, MI = WM / 16;
+  constexpr int HALF = WAVES_N / 2;
+  constexpr int XCH = WAVES_M * HALF * NI * MI * 64 * 16;   // bytes of handed-over tiles
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const bool upw = wn >= HALF;
+  const int pair = wm * HALF + (wn % HALF);
+  v4f* xch = (v4f*)lds + (int64_t)pair * NI * MI * 64;
+  float* amx = (float*)(lds + XCH);                    // [WAVES_M][HALF][MI][16]
+  __syncthreads();        // every DMA landed, every fragment read done
+  if (upw) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int j = 0; j < MI; ++j) xch[(i * MI + j) * 64 + lane] = acc[i][j];
+  }
+  __syncthreads();
+  // h of one accumulator tile: bf16(silu(g) * u), as a float
+  auto h4 = [&](int i, int j) -> v4f {
+    const v4f u = xch[(i * MI + j) * 64 + lane];
+    v4f h;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float g = acc[i][j][q];
+      h[q] = __uint_as_float(f32_to_bf16(g / (1.0f + expf(-g)) * u[q]) << 16);
+    }
+    return h;
+  };
+  // pass 1: the row maxima of |h| (acc stays read-only: both passes form h)
+  float amax[MI];
+#pragma unroll
+  for (int j = 0; j < MI; ++j) amax[j] = 0.0f;
+  if (!upw) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+#pragma unroll
+      for (int j = 0; j < MI; ++j) {
+        const v4f h = h4(i, j);
+        amax[j] = fmaxf(amax[j], fmaxf(fmaxf(fabsf(h[0]), fabsf(h[1])),
+                                       fmaxf(fabsf(h[2]), fabsf(h[3]))));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int j = 0; j < MI; ++j) {
+      amax[j] = fmaxf(amax[j], __shfl_xor(amax[j], 16));
+      amax[j] = fmaxf(amax[j], __shfl_xor(amax[j], 32));
+    }
+    if (HALF > 1 && g4 == 0) {
+#pragma unroll
+      for (int j = 0; j < MI; ++j) amx[((wm * HALF + wn) * MI + j) * 16 + l16] = amax[j];
+    }
+  }
+  if constexpr (HALF > 1) {
+    __syncthreads();
+    if (!upw) {
+#pragma unroll
+      for (int j = 0; j < MI; ++j)
+#pragma unroll
+        for (int h2 = 0; h2 < HALF; ++h2)
+          amax[j] = fmaxf(amax[j], amx[((wm * HALF + h2) * MI + j) * 16 + l16]);
+    }
+  }
+  if (upw) return;
+  // pass 2: scales, codes, stores
+  const int64_t G = I / 128;
+#pragma unroll
+  for (int j = 0; j < MI; ++j) {
+    const int64_t m = tl.m0 + wm * WM + j * 16 + l16;
+    if (m >= tl.mlim) continue;
+    const float s = FMT == 0 ? act_scale_f32(amax[j]) : 0.0f;
+    const int e = FMT == 0 ? 0 : ue8m0_exp(amax[j]);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int64_t c = c0 + wn * WN + i * 16 + 4 * g4;
+      const v4f v = h4(i, j);
+      *(uint32_t*)(hq + m * I + c) = act_encode4<FMT>(v[0], v[1], v[2], v[3], s, e);
+      if (h_bf16) {
+        uint2 o;
+        o.x = (__float_as_uint(v[0]) >> 16) | (__float_as_uint(v[1]) & 0xffff0000u);
+        o.y = (__float_as_uint(v[2]) >> 16) | (__float_as_uint(v[3]) & 0xffff0000u);
+        *(uint2*)(h_bf16 + m * I + c) = o;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (wn == 0 && g4 == 0) {
+      if (FMT == 0) ((float*)hs)[m * G + c0 / 128] = s;
+      else ((uint8_t*)hs)[m * G + c0 / 128] = (uint8_t)(e + 127);
+    }
+  }
+}
+
 // Workgroup tile BM x BN = (WAVES_M * WM) x (WAVES_N * WN), K step 128 (one
 // scale block).  Operands go global -> LDS directly (buffer_load ... lds,
 // 16 bytes per lane), double-buffered; in LDS every 128-byte row keeps
@@ -249,12 +356,13 @@ __device__ __forceinline__ v8i read_frag(const uint8_t* __restrict__ row, int ch
 // takes chunk g4, the weights K 32 g4 .. 32 g4 + 31, which the MFMA pairs
 // with the X chunks g4 and g4 + 4 of the FP8 operand (the lane layout of
 // the FP4 x FP8 form, checked on the GPU), and passes its own group's scale.
-template <int FMT, int WAVES_M, int WAVES_N, int WM, int WN, bool GROUPED, bool W4 = false>
+template <int FMT, int WAVES_M, int WAVES_N, int WM, int WN, bool GROUPED, bool W4 = false,
+          bool SWIGLU = false>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
     const uint8_t* __restrict__ xq, const void* __restrict__ xs, const uint8_t* __restrict__ wq,
     const void* __restrict__ wsc, const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
     int64_t M, int64_t N, int64_t K, const int32_t* __restrict__ seg, int E, int gsel,
-    float* __restrict__ part, int kbps) {
+    float* __restrict__ part, int kbps, uint8_t* __restrict__ hq, void* __restrict__ hs) {
   // The body exists only in the device pass; the host pass needs nothing
   // but the launch stub of each instantiation.
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -265,6 +373,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
   constexpr int MI = WM / 16, NI = WN / 16;
   static_assert(WN == 64 || WN == 128, "a wave's N range lies inside one weight block");
   static_assert(!(W4 && GROUPED), "MXFP4 weights: dense launches");
+  static_assert(!SWIGLU || (GROUPED && !W4 && WAVES_N % 2 == 0 && WAVES_N / 2 * WN == 128),
+                "SiLU-mul tiles: 128 gate rows then the 128 matching up rows");
   constexpr int kWRow = W4 ? 64 : kRowBytes;   // W bytes per row per K block
   constexpr int XJ = BM * 8 / THREADS;      // DMA loads per lane per stage (X)
   constexpr int WJ = BN * (kWRow / 16) / THREADS;   // (W)
@@ -275,6 +385,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
   constexpr int LOADS = XJ + WJ + MI + 1;   // vector-memory ops per stage per lane
   __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES * STAGE];
   static_assert(!GROUPED || STAGES * STAGE >= 1025 * 4, "tile table fits the stage buffers");
+  static_assert(!SWIGLU || WAVES_M * (WAVES_N / 2) * MI * NI * 1024 +
+                               (WAVES_N > 2 ? WAVES_M * (WAVES_N / 2) * MI * 64 : 0) <=
+                           STAGES * STAGE,
+                "the up tiles and row maxima fit the stage buffers");
 
   Tile tl;
   // the grouped tile table lives in the stage buffers until the tile is known
@@ -300,7 +414,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
   const int64_t nrows = min((int64_t)BN, N - tl.n0);
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(xq + tl.m0 * K, mrows * K);
   const int64_t KW = W4 ? K / 2 : K;         // W bytes per row
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(wbase + tl.n0 * KW, nrows * KW);
+  // SWIGLU: N = 2 I weight rows, gate rows [0, I) then up rows [I, 2 I); an
+  // N tile at n0 = 256 t covers h columns [128 t, 128 t + 128): its rows
+  // [0, 128) are gate rows 128 t + r, rows [128, 256) the up rows I + 128 t + r
+  const int64_t I = N / 2, c0 = tl.n0 / 2;
+  auto wrow_of = [&](int r) -> int64_t { return r < 128 ? c0 + r : I + c0 + (r - 128); };
+  const __amdgpu_buffer_rsrc_t rw = SWIGLU ? make_rsrc(wbase, N * K)
+                                           : make_rsrc(wbase + tl.n0 * KW, nrows * KW);
   const __amdgpu_buffer_rsrc_t rsa = make_rsrc((const uint8_t*)xs + tl.m0 * KB * SB,
                                                mrows * KB * SB);
   const __amdgpu_buffer_rsrc_t rsw = make_rsrc(wsb, NB * KB * SB);
@@ -311,6 +431,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
     const int row = q >> 3, c = (q & 7) ^ ((row >> 1) & 7);
     const uint32_t kc = kbyte + c * 16;
     return (row < rows && kc < (uint32_t)K) ? (uint32_t)(row * K) + kc : kOOB;
+  };
+  // the same for W rows of a gate/up tile (rows from both halves of W)
+  auto dma_src_gu = [&](int q, uint32_t kbyte) -> uint32_t {
+    const int row = q >> 3, c = (q & 7) ^ ((row >> 1) & 7);
+    const uint32_t kc = kbyte + c * 16;
+    return kc < (uint32_t)K ? (uint32_t)(wrow_of(row) * K) + kc : kOOB;
   };
   // the same for a 64-byte MXFP4 W row: four chunks, swizzle (row >> 2) & 3
   auto dma_src4 = [&](int q, int64_t rows, int kb) -> uint32_t {
@@ -330,7 +456,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
     saoff[i] = r < mrows ? (uint32_t)(r * KB * SB) : kOOB;
   }
   const int64_t nwave = tl.n0 + wn * WN;
-  const uint32_t swoff = nwave < N ? (uint32_t)((nwave >> 7) * KB * SB) : kOOB;
+  const int64_t nwave_w = SWIGLU ? wrow_of(wn * WN) : nwave;   // its first weight row
+  const uint32_t swoff = nwave < N ? (uint32_t)((nwave_w >> 7) * KB * SB) : kOOB;
 
   float sa_reg[STAGES][MI];
   float sw_reg[STAGES];
@@ -353,7 +480,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
       const int q = (j * WAVES + wave) * 64 + lane;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rw, BSFP8_LDS(sw + (j * WAVES + wave) * 1024), 16,
-          W4 ? dma_src4(q, nrows, kb) : dma_src(q, nrows, kbyte), 0, 0, 0);
+          W4 ? dma_src4(q, nrows, kb) : SWIGLU ? dma_src_gu(q, kbyte) : dma_src(q, nrows, kbyte),
+          0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
@@ -478,6 +606,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
   }
   // drain: no DMA may land in LDS after this workgroup has finished
   wait_vmcnt<0>();
+
+  if constexpr (SWIGLU) {
+    swiglu_epilogue<FMT, WAVES_M, WAVES_N, WM, WN>(acc, lds, tl, wm, wn, lane, I, c0, y, hq, hs);
+    return;
+  }
 
   // epilogue: lane holds n = nwave + 16 i + 4 g4 + {0..3} for token m_j
 #pragma unroll
@@ -668,18 +801,21 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
 // Explicit instantiations of every tile configuration the dispatcher below
 // can launch (the host pass does not always emit launch stubs for kernel
 // templates that are only instantiated implicitly).
-#define BSFP8_INST(FMT, WMN, WNN, WM, WN, G, W4)                                              \
-  template __global__ void gemm_lds_kernel<FMT, WMN, WNN, WM, WN, G, W4>(                    \
+#define BSFP8_INST(FMT, WMN, WNN, WM, WN, G, W4, SW)                                          \
+  template __global__ void gemm_lds_kernel<FMT, WMN, WNN, WM, WN, G, W4, SW>(                \
       const uint8_t* __restrict__, const void* __restrict__, const uint8_t* __restrict__,     \
       const void* __restrict__, const uint16_t* __restrict__, uint16_t* __restrict__, int64_t, \
-      int64_t, int64_t, const int32_t* __restrict__, int, int, float* __restrict__, int);
-#define BSFP8_INST_ALL(FMT)                   \
-  BSFP8_INST(FMT, 4, 2, 64, 128, false, false) \
-  BSFP8_INST(FMT, 2, 4, 64, 64, false, false)  \
-  BSFP8_INST(FMT, 2, 4, 64, 64, false, true)   \
-  BSFP8_INST(FMT, 4, 2, 64, 128, false, true)  \
-  BSFP8_INST(FMT, 1, 4, 64, 64, true, false)   \
-  BSFP8_INST(FMT, 4, 2, 64, 128, true, false)
+      int64_t, int64_t, const int32_t* __restrict__, int, int, float* __restrict__, int,      \
+      uint8_t* __restrict__, void* __restrict__);
+#define BSFP8_INST_ALL(FMT)                          \
+  BSFP8_INST(FMT, 4, 2, 64, 128, false, false, false) \
+  BSFP8_INST(FMT, 2, 4, 64, 64, false, false, false)  \
+  BSFP8_INST(FMT, 2, 4, 64, 64, false, true, false)   \
+  BSFP8_INST(FMT, 4, 2, 64, 128, false, true, false)  \
+  BSFP8_INST(FMT, 1, 4, 64, 64, true, false, false)   \
+  BSFP8_INST(FMT, 4, 2, 64, 128, true, false, false)  \
+  BSFP8_INST(FMT, 1, 4, 64, 64, true, false, true)    \
+  BSFP8_INST(FMT, 4, 2, 64, 128, true, false, true)
 BSFP8_INST_ALL(0)
 BSFP8_INST_ALL(1)
 #undef BSFP8_INST_ALL
@@ -702,7 +838,8 @@ constexpr int64_t kDecodeFusedMaxN = 8192;
 //          1.5x faster per CU once every CU has a tile of its own.
 // Two stages wait for vmcnt(0) before each K block, which does not depend
 // on the completion order of the LDS-DMA loads and the scale loads.
-template <int FMT, int WMN, int WNN, int WM, int WN, bool GROUPED, bool W4 = false>
+template <int FMT, int WMN, int WNN, int WM, int WN, bool GROUPED, bool W4 = false,
+          bool SW = false>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t st, int splits, int kbps, int gsel = 0) {
   constexpr int BM = WMN * WM, BN = WNN * WN;
   const int64_t NT = (a.N + BN - 1) / BN;
@@ -719,10 +856,10 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t st, int splits, int kbps, i
     tiles = (tiles + 7) / 8 * 8;                 // whole rounds over the 8 XCDs
   }
   float* part = splits > 1 ? (float*)a.workspace : nullptr;
-  hipLaunchKernelGGL((gemm_lds_kernel<FMT, WMN, WNN, WM, WN, GROUPED, W4>), dim3((unsigned)tiles),
-                     dim3(64 * WMN * WNN), 0, st, a.xq, a.xs, a.wq, a.ws,
+  hipLaunchKernelGGL((gemm_lds_kernel<FMT, WMN, WNN, WM, WN, GROUPED, W4, SW>),
+                     dim3((unsigned)tiles), dim3(64 * WMN * WNN), 0, st, a.xq, a.xs, a.wq, a.ws,
                      GROUPED ? nullptr : a.bias, a.y, a.M, a.N, a.K, a.seg, a.E, gsel, part,
-                     kbps);
+                     kbps, a.hq, a.hs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || part == nullptr) return e;
   const int64_t MN = a.M * a.N;
@@ -770,9 +907,16 @@ Plan plan_dense(int64_t M, int64_t N, int64_t K, bool allow_big = true) {
   return best;
 }
 
-template <int FMT, bool GROUPED>
+template <int FMT, bool GROUPED, bool SW = false>
 hipError_t launch_lds(const GemmArgs& a, hipStream_t st) {
-  if constexpr (GROUPED) {
+  if constexpr (SW) {
+    // gate/up tiles with the SiLU-mul requant epilogue: the same two expert
+    // classes and tile shapes as the plain grouped GEMM
+    const int kb = (int)((a.K + 127) / 128);
+    hipError_t e = launch_cfg<FMT, 4, 2, 64, 128, true, false, true>(a, st, 1, kb, 1);
+    if (e != hipSuccess) return e;
+    return launch_cfg<FMT, 1, 4, 64, 64, true, false, true>(a, st, 1, kb, 2);
+  } else if constexpr (GROUPED) {
     // experts with many rows on 256 x 256 tiles, the short segments (most
     // of them under skewed routing) on 64 x 256 tiles of four waves (two
     // workgroups per CU), which pad a 42-row median segment to 64 rather
@@ -854,6 +998,10 @@ hipError_t launch_block_gemm(const GemmArgs& a, hipStream_t st) {
 
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t st) {
   return a.fmt == 0 ? launch_lds<0, true>(a, st) : launch_lds<1, true>(a, st);
+}
+
+hipError_t launch_grouped_silu_mul_quant(const GemmArgs& a, hipStream_t st) {
+  return a.fmt == 0 ? launch_lds<0, true, true>(a, st) : launch_lds<1, true, true>(a, st);
 }
 
 }  // namespace bsfp8

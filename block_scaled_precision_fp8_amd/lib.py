@@ -24,7 +24,8 @@ GEMM_NONE, GEMM_TILE_128x256, GEMM_TILE_256x256, GEMM_DECODE = 0, 2, 3, 4
 EXPORTS = ("bsfp8_version", "bsfp8_status_string", "bsfp8_workspace_size", "bsfp8_gemm_kernel",
            "fp8_quant_act", "fp8_quant_weight", "fp8_block_gemm", "fp8_linear",
            "fp8_grouped_gemm", "fp4_quant", "fp4_group_gemm", "fp8_dequant_weight",
-           "fp8_scale_to_ue8m0", "mxfp4_quant_weight", "fp8_fp4_gemm")
+           "fp8_scale_to_ue8m0", "mxfp4_quant_weight", "fp8_fp4_gemm",
+           "fp8_grouped_gemm_silu_mul_quant")
 
 
 class BsFp8Error(RuntimeError):
@@ -49,6 +50,8 @@ _SIGS = {
     "fp8_scale_to_ue8m0": (_I32, [_P, _I64, _P, _P]),
     "mxfp4_quant_weight": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "fp8_fp4_gemm": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _SZ, _P]),
+    "fp8_grouped_gemm_silu_mul_quant": (_I32, [_P, _P, _P, _P, _P, _I32, _P, _P, _P, _I64, _I64,
+                                               _I64, _I32, _P]),
     "fp8_quant_act": (_I32, [_P, _I64, _I64, _I64, _I32, _I32, _I32, _P, _P, _P]),
     "fp8_quant_weight": (_I32, [_P, _I64, _I64, _I64, _I32, _I32, _I32, _P, _P, _P]),
     "fp8_block_gemm": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32,
@@ -163,6 +166,17 @@ def fp8_fp4_gemm(xq, x_scale, wq4, w_scale, y, bias=None, scale_fmt=SCALE_FLOAT,
     _check("fp8_fp4_gemm", load().fp8_fp4_gemm(_ptr(xq), _ptr(x_scale), _ptr(wq4), _ptr(w_scale),
                                                _ptr(bias), _ptr(y), M, N, K, scale_fmt, _ptr(ws), wsb,
                                                _stream(stream)))
+
+
+def fp8_grouped_gemm_silu_mul_quant(xq, x_scale, wq, w_scale_inv, seg_offsets, hq, h_scale,
+                                    h_bf16=None, scale_fmt=SCALE_FLOAT, stream=None):
+    """xq (T, K); wq (E, 2I, K) gate rows then up rows; hq (T, I) uint8;
+    h_scale (T, I/128); h_bf16 optional bf16 (T, I)."""
+    T, K = xq.shape
+    E, N2 = wq.shape[0], wq.shape[1]
+    _check("fp8_grouped_gemm_silu_mul_quant", load().fp8_grouped_gemm_silu_mul_quant(
+        _ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale_inv), _ptr(seg_offsets), E, _ptr(hq),
+        _ptr(h_scale), _ptr(h_bf16), T, N2 // 2, K, scale_fmt, _stream(stream)))
 
 
 def fp8_quant_weight(w, wq, w_scale_inv, block_n=128, block_k=128, scale_fmt=SCALE_FLOAT,

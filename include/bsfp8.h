@@ -208,6 +208,37 @@ BSFP8_API int32_t fp8_grouped_gemm(const void* xq, const void* x_scale, const vo
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * fp8_grouped_gemm_silu_mul_quant -- an MoE expert MLP's gate/up GEMM with
+ * the step to the down GEMM fused into its epilogue: the gate/up/down MLP
+ * of [NVFP4] (layer-wise quantization section) run as FP8 experts
+ * ([FG-FP8] §一 FP8Experts, §6.4), the down projection's input quantized
+ * per token in 1 x 128 groups like any activation ([FG-FP8] §一).
+ * For every expert e and row t in [off[e], off[e+1]):
+ *   g = (X W_e[0:I]^T)[t],  u = (X W_e[I:2I]^T)[t]   (fp32 accumulation),
+ *   h = bf16(silu(g) * u),  silu(g) = g / (1 + e^-g),
+ *   (hq, h_scale) = the 1 x 128 activation quantization of h (the codes
+ *   and scales fp8_quant_act writes for that bf16 row), in scale_fmt.
+ * The result feeds fp8_grouped_gemm (the down projection) unchanged.
+ *
+ *   xq, x_scale  as fp8_grouped_gemm (K input channels, 1 x 128 groups).
+ *   wq           E4M3 [E][2I][K]: rows [0, I) gate, rows [I, 2I) up;
+ *                w_scale_inv [E][2I/128][ceil(K/128)] (fp32 | UE8M0).
+ *   seg_offsets  DEVICE int32 [E+1], the same precondition as
+ *                fp8_grouped_gemm.
+ *   hq           out, E4M3 [T][I];  h_scale out, [T][I/128] fp32 | UE8M0.
+ *   h_bf16       out, bf16 [T][I] (the rounded h), or NULL.
+ *   I            intermediate size, a positive multiple of 128.
+ * No workspace.  Errors: those of fp8_grouped_gemm with N = 2I; EINVAL for
+ * I <= 0 or I % 128 != 0, a null or misaligned h_scale (4 bytes) or a
+ * misaligned h_bf16 (16 bytes).
+ */
+BSFP8_API int32_t fp8_grouped_gemm_silu_mul_quant(const void* xq, const void* x_scale,
+                                        const void* wq, const void* w_scale_inv,
+                                        const int32_t* seg_offsets, int32_t E, void* hq,
+                                        void* h_scale, void* h_bf16, int64_t T, int64_t I,
+                                        int64_t K, int32_t scale_fmt, void* stream);
+
+/*
  * fp4_quant -- NVFP4-style quantization ([NVFP4]: 4-bit float weights and
  * input activations in 16-element groups, group_size 16): E2M1 codes with
  * an E4M3 scale per 16-element group and one fp32 scale per tensor.
