@@ -11,8 +11,8 @@ from oracle import gemm as G
 from oracle import fp4 as P
 
 
-def _brute_block_gemm(xq, xs, wq, ws, bias, fmt):
-    """Y[m,n] = sum_kb S_a[m,kb] S_w[n//128,kb] sum_{k in kb} dec(xq) dec(wq),
+def _brute_block_gemm(xq, xs, wq, ws, bias, fmt, blk=128):
+    """Y[m,n] = sum_kb S_a[m,kb] S_w[n//blk,kb] sum_{k in kb} dec(xq) dec(wq),
     plain Python loops over every index (the block-by-block form)."""
     M, K = xq.shape
     N = wq.shape[0]
@@ -24,11 +24,11 @@ def _brute_block_gemm(xq, xs, wq, ws, bias, fmt):
     for m in range(M):
         for n in range(N):
             tot = 0.0
-            for kb in range(-(-K // 128)):
+            for kb in range(-(-K // blk)):
                 part = 0.0
-                for k in range(kb * 128, min(K, kb * 128 + 128)):
+                for k in range(kb * blk, min(K, kb * blk + blk)):
                     part += float(dx[m, k]) * float(dw[n, k])
-                tot += float(sa[m, kb]) * float(sw[n // 128, kb]) * part
+                tot += float(sa[m, kb]) * float(sw[n // blk, kb]) * part
             Y[m, n] = tot + (0.0 if bias is None else float(bias[n]))
     return Y
 
@@ -44,6 +44,20 @@ def test_block_gemm_bruteforce(fmt, shape):
     bias = F.bf16_decode(synth.normal_bf16((N,), 0.5, "llama", "bias", seed=1))
     Y = G.block_gemm(xq, xs, wq, ws, bias, fmt=fmt)
     R = _brute_block_gemm(xq, xs, wq, ws, bias, fmt)
+    assert np.allclose(Y, R, rtol=1e-12, atol=1e-12 * np.abs(R).max())
+
+
+@pytest.mark.parametrize("fmt", [Q.SCALE_FLOAT, Q.SCALE_UE8M0])
+def test_block_gemm_bruteforce_block32(fmt):
+    """(32, 32) weight blocks with 1 x 32 act groups, partial on every axis."""
+    M, N, K = 3, 40, 80
+    x = synth.deepseek_acts(M, K, seed=2)
+    w = synth.normal_bf16((N, K), 0.02, "llama", "w", seed=2)
+    xq, xs = Q.quant_act(x, 32, fmt)
+    wq, ws = Q.quant_weight(w, 32, 32, fmt)
+    assert xs.shape == (M, 3) and ws.shape == (2, 3)
+    Y = G.block_gemm(xq, xs, wq, ws, None, 32, 32, fmt=fmt)
+    R = _brute_block_gemm(xq, xs, wq, ws, None, fmt, blk=32)
     assert np.allclose(Y, R, rtol=1e-12, atol=1e-12 * np.abs(R).max())
 
 

@@ -54,18 +54,18 @@ def _brute_group(vals, fmt):
 
 
 @pytest.mark.parametrize("fmt", [Q.SCALE_FLOAT, Q.SCALE_UE8M0])
-@pytest.mark.parametrize("K", [128, 200, 48])
-def test_quant_act_bruteforce(fmt, K):
+@pytest.mark.parametrize("K,gk", [(128, 128), (200, 128), (48, 128), (200, 32), (48, 32)])
+def test_quant_act_bruteforce(fmt, K, gk):
     x = synth.deepseek_acts(3, K, seed=4)
-    xq, s = Q.quant_act(x, 128, fmt)
+    xq, s = Q.quant_act(x, gk, fmt)
     xv = F.bf16_decode(x)
-    G = -(-K // 128)
+    G = -(-K // gk)
     assert xq.shape == (3, K) and s.shape == (3, G)
     for m in range(3):
         for g in range(G):
-            vals = xv[m, g * 128:(g + 1) * 128]
+            vals = xv[m, g * gk:(g + 1) * gk]
             codes, sc = _brute_group(vals, fmt)
-            assert list(xq[m, g * 128:(g + 1) * 128]) == codes
+            assert list(xq[m, g * gk:(g + 1) * gk]) == codes
             assert s[m, g] == sc
 
 
@@ -81,6 +81,22 @@ def test_quant_weight_bruteforce_partial_blocks(fmt):
             blk = wv[nb * 128:(nb + 1) * 128, kb * 128:(kb + 1) * 128]
             codes, sc = _brute_group(blk.reshape(-1), fmt)
             got = wq[nb * 128:(nb + 1) * 128, kb * 128:(kb + 1) * 128].reshape(-1)
+            assert list(got) == codes, (nb, kb)
+            assert s[nb, kb] == sc
+
+
+@pytest.mark.parametrize("fmt", [Q.SCALE_FLOAT, Q.SCALE_UE8M0])
+def test_quant_weight_bruteforce_block32(fmt):
+    N, K = 70, 80            # (32, 32) blocks, partial on both axes
+    w = synth.normal_bf16((N, K), 0.02, "llama", "w", seed=8)
+    wq, s = Q.quant_weight(w, 32, 32, fmt)
+    assert wq.shape == (N, K) and s.shape == (3, 3)
+    wv = F.bf16_decode(w)
+    for nb in range(3):
+        for kb in range(3):
+            blk = wv[nb * 32:(nb + 1) * 32, kb * 32:(kb + 1) * 32]
+            codes, sc = _brute_group(blk.reshape(-1), fmt)
+            got = wq[nb * 32:(nb + 1) * 32, kb * 32:(kb + 1) * 32].reshape(-1)
             assert list(got) == codes, (nb, kb)
             assert s[nb, kb] == sc
 
