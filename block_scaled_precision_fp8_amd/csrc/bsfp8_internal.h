@@ -107,14 +107,15 @@ __device__ __forceinline__ uint32_t act_encode4_rcp(float a, float b, float c, f
 // one calibrated per-tensor scale (fp32, or the E8M0 byte).
 hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                             int fmt, uint8_t* xq, void* scale, hipStream_t s,
-                            const void* static_scale = nullptr);
+                            const void* static_scale = nullptr, int group_k = 128);
 hipError_t launch_dequant_weight(const uint8_t* wq, int64_t N, int64_t K, int fmt,
-                                 const void* scale, uint16_t* w, hipStream_t s);
+                                 const void* scale, uint16_t* w, hipStream_t s, int blk = 128);
 hipError_t launch_pow2_to_ue8m0(const float* in, int64_t n, uint8_t* out, hipStream_t s);
 hipError_t launch_mxfp4_quant_weight(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
                                      uint8_t* wq4, uint8_t* scale, hipStream_t s);
 hipError_t launch_quant_weight(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
-                               int fmt, uint8_t* wq, void* scale, hipStream_t s);
+                               int fmt, uint8_t* wq, void* scale, hipStream_t s,
+                               int block = 128);
 
 struct GemmArgs {
   const uint8_t* xq;
@@ -138,12 +139,14 @@ struct GemmArgs {
   // (M, N/2) and scales (M, N/256); y is then the optional bf16 h
   uint8_t* hq;
   void* hs;
+  // weight block edge = activation group width: 128, or 32 for (32, 32)
+  int blk = 128;
 };
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 size_t fp8_fp4_workspace_bytes(int64_t M, int64_t N, int64_t K);
 int gemm_kind(int64_t M, int64_t N, int64_t K, int* splits);   // a bsfp8_gemm_kind
-size_t linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
+size_t linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int blk = 128);
 bool linear_fused(int64_t M, int64_t N);   // fp8_linear quantizes inside the GEMM
 size_t grouped_workspace_bytes(int64_t T, int64_t N, int64_t K, int E);
 hipError_t launch_block_gemm(const GemmArgs& a, hipStream_t s);

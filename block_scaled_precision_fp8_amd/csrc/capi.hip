@@ -23,9 +23,10 @@ bool valid_fmt(int32_t f) { return f == BSFP8_SCALE_FLOAT || f == BSFP8_SCALE_UE
 
 // block sizes: the pages allow any positive pair ([FG-FP8] §四); only 128
 // is provided here.
+// Supported weight blocks: 128 x 128, and 32 x 32 (with 1 x 32 act groups).
 int32_t check_blocks(int32_t bn, int32_t bk) {
   if (bn <= 0 || bk <= 0) return BSFP8_EINVAL;
-  if (bn != 128 || bk != 128) return BSFP8_ENOTSUP;
+  if (!((bn == 128 && bk == 128) || (bn == 32 && bk == 32))) return BSFP8_ENOTSUP;
   return BSFP8_OK;
 }
 
@@ -102,6 +103,7 @@ size_t bsfp8_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int32_t
     case BSFP8_OP_FP4_QUANT: return fp4_quant_workspace_bytes(M, K);
     case BSFP8_OP_FP4_GEMM: return fp4_gemm_workspace_bytes(M, N, K);
     case BSFP8_OP_FP8_FP4_GEMM: return fp8_fp4_workspace_bytes(M, N, K);
+    case BSFP8_OP_LINEAR_B32: return linear_workspace_bytes(M, N, K, 32);
     default: return (size_t)-1;
   }
 }
@@ -122,19 +124,21 @@ int32_t fp8_quant_act(const void* x, int64_t M, int64_t K, int64_t ldx, int32_t 
   if (act_scheme != BSFP8_ACT_DYNAMIC && act_scheme != BSFP8_ACT_STATIC) return BSFP8_EINVAL;
   if (!valid_fmt(scale_fmt)) return BSFP8_EINVAL;
   if (group_k <= 0) return BSFP8_EINVAL;
-  if (group_k != 128) return BSFP8_ENOTSUP;
+  if (group_k != 128 && group_k != 32) return BSFP8_ENOTSUP;
+  if (act_scheme == BSFP8_ACT_STATIC && group_k != 128) return BSFP8_ENOTSUP;
   if (M == 0) return BSFP8_OK;
   if (K == 0) return BSFP8_EINVAL;
   if (!x || !xq || !x_scale) return BSFP8_EINVAL;
   if (!al16(x) || !al16(xq) || !al16(x_scale)) return BSFP8_EINVAL;
-  if (!fits_i32(M * ((K + 127) / 128))) return BSFP8_EINVAL;
+  if (!fits_i32(M * ((K + group_k - 1) / group_k))) return BSFP8_EINVAL;
   int32_t r = check_device(stream);
   if (r != BSFP8_OK) return r;
   // STATIC: the calibrated scale sits in x_scale[0] on entry; every group's
   // entry (x_scale[0] included) is set to that same value
   return hip_status(launch_quant_act((const uint16_t*)x, M, K, ldx, scale_fmt, (uint8_t*)xq,
                                      x_scale, (hipStream_t)stream,
-                                     act_scheme == BSFP8_ACT_STATIC ? x_scale : nullptr));
+                                     act_scheme == BSFP8_ACT_STATIC ? x_scale : nullptr,
+                                     group_k));
 }
 
 int32_t fp8_dequant_weight(const void* wq, int64_t N, int64_t K, int32_t block_n,
@@ -151,7 +155,7 @@ int32_t fp8_dequant_weight(const void* wq, int64_t N, int64_t K, int32_t block_n
   r = check_device(stream);
   if (r != BSFP8_OK) return r;
   return hip_status(launch_dequant_weight((const uint8_t*)wq, N, K, scale_fmt, w_scale_inv,
-                                          (uint16_t*)w, (hipStream_t)stream));
+                                          (uint16_t*)w, (hipStream_t)stream, block_n));
 }
 
 int32_t fp8_scale_to_ue8m0(const float* scale, int64_t n, void* out, void* stream) {
@@ -213,7 +217,7 @@ int32_t fp8_quant_weight(const void* w, int64_t N, int64_t K, int64_t ldw, int32
   r = check_device(stream);
   if (r != BSFP8_OK) return r;
   return hip_status(launch_quant_weight((const uint16_t*)w, N, K, ldw, scale_fmt, (uint8_t*)wq,
-                                        w_scale_inv, (hipStream_t)stream));
+                                        w_scale_inv, (hipStream_t)stream, block_n));
 }
 
 int32_t fp8_block_gemm(const void* xq, const void* x_scale, const void* wq,
@@ -223,15 +227,18 @@ int32_t fp8_block_gemm(const void* xq, const void* x_scale, const void* wq,
   int32_t r = check_gemm(xq, x_scale, wq, w_scale_inv, bias, y, M, N, K, block_n, block_k,
                          scale_fmt);
   if (r != BSFP8_OK || M == 0) return r;
-  const size_t need = gemm_workspace_bytes(M, N, K);
+  // (32, 32) blocks run without workspace
+  const size_t need = block_n == 32 ? 0 : gemm_workspace_bytes(M, N, K);
   if (workspace_bytes < need) return BSFP8_ENOSPC;
   if (need && (!workspace || !al16(workspace))) return BSFP8_EINVAL;
+  if (block_n == 32 && !fits_i32((M + 127) / 128 * ((N + 127) / 128) + 8)) return BSFP8_EINVAL;
   r = check_device(stream);
   if (r != BSFP8_OK) return r;
   GemmArgs a{};
   a.xq = (const uint8_t*)xq; a.xs = x_scale; a.wq = (const uint8_t*)wq; a.ws = w_scale_inv;
   a.bias = (const uint16_t*)bias; a.y = (uint16_t*)y; a.M = M; a.N = N; a.K = K;
   a.fmt = scale_fmt; a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+  a.blk = block_n;
   return hip_status(launch_block_gemm(a, (hipStream_t)stream));
 }
 
@@ -248,8 +255,9 @@ int32_t fp8_linear(const void* x, int64_t ldx, const void* wq, const void* w_sca
   if (act_scheme == BSFP8_ACT_STATIC) return BSFP8_ENOTSUP;
   if (M == 0) return BSFP8_OK;
   if (ldx < K || ldx % 8 != 0) return BSFP8_EINVAL;
-  if (!fits_i32(M * ((K + 127) / 128))) return BSFP8_EINVAL;
-  const size_t need = linear_workspace_bytes(M, N, K);
+  const int blk = block_k;                  // 128, or 32 for (32, 32) blocks
+  if (!fits_i32(M * ((K + blk - 1) / blk))) return BSFP8_EINVAL;
+  const size_t need = linear_workspace_bytes(M, N, K, blk);
   if (workspace_bytes < need) return BSFP8_ENOSPC;
   if (need && (!workspace || !al16(workspace))) return BSFP8_EINVAL;
   r = check_device(stream);
@@ -259,20 +267,22 @@ int32_t fp8_linear(const void* x, int64_t ldx, const void* wq, const void* w_sca
   a.wq = (const uint8_t*)wq; a.ws = w_scale_inv;
   a.bias = (const uint16_t*)bias; a.y = (uint16_t*)y; a.M = M; a.N = N; a.K = K;
   a.fmt = scale_fmt;
-  if (linear_fused(M, N)) {
+  a.blk = blk;
+  if (blk == 128 && linear_fused(M, N)) {
     // one launch: the decode kernel quantizes the activations itself
     if (!al16(x)) return BSFP8_EINVAL;
     a.x_bf16 = (const uint16_t*)x; a.ldx = ldx;
     return hip_status(launch_block_gemm(a, st));
   }
   // workspace: [xq M*K][x_scale M*G*4][gemm workspace], 256-byte aligned parts
-  const int64_t G = (K + 127) / 128;
+  const int64_t G = (K + blk - 1) / blk;
   auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
   uint8_t* ws = (uint8_t*)workspace;
   uint8_t* xq = ws;
   void* xs = ws + up((size_t)M * K);
   void* gw = ws + up((size_t)M * K) + up((size_t)M * G * 4);
-  hipError_t e = launch_quant_act((const uint16_t*)x, M, K, ldx, scale_fmt, xq, xs, st);
+  hipError_t e = launch_quant_act((const uint16_t*)x, M, K, ldx, scale_fmt, xq, xs, st, nullptr,
+                                  blk);
   if (e != hipSuccess) return BSFP8_EHIP;
   a.xq = xq; a.xs = xs; a.workspace = gw;
   a.workspace_bytes = workspace_bytes - (size_t)((uint8_t*)gw - ws);
@@ -288,6 +298,7 @@ int32_t fp8_grouped_gemm(const void* xq, const void* x_scale, const void* wq,
   int32_t r = check_gemm(xq, x_scale, wq, w_scale_inv, nullptr, y, T, N, K, block_n, block_k,
                          scale_fmt);
   if (r != BSFP8_OK) return r;
+  if (block_n != 128) return BSFP8_ENOTSUP;       // experts: 128 x 128 blocks
   if (T == 0) return BSFP8_OK;
   if (!seg_offsets || ((uintptr_t)seg_offsets & 3u)) return BSFP8_EINVAL;
   const size_t need = grouped_workspace_bytes(T, N, K, E);

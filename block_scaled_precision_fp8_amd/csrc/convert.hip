@@ -1,5 +1,5 @@
 // Conversions around the FP8 path (fine-grained FP8 guide, sections 五 and 七):
-//  * dequant_weight_kernel: fold the 128x128 block scales into the weights
+//  * dequant_weight_kernel: fold the block scales (128 x 128 or 32 x 32) into the weights
 //    (the dequantize-on-load step): bf16_rne(fl32(E4M3(code) * scale));
 //  * pow2_to_ue8m0_kernel: power-of-two scales kept in float32 containers
 //    -> the one-byte E8M0 form, exactly; any other value -> 0xFF (E8M0 NaN).
@@ -11,15 +11,16 @@ namespace detail {
 
 // Eight codes per thread: one 8-byte load, one 16-byte store of bf16.
 // E4M3 decode is the hardware conversion (exact for every finite code).
+// lg = log2 of the block edge (7 for 128 x 128 blocks, 5 for 32 x 32).
 template <int FMT>
 __global__ __launch_bounds__(256) void dequant_weight_kernel(
-    const uint8_t* __restrict__ wq, int64_t N, int64_t K, int64_t KB,
+    const uint8_t* __restrict__ wq, int64_t N, int64_t K, int64_t KB, int lg,
     const void* __restrict__ scale, uint16_t* __restrict__ w) {
   const int64_t per_row = K / 8;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= N * per_row) return;
   const int64_t n = i / per_row, k = (i - n * per_row) * 8;
-  const int64_t sidx = (n >> 7) * KB + (k >> 7);
+  const int64_t sidx = (n >> lg) * KB + (k >> lg);
   float s;
   if (FMT == 0) {
     s = ((const float*)scale)[sidx];
@@ -67,14 +68,17 @@ __global__ __launch_bounds__(256) void pow2_to_ue8m0_kernel(const float* __restr
 using namespace detail;
 
 hipError_t launch_dequant_weight(const uint8_t* wq, int64_t N, int64_t K, int fmt,
-                                 const void* scale, uint16_t* w, hipStream_t s) {
-  const int64_t KB = (K + 127) / 128;
+                                 const void* scale, uint16_t* w, hipStream_t s, int blk) {
+  const int lg = blk == 32 ? 5 : 7;
+  const int64_t KB = (K + blk - 1) / blk;
   const int64_t total = N * (K / 8);
   const dim3 grid((unsigned)((total + 255) / 256));
   if (fmt == 0)
-    hipLaunchKernelGGL(dequant_weight_kernel<0>, grid, dim3(256), 0, s, wq, N, K, KB, scale, w);
+    hipLaunchKernelGGL(dequant_weight_kernel<0>, grid, dim3(256), 0, s, wq, N, K, KB, lg, scale,
+                       w);
   else
-    hipLaunchKernelGGL(dequant_weight_kernel<1>, grid, dim3(256), 0, s, wq, N, K, KB, scale, w);
+    hipLaunchKernelGGL(dequant_weight_kernel<1>, grid, dim3(256), 0, s, wq, N, K, KB, lg, scale,
+                       w);
   return hipGetLastError();
 }
 

@@ -798,6 +798,182 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
   if (mvalid && n < N) store_out4(y, N, l16, n, sum, bias);
 }
 
+// ------------------------------------------------------------------------
+// (32, 32) weight blocks with 1 x 32 activation groups (the fine-grained FP8
+// guide, section 九, names weight_block_size=(32, 32) among the non-default
+// blocks its tests cover).  A 128-wide K block then holds four
+// scale groups and, with fp32 scales, each group's partial product needs a
+// promotion of its own, so a K block runs as four 16x16x32 FP8 MFMAs per
+// output tile: acc += (s_a[m, g] s_w[n / 32, g]) P_g.  (The 16x16x128
+// scaled form applies one power of two per lane's 32 values and cannot
+// carry fp32 scales.)  UE8M0 scales take the same path as the powers of two
+// they encode.  Tile 128 (m) x 128 (n), four waves of 64 x 64, two LDS
+// stages laid out as in the large-M kernel: the 8-byte fragment a lane
+// takes for group g is half (u & 1) of logical chunk u >> 1, u = 4 g + g4,
+// and the chunk swizzle keeps those reads free of bank conflicts.
+// ------------------------------------------------------------------------
+__device__ __forceinline__ float e8m0_f32(uint32_t b) {
+  return __uint_as_float(b == 0 ? 0x00400000u : b << 23);   // 2^(b - 127)
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256, 2) void gemm_b32_kernel(
+    const uint8_t* __restrict__ xq, const void* __restrict__ xs, const uint8_t* __restrict__ wq,
+    const void* __restrict__ wsc, const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
+    int64_t M, int64_t N, int64_t K) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int BM = 128, BN = 128, WAVES = 4;
+  constexpr int MI = 4, NI = 4;                      // 64 x 64 per wave
+  constexpr int XBYTES = BM * kRowBytes;
+  constexpr int STAGE = (BM + BN) * kRowBytes;
+  constexpr int SB = FMT == 0 ? 4 : 1;
+  constexpr int J = BM * 8 / (64 * WAVES);           // DMA loads per lane per operand
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE];
+  const Tile tl = dense_tile<BM, BN>(M, N, 1);
+  if (!tl.valid) return;
+  const int KB = (int)((K + 127) / 128);
+  const int GS = (int)((K + 31) / 32);               // scale groups per row
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int64_t mrows = min((int64_t)BM, M - tl.m0);
+  const int64_t nrows = min((int64_t)BN, N - tl.n0);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(xq + tl.m0 * K, mrows * K);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(wq + tl.n0 * K, nrows * K);
+  const __amdgpu_buffer_rsrc_t rsa =
+      make_rsrc((const uint8_t*)xs + tl.m0 * GS * SB, mrows * GS * SB);
+  const int64_t NBS = (N + 31) / 32;
+  const __amdgpu_buffer_rsrc_t rsw = make_rsrc(wsc, NBS * GS * SB);
+  auto dma_src = [&](int q, int64_t rows, uint32_t kbyte) -> uint32_t {
+    const int row = q >> 3, c = (q & 7) ^ ((row >> 1) & 7);
+    const uint32_t kc = kbyte + c * 16;
+    return (row < rows && kc < (uint32_t)K) ? (uint32_t)(row * K) + kc : kOOB;
+  };
+  uint32_t saoff[MI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    const int r = wm * 64 + i * 16 + l16;
+    saoff[i] = r < mrows ? (uint32_t)(r * GS * SB) : kOOB;
+  }
+  const int64_t nb0 = (tl.n0 + wn * 64) >> 5;        // the wave's two weight blocks
+  float sa_reg[2][MI][4];
+  float sw_reg[2][2][4];
+
+  auto issue = [&](int kb, int buf) {
+    uint8_t* sx = lds + buf * STAGE;
+    uint8_t* sw = sx + XBYTES;
+    const uint32_t kbyte = (uint32_t)kb * 128;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int q = (j * WAVES + wave) * 64 + lane;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, BSFP8_LDS(sx + (j * WAVES + wave) * 1024), 16,
+                                               dma_src(q, mrows, kbyte), 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, BSFP8_LDS(sw + (j * WAVES + wave) * 1024), 16,
+                                               dma_src(q, nrows, kbyte), 0, 0, 0);
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int gi = kb * 4 + g;
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const uint32_t off = (saoff[i] == kOOB || gi >= GS) ? kOOB : saoff[i] + gi * SB;
+        sa_reg[buf][i][g] = FMT == 0
+            ? __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsa, off, 0, 0))
+            : e8m0_f32(__builtin_amdgcn_raw_buffer_load_b8(rsa, off, 0, 0));
+      }
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int64_t nbs = nb0 + b;
+        const uint32_t off = (nbs < NBS && gi < GS) ? (uint32_t)((nbs * GS + gi) * SB) : kOOB;
+        sw_reg[buf][b][g] = FMT == 0
+            ? __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsw, off, 0, 0))
+            : e8m0_f32(__builtin_amdgcn_raw_buffer_load_b8(rsw, off, 0, 0));
+      }
+    }
+  };
+
+  v4f acc[NI][MI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < MI; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  auto step = [&](auto buf_c, int kb_next) {
+    constexpr int buf = decltype(buf_c)::value;
+    const uint8_t* sx = lds + buf * STAGE + (wm * 64 + l16) * kRowBytes;
+    const uint8_t* swl = lds + buf * STAGE + XBYTES + (wn * 64 + l16) * kRowBytes;
+    issue(kb_next, buf ^ 1);
+    const v4f zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      // rows start at multiples of 16: the row swizzle is the lane's (l16 >> 1)
+      const int u = 4 * g + g4;
+      const int off = (((u >> 1) ^ (l16 >> 1)) << 4) + ((u & 1) << 3);
+      long bx[MI], aw[NI];
+#pragma unroll
+      for (int j = 0; j < MI; ++j) bx[j] = *(const long*)(sx + j * 16 * kRowBytes + off);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) aw[i] = *(const long*)(swl + i * 16 * kRowBytes + off);
+      float sc[2][MI];
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int j = 0; j < MI; ++j) sc[b][j] = sa_reg[buf][j][g] * sw_reg[buf][b][g];
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int j = 0; j < MI; ++j) {
+          const v4f t = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(aw[i], bx[j], zero, 0, 0, 0);
+          const float s = sc[i >> 1][j];
+          acc[i][j][0] = fmaf(t[0], s, acc[i][j][0]);
+          acc[i][j][1] = fmaf(t[1], s, acc[i][j][1]);
+          acc[i][j][2] = fmaf(t[2], s, acc[i][j][2]);
+          acc[i][j][3] = fmaf(t[3], s, acc[i][j][3]);
+        }
+    }
+  };
+
+  issue(0, 0);
+  for (int kb0 = 0;; kb0 += 2) {
+    bool last = false;
+    static_for<2>([&](auto sc) {
+      constexpr int st = decltype(sc)::value;
+      if (last) return;
+      const int kb = kb0 + st;
+      wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      step(std::integral_constant<int, st>{}, kb + 1);
+      last = kb + 1 >= KB;
+    });
+    if (last) break;
+  }
+  wait_vmcnt<0>();
+
+  // lane holds n = 16 i + 4 g4 + {0..3} of its wave's columns, token m_j
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int64_t n = tl.n0 + wn * 64 + i * 16 + 4 * g4;
+    if (n >= N) continue;
+#pragma unroll
+    for (int j = 0; j < MI; ++j) {
+      const int64_t m = tl.m0 + wm * 64 + j * 16 + l16;
+      if (m < M) store_out4(y, N, m, n, acc[i][j], bias);
+    }
+  }
+#endif
+}
+
+template __global__ void gemm_b32_kernel<0>(const uint8_t* __restrict__, const void* __restrict__,
+                                            const uint8_t* __restrict__, const void* __restrict__,
+                                            const uint16_t* __restrict__, uint16_t* __restrict__,
+                                            int64_t, int64_t, int64_t);
+template __global__ void gemm_b32_kernel<1>(const uint8_t* __restrict__, const void* __restrict__,
+                                            const uint8_t* __restrict__, const void* __restrict__,
+                                            const uint16_t* __restrict__, uint16_t* __restrict__,
+                                            int64_t, int64_t, int64_t);
+
 // Explicit instantiations of every tile configuration the dispatcher below
 // can launch (the host pass does not always emit launch stubs for kernel
 // templates that are only instantiated implicitly).
@@ -957,10 +1133,12 @@ bool linear_fused(int64_t M, int64_t N) {
   return M > 0 && M <= kDecodeMaxM && N <= kDecodeFusedMaxN;
 }
 
-size_t linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  if (M <= 0 || linear_fused(M, N)) return 0;   // quantization inside the decode kernel
-  const int64_t G = (K + 127) / 128;
+size_t linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int blk) {
+  if (M <= 0) return 0;
   auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  if (blk == 32) return up((size_t)M * K) + up((size_t)M * ((K + 31) / 32) * 4);
+  if (linear_fused(M, N)) return 0;   // quantization inside the decode kernel
+  const int64_t G = (K + 127) / 128;
   return up((size_t)M * K) + up((size_t)M * G * 4) + gemm_workspace_bytes(M, N, K);
 }
 
@@ -991,7 +1169,20 @@ hipError_t launch_decode(const GemmArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+hipError_t launch_b32(const GemmArgs& a, hipStream_t st) {
+  int64_t tiles = (a.M + 127) / 128 * ((a.N + 127) / 128);
+  tiles = (tiles + 7) / 8 * 8;                   // whole rounds over the 8 XCDs
+  if (a.fmt == 0)
+    hipLaunchKernelGGL(gemm_b32_kernel<0>, dim3((unsigned)tiles), dim3(256), 0, st, a.xq, a.xs,
+                       a.wq, a.ws, a.bias, a.y, a.M, a.N, a.K);
+  else
+    hipLaunchKernelGGL(gemm_b32_kernel<1>, dim3((unsigned)tiles), dim3(256), 0, st, a.xq, a.xs,
+                       a.wq, a.ws, a.bias, a.y, a.M, a.N, a.K);
+  return hipGetLastError();
+}
+
 hipError_t launch_block_gemm(const GemmArgs& a, hipStream_t st) {
+  if (a.blk == 32) return launch_b32(a, st);
   if (a.M <= kDecodeMaxM) return a.fmt == 0 ? launch_decode<0>(a, st) : launch_decode<1>(a, st);
   return a.fmt == 0 ? launch_lds<0, false>(a, st) : launch_lds<1, false>(a, st);
 }

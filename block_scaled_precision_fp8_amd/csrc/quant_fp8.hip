@@ -55,16 +55,22 @@ __device__ __forceinline__ uint2 encode8(const Unpacked& u, float amax, float* s
   return r;
 }
 
-// One 16-lane quarter-wave owns one 1x128 group of one row: each lane holds
-// eight consecutive bf16 values (one 16-byte load).  A workgroup of 16
-// quarters covers QG consecutive groups of RQ rows (QG * RQ = 16) and walks
-// kActRows such row sets, with kActUnroll loads issued before use.
+// One 16-lane quarter-wave owns 128 consecutive values of one row: each lane
+// holds eight consecutive bf16 values (one 16-byte load).  A workgroup of 16
+// quarters covers QG consecutive 128-value chunks of RQ rows (QG * RQ = 16)
+// and walks kActRows such row sets, with kActUnroll loads issued before use.
+// GK is the group width: 128 (the quarter-wave is one group) or 32 (four
+// lanes per group, for (32, 32) weight blocks); G counts 128-value chunks,
+// GS the stored scales per row.
 // STATIC: one calibrated scale for the whole tensor, read from `sscale`
 // (fp32, or the E8M0 byte), replaces the group amax.
-template <int FMT, bool STATIC>
+template <int FMT, bool STATIC, int GK = 128>
 __global__ __launch_bounds__(256) void quant_act_kernel(
     const uint16_t* __restrict__ x, int M, int K, int64_t ldx, int G, int qg_log2,
     uint8_t* __restrict__ xq, void* __restrict__ scale, const void* sscale) {
+  static_assert(GK == 128 || GK == 32, "group width");
+  constexpr int LPG = GK / 8;                // lanes per group
+  const int GS = (K + GK - 1) / GK;
   const int tid = threadIdx.x;
   const int l16 = tid & 15;
   const int q = tid >> 4;
@@ -100,17 +106,18 @@ __global__ __launch_bounds__(256) void quant_act_kernel(
         codes.y = act_encode4<FMT>(f.f[4], f.f[5], f.f[6], f.f[7], sf, se);
       } else {
         float amax = amax8(f);
-        amax = fmaxf(amax, __shfl_xor(amax, 1, 16));
-        amax = fmaxf(amax, __shfl_xor(amax, 2, 16));
-        amax = fmaxf(amax, __shfl_xor(amax, 4, 16));
-        amax = fmaxf(amax, __shfl_xor(amax, 8, 16));
+#pragma unroll
+        for (int o = 1; o < LPG; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
         codes = encode8<FMT>(f, amax, &sf, &se);
       }
       if (m < M) {
         if (kvalid) *(uint2*)(xq + (int64_t)m * K + k0) = codes;
-        if (gvalid && l16 == 0) {
-          if (FMT == 0) ((float*)scale)[(int64_t)m * G + g] = sf;
-          else ((uint8_t*)scale)[(int64_t)m * G + g] = (uint8_t)(se + 127);
+        // the group's first lane stores its scale (a group exists when its
+        // first element is in range)
+        if (kvalid && (l16 & (LPG - 1)) == 0) {
+          const int64_t gi = (int64_t)m * GS + k0 / GK;
+          if (FMT == 0) ((float*)scale)[gi] = sf;
+          else ((uint8_t*)scale)[gi] = (uint8_t)(se + 127);
         }
       }
     }
@@ -118,14 +125,20 @@ __global__ __launch_bounds__(256) void quant_act_kernel(
   }
 }
 
-// One workgroup per 128x128 weight block.  Thread t loads column chunk
+// One workgroup per 128x128 tile of W.  Thread t loads column chunk
 // (t % 16) of rows (t / 16) + 16 i, i = 0..7: each wave reads four full
-// 256-byte row segments per load instruction.
-template <int FMT>
+// 256-byte row segments per load instruction.  BLK = 128: the tile is one
+// weight block.  BLK = 32: the tile holds 4 x 4 blocks of 32 x 32; block
+// (rb, cb) is rows 32 rb + {r0, r0 + 16} (loads 2 rb and 2 rb + 1) and
+// column chunks 4 cb .. 4 cb + 3, so its amax gathers over lanes xor 1, 2
+// (chunks), xor 16, 32 (rows within a wave) and the four waves.
+template <int FMT, int BLK = 128>
 __global__ __launch_bounds__(256) void quant_weight_kernel(
     const uint16_t* __restrict__ w, int N, int K, int64_t ldw, int KB,
     uint8_t* __restrict__ wq, void* __restrict__ scale) {
-  __shared__ float red[4];
+  static_assert(BLK == 128 || BLK == 32, "block size");
+  constexpr int NSB = kBlock / BLK;          // blocks per tile side
+  __shared__ float red[4][NSB][NSB];
   const int kb = blockIdx.x, nb = blockIdx.y;
   const int t = threadIdx.x;
   const int ch = t & 15, r0 = t >> 4;
@@ -139,26 +152,48 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(
     if (kvalid && n < N)
       v[i] = ld_stream16(w + (int64_t)n * ldw + k0);
   }
-  float amax = 0.0f;
+  // per block row rb (loads i with i * NSB / 8 == rb): lane-local amax, then
+  // over the lanes and waves that share the block
+  float amax[NSB];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, amax8(unpack8(v[i])));
+  for (int rb = 0; rb < NSB; ++rb) amax[rb] = 0.0f;
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
-  if ((t & 63) == 0) red[t >> 6] = amax;
+  for (int i = 0; i < 8; ++i) amax[i * NSB / 8] = fmaxf(amax[i * NSB / 8], amax8(unpack8(v[i])));
+  const int cb = ch / (16 / NSB);
+#pragma unroll
+  for (int rb = 0; rb < NSB; ++rb) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      if (BLK == 32 && (o == 4 || o == 8)) continue;    // keep column blocks apart
+      amax[rb] = fmaxf(amax[rb], __shfl_xor(amax[rb], o, 64));
+    }
+    if ((t & 63) == cb * (16 / NSB)) red[t >> 6][rb][cb] = amax[rb];
+  }
   __syncthreads();
-  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+#pragma unroll
+  for (int rb = 0; rb < NSB; ++rb)
+    amax[rb] = fmaxf(fmaxf(red[0][rb][cb], red[1][rb][cb]), fmaxf(red[2][rb][cb], red[3][rb][cb]));
 
-  float sf = 0.0f;
-  int se = 0;
+  float sf[NSB];
+  int se[NSB];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
+    const int rb = i * NSB / 8;
     const int n = nb * kBlock + r0 + 16 * i;
-    const uint2 codes = encode8<FMT>(unpack8(v[i]), amax, &sf, &se);
+    const uint2 codes = encode8<FMT>(unpack8(v[i]), amax[rb], &sf[rb], &se[rb]);
     if (kvalid && n < N) *(uint2*)(wq + (int64_t)n * K + k0) = codes;
   }
-  if (t == 0) {
-    if (FMT == 0) ((float*)scale)[(int64_t)nb * KB + kb] = sf;
-    else ((uint8_t*)scale)[(int64_t)nb * KB + kb] = (uint8_t)(se + 127);
+  // one thread per block stores its scale: rows r0 == 0, first chunk of cb
+  if (r0 == 0 && (ch % (16 / NSB)) == 0 && kvalid) {
+    const int KS = (K + BLK - 1) / BLK;
+#pragma unroll
+    for (int rb = 0; rb < NSB; ++rb) {
+      const int nbs = nb * NSB + rb, kbs = kb * NSB + cb;
+      if (nbs * BLK >= N) continue;
+      const int64_t gi = (int64_t)nbs * KS + kbs;
+      if (FMT == 0) ((float*)scale)[gi] = sf[rb];
+      else ((uint8_t*)scale)[gi] = (uint8_t)(se[rb] + 127);
+    }
   }
 }
 
@@ -166,7 +201,8 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(
 using namespace detail;
 
 hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int fmt,
-                            uint8_t* xq, void* scale, hipStream_t s, const void* static_scale) {
+                            uint8_t* xq, void* scale, hipStream_t s, const void* static_scale,
+                            int group_k) {
   const int G = (int)((K + kBlock - 1) / kBlock);
   int qg_log2 = 0;
   while ((1 << qg_log2) < G && qg_log2 < 4) ++qg_log2;
@@ -174,29 +210,34 @@ hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx
   int64_t gy = (M + RQ * kActRows - 1) / (RQ * kActRows);
   if (gy > 65535) gy = 65535;
   dim3 grid((G + QG - 1) / QG, (unsigned)gy);
-#define BSFP8_ACT(F, S)                                                                      \
-  hipLaunchKernelGGL((quant_act_kernel<F, S>), grid, dim3(256), 0, s, x, (int)M, (int)K, ldx, \
+#define BSFP8_ACT(F, S, GK)                                                                    \
+  hipLaunchKernelGGL((quant_act_kernel<F, S, GK>), grid, dim3(256), 0, s, x, (int)M, (int)K, ldx, \
                      G, qg_log2, xq, scale, static_scale)
   if (static_scale) {
-    if (fmt == 0) BSFP8_ACT(0, true); else BSFP8_ACT(1, true);
+    if (fmt == 0) BSFP8_ACT(0, true, 128); else BSFP8_ACT(1, true, 128);
+  } else if (group_k == 32) {
+    if (fmt == 0) BSFP8_ACT(0, false, 32); else BSFP8_ACT(1, false, 32);
   } else {
-    if (fmt == 0) BSFP8_ACT(0, false); else BSFP8_ACT(1, false);
+    if (fmt == 0) BSFP8_ACT(0, false, 128); else BSFP8_ACT(1, false, 128);
   }
 #undef BSFP8_ACT
   return hipGetLastError();
 }
 
 hipError_t launch_quant_weight(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, int fmt,
-                               uint8_t* wq, void* scale, hipStream_t s) {
+                               uint8_t* wq, void* scale, hipStream_t s, int block) {
   const int KB = (int)((K + kBlock - 1) / kBlock);
   const int NB = (int)((N + kBlock - 1) / kBlock);
   dim3 grid(KB, NB);
-  if (fmt == 0)
-    hipLaunchKernelGGL(quant_weight_kernel<0>, grid, dim3(256), 0, s, w, (int)N, (int)K, ldw, KB,
-                       wq, scale);
-  else
-    hipLaunchKernelGGL(quant_weight_kernel<1>, grid, dim3(256), 0, s, w, (int)N, (int)K, ldw, KB,
-                       wq, scale);
+#define BSFP8_WQ(F, B)                                                                        \
+  hipLaunchKernelGGL((quant_weight_kernel<F, B>), grid, dim3(256), 0, s, w, (int)N, (int)K, ldw, \
+                     KB, wq, scale)
+  if (block == 32) {
+    if (fmt == 0) BSFP8_WQ(0, 32); else BSFP8_WQ(1, 32);
+  } else {
+    if (fmt == 0) BSFP8_WQ(0, 128); else BSFP8_WQ(1, 128);
+  }
+#undef BSFP8_WQ
   return hipGetLastError();
 }
 

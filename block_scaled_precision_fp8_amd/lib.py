@@ -19,6 +19,7 @@ SCALE_FLOAT, SCALE_UE8M0 = 0, 1
 ACT_DYNAMIC, ACT_STATIC = 0, 1
 OP_BLOCK_GEMM, OP_LINEAR, OP_GROUPED_GEMM, OP_FP4_QUANT, OP_FP4_GEMM, OP_FP8_FP4_GEMM = \
     0, 1, 2, 3, 4, 5
+OP_LINEAR_B32 = 6
 GEMM_NONE, GEMM_TILE_128x256, GEMM_TILE_256x256, GEMM_DECODE = 0, 2, 3, 4
 
 EXPORTS = ("bsfp8_version", "bsfp8_status_string", "bsfp8_workspace_size", "bsfp8_gemm_kernel",
@@ -192,7 +193,8 @@ def fp8_block_gemm(xq, x_scale, wq, w_scale_inv, y, bias=None, block_n=128, bloc
                    scale_fmt=SCALE_FLOAT, workspace=None, stream=None):
     M, K = xq.shape
     N = wq.shape[0]
-    ws, wsb = _workspace(OP_BLOCK_GEMM, M, N, K, 0, workspace, xq.device)
+    ws, wsb = (None, 0) if block_n == 32 else _workspace(OP_BLOCK_GEMM, M, N, K, 0, workspace,
+                                                          xq.device)
     _check("fp8_block_gemm", load().fp8_block_gemm(
         _ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale_inv), _ptr(bias), _ptr(y), M, N, K,
         block_n, block_k, scale_fmt, _ptr(ws), wsb, _stream(stream)))
@@ -202,7 +204,8 @@ def fp8_linear(x, wq, w_scale_inv, y, bias=None, block_n=128, block_k=128,
                act_scheme=ACT_DYNAMIC, scale_fmt=SCALE_FLOAT, workspace=None, stream=None):
     M = x.shape[0]
     N, K = wq.shape
-    ws, wsb = _workspace(OP_LINEAR, M, N, K, 0, workspace, x.device)
+    ws, wsb = _workspace(OP_LINEAR_B32 if block_k == 32 else OP_LINEAR, M, N, K, 0, workspace,
+                         x.device)
     _check("fp8_linear", load().fp8_linear(
         _ptr(x), x.stride(0), _ptr(wq), _ptr(w_scale_inv), _ptr(bias), _ptr(y), M, N, K,
         block_n, block_k, act_scheme, scale_fmt, _ptr(ws), wsb, _stream(stream)))

@@ -71,7 +71,8 @@ typedef enum {
   BSFP8_OP_GROUPED_GEMM = 2,
   BSFP8_OP_FP4_QUANT = 3,
   BSFP8_OP_FP4_GEMM = 4,
-  BSFP8_OP_FP8_FP4_GEMM = 5
+  BSFP8_OP_FP8_FP4_GEMM = 5,
+  BSFP8_OP_LINEAR_B32 = 6      /* fp8_linear with (32, 32) weight blocks */
 } bsfp8_op;
 
 /* Kernels fp8_block_gemm / fp8_linear choose between (bsfp8_gemm_kernel). */
@@ -97,8 +98,10 @@ BSFP8_API const char* bsfp8_status_string(int32_t status);
  *   x        bf16 [M][ldx], read-only; only the first K columns are used.
  *   M, K     rows (tokens) and columns (input channels); K % 16 == 0.
  *   ldx      row stride of x in elements, ldx >= K, ldx % 8 == 0.
- *   group_k  group width; must equal the weight block's K size, 128
- *            ([FG-FP8] §一: the groups line up with the weight blocks).
+ *   group_k  group width; must equal the weight block's K size: 128, or
+ *            32 for (32, 32) weight blocks ([FG-FP8] §一: the groups line
+ *            up with the weight blocks; §九: (32, 32) is a tested
+ *            non-default block).  STATIC takes 128 only.
  *   act_scheme  BSFP8_ACT_DYNAMIC: the scales below, per group.
  *               BSFP8_ACT_STATIC: x_scale[0] holds the calibrated
  *               per-tensor scale on entry (fp32 s > 0, or the E8M0 byte
@@ -115,7 +118,8 @@ BSFP8_API const char* bsfp8_status_string(int32_t status);
  *   x_scale  out, [M][ceil(K/group_k)] fp32 (FLOAT) or uint8 (UE8M0); the
  *            dequantization multiplier of each group.
  * Errors: EINVAL (null pointers, M or K < 0, K % 16, ldx < K, ldx % 8,
- * group_k <= 0, bad enum, misalignment); ENOTSUP (group_k other than 128).
+ * group_k <= 0, bad enum, misalignment); ENOTSUP (group_k other than 128 or
+ * 32, or 32 with STATIC).
  */
 BSFP8_API int32_t fp8_quant_act(const void* x, int64_t M, int64_t K, int64_t ldx,
                       int32_t group_k, int32_t act_scheme, int32_t scale_fmt,
@@ -124,16 +128,17 @@ BSFP8_API int32_t fp8_quant_act(const void* x, int64_t M, int64_t K, int64_t ldx
 /*
  * fp8_quant_weight -- per 2D block weight quantization
  * (weight_block_size = (block_n, block_k), [FG-FP8] §一 first bullet; the
- * scale tensor weight_scale_inv has shape (ceil(N/128), ceil(K/128)),
+ * scale tensor weight_scale_inv has shape (ceil(N/bn), ceil(K/bk)),
  * [FG-FP8] §一 third paragraph).
  *
  *   w        bf16 [N][ldw] in nn.Linear orientation (out, in); read-only.
  *   N, K     output and input features; K % 16 == 0.
  *   ldw      row stride in elements, ldw >= K, ldw % 8 == 0.
- *   block_n, block_k   must be 128 (other positive sizes -> ENOTSUP).
+ *   block_n, block_k   (128, 128) or (32, 32) ([FG-FP8] §九); other
+ *            positive sizes -> ENOTSUP.
  *   scale_fmt  as for fp8_quant_act, with the amax over the whole block.
  *   wq       out, E4M3 [N][K].
- *   w_scale_inv  out, [ceil(N/128)][ceil(K/128)] fp32 or uint8 E8M0.
+ *   w_scale_inv  out, [ceil(N/bn)][ceil(K/bk)] fp32 or uint8 E8M0.
  * A partial edge block takes its amax over its in-range elements only.
  */
 BSFP8_API int32_t fp8_quant_weight(const void* w, int64_t N, int64_t K, int64_t ldw,
@@ -144,25 +149,29 @@ BSFP8_API int32_t fp8_quant_weight(const void* w, int64_t N, int64_t K, int64_t 
  * fp8_block_gemm -- the block-scaled FP8 GEMM ([FG-FP8] §一: aligned act
  * groups and weight blocks let the matmul run block by block):
  *
- *   Y[m][n] = bf16_rne( sum_kb S_a[m][kb] * S_w[n/128][kb]
+ *   Y[m][n] = bf16_rne( sum_kb S_a[m][kb] * S_w[n/B][kb]
  *                          * sum_{k in kb} Xq[m][k] * Wq[n][k]  + bias[n] )
  *
- * with exact FP8 products, fp32 accumulation, the combined scale applied to
- * the fp32 partial sum once per 128-wide K block, and the unquantized bias
- * ([FG-FP8] §三: bias is not quantized) added in fp32.
+ * with B the block edge (128, or 32), exact FP8 products, fp32
+ * accumulation, the combined scale applied to the fp32 partial sum once per
+ * B-wide K block, and the unquantized bias ([FG-FP8] §三: bias is not
+ * quantized) added in fp32.
  *
  *   xq, x_scale       as written by fp8_quant_act (M rows).
  *   wq, w_scale_inv   as written by fp8_quant_weight (N rows).
  *   bias              bf16 [N] or NULL.
  *   y                 out, bf16 [M][N].
- *   block_n, block_k  must be 128.
+ *   block_n, block_k  (128, 128), or (32, 32) with 1 x 32 act groups
+ *                     (a separate kernel, no workspace).
  *   workspace         device buffer of at least
  *                     bsfp8_workspace_size(BSFP8_OP_BLOCK_GEMM, M, N, K, 0)
  *                     bytes (may be NULL when that size is 0); contents on
  *                     entry are ignored, on exit undefined.
  * Errors: EINVAL (dims < 0, K % 16, N % 8, null required pointers, bad
- * enum, misalignment); ENOTSUP (block sizes other than 128, K > 2^22);
- * ENOSPC.  fp8_linear and fp8_grouped_gemm share these limits.
+ * enum, misalignment); ENOTSUP (other block sizes, K > 2^22); ENOSPC.
+ * fp8_linear shares these limits (with (32, 32) blocks its workspace is
+ * bsfp8_workspace_size(BSFP8_OP_LINEAR_B32, ...)); fp8_grouped_gemm takes
+ * 128 x 128 blocks only.
  */
 BSFP8_API int32_t fp8_block_gemm(const void* xq, const void* x_scale, const void* wq,
                        const void* w_scale_inv, const void* bias, void* y,
@@ -319,14 +328,15 @@ BSFP8_API int32_t fp8_fp4_gemm(const void* xq, const void* x_scale, const void* 
 /*
  * fp8_dequant_weight -- fold the block scales back into the weights, the
  * dequantize-on-load step for pre-quantized checkpoints ([FG-FP8] §五,
- * Fp8Dequantize):  W[n][k] = bf16_rne(fl32(E4M3(wq[n][k]) * S_w[n/128][k/128])).
+ * Fp8Dequantize):  W[n][k] = bf16_rne(fl32(E4M3(wq[n][k]) * S_w[n/B][k/B]))
+ * for (B, B) blocks, B = 128 or 32.
  *
  *   wq           E4M3 [N][K], K % 16 == 0.
- *   w_scale_inv  [ceil(N/128)][ceil(K/128)] fp32 or UE8M0 bytes.
+ *   w_scale_inv  [ceil(N/B)][ceil(K/B)] fp32 or UE8M0 bytes.
  *   w            out, bf16 [N][K].
  * Codes 0x7F / 0xFF (E4M3 NaN) and the E8M0 byte 0xFF are outside the
  * contract.  Errors: EINVAL (sizes, null pointers, misalignment, bad enum);
- * ENOTSUP (block sizes other than 128).
+ * ENOTSUP (block sizes other than (128, 128) and (32, 32)).
  */
 BSFP8_API int32_t fp8_dequant_weight(const void* wq, int64_t N, int64_t K, int32_t block_n,
                                      int32_t block_k, int32_t scale_fmt,

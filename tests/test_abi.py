@@ -72,7 +72,7 @@ def _qw(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(N=-1), L.EINVAL), (dict(K=8), L.EINVAL), (dict(bn=0), L.EINVAL),
-    (dict(bk=-128), L.EINVAL), (dict(bn=32, bk=32), L.ENOTSUP), (dict(fmt=-1), L.EINVAL),
+    (dict(bk=-128), L.EINVAL), (dict(bn=64, bk=64), L.ENOTSUP), (dict(bn=32, bk=128), L.ENOTSUP), (dict(fmt=-1), L.EINVAL),
     (dict(wq=None), L.EINVAL), (dict(ws=MIS), L.EINVAL), (dict(N=0), L.OK),
 ])
 def test_quant_weight_argument_checks(kw, code):
