@@ -20,7 +20,7 @@ the MoE expert MLP (256 experts, Zipf-routed top-8: gate/up grouped GEMM,
 the same with the fused SiLU-mul requant, the down GEMM on its output), the
 NVFP4-style MLP (fp4_quant + fp4_group_gemm) with its FP8 attention
 projection, the FP8 activation x MXFP4 weight linear at DeepSeek-V3 expert
-shapes, and weight quantization.
+shapes, FP8 linears with (32, 32) weight blocks, and weight quantization.
 
 ``roofline`` is for the dominant kernel, the large-M GEMM with 256 x 256 tiles
 (gemm_lds_kernel, every run the library sends to it, split-K ones included
@@ -462,6 +462,53 @@ def run_mxfp4(torch, L, synth, steps, warmup, dev, sp):
     return out
 
 
+def run_block32(torch, L, synth, steps, warmup, dev, sp):
+    """FP8 linears with (32, 32) weight blocks and 1x32 act groups (fp32
+    scales) at Llama-3-8B o_proj / gate+up shapes: fp8_linear, act quant
+    included."""
+    out = []
+    stream = torch.cuda.current_stream()
+    for M, K, N in ((16, 4096, 4096), (2048, 4096, 4096), (8192, 4096, 28672)):
+        wb = synth.device_normal_bf16((N, K), 0.02, "llama", "w", index=N + 32)
+        copies = []
+        for c in range(2):
+            wq = torch.empty((N, K), dtype=torch.uint8, device=dev)
+            ws = torch.empty((N // 32, K // 32), dtype=torch.float32, device=dev)
+            L.fp8_quant_weight(wb, wq, ws, block_n=32, block_k=32, stream=sp)
+            copies.append((wq, ws))
+        del wb
+        x = synth.device_llama_acts(M, K, index=M)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        wsp = torch.empty(L.workspace_size(L.OP_LINEAR_B32, M, N, K), dtype=torch.uint8,
+                          device=dev)
+
+        def call(i):
+            wq, ws = copies[i & 1]
+            L.fp8_linear(x, wq, ws, y, block_n=32, block_k=32, workspace=wsp, stream=sp)
+        for i in range(warmup):
+            call(i)
+        torch.cuda.synchronize()
+        tm = Timer(torch, stream)
+        for i in range(steps):
+            tm.mark("a")
+            call(i)
+            tm.mark("b")
+        torch.cuda.synchronize()
+        ms = tm.ms("a", "b")
+        fl = 2.0 * M * N * K
+        sa, sw = 4 * M * (K // 32), 4 * (N // 32) * (K // 32)     # fp32 scales
+        byt = (3 * M * K + sa) + (M * K + sa + N * K + sw + 2 * M * N)   # quant + GEMM
+        d = dict(M=M, K=K, N=N, linear_us=round(ms * 1e3, 2),
+                 tflops=round(fl / (ms * 1e-3) / 1e12, 1),
+                 frac_fp8_peak=round(fl / (ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+                 gbs=round(byt / (ms * 1e-3) / 1e9, 1))
+        out.append(d)
+        log(f"[block32] {d}")
+        del copies, x, y, wsp
+        torch.cuda.empty_cache()
+    return out
+
+
 def run_wquant(torch, L, synth, steps, warmup, dev, sp):
     """Weight quantization (load-time step) of the 28672 x 4096 weight."""
     N, K = 28672, 4096
@@ -529,7 +576,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--suites", default="deepseek,moe,nvfp4,mxfp4,wquant",
+    ap.add_argument("--suites", default="deepseek,moe,nvfp4,mxfp4,block32,wquant",
                     help="extra rows timed for `detail` (comma list, or 'none')")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a known-size "
@@ -565,7 +612,7 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
                 "traffic": traffic,
-                "kernel": "gemm_lds_kernel<0,4,2,64,128,false> (fp32 scales, 256x256 "
+                "kernel": "gemm_lds_kernel<0,4,2,64,128,false,false,false> (fp32 scales, 256x256 "
                           "tiles), large-M block-scaled GEMM",
                 "launches_per_step": r["n_big"],
                 "avg_launch_us": round(r["big_ms"] / r["n_big"] * 1e3, 2),
@@ -587,6 +634,9 @@ def main():
     if "mxfp4" in suites:
         detail["fp8_x_mxfp4_ue8m0"] = run_mxfp4(torch, L, synth, max(5, args.steps // 2), 2,
                                                 dev, sp)
+    if "block32" in suites:
+        detail["block32_fp32_scales"] = run_block32(torch, L, synth, max(5, args.steps // 2), 2,
+                                                    dev, sp)
     if "wquant" in suites:
         detail["weight_quant"] = run_wquant(torch, L, synth, 10, 2, dev, sp)
 
