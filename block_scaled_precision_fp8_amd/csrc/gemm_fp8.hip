@@ -57,6 +57,10 @@ __device__ __forceinline__ float load_scale(const void* p, int64_t idx) {
   return __int_as_float(((const uint8_t*)p)[idx]);   // carries the byte
 }
 
+__device__ __forceinline__ float e8m0_f32(uint32_t b) {
+  return __uint_as_float(b == 0 ? 0x00400000u : b << 23);   // 2^(b - 127)
+}
+
 // MFMA step for one 16x16 tile and one K block.
 template <int FMT>
 __device__ __forceinline__ v4f mfma_step(v4f acc, const v8i& a, const v8i& b, float sa,
@@ -671,7 +675,12 @@ constexpr int kDecodeDepth = 2;
 // and takes the X chunks g4 and g4 + 4 (the FP4 x FP8 lane pairing of the
 // scaled MFMA).  The kernel is bound by the latency of each workgroup's one
 // round of loads, not by bytes, so MXFP4 rows run at about the FP8 time.
-template <int FMT, bool FUSED, bool W4 = false>
+// B32: (32, 32) weight blocks with 1 x 32 act groups.  A lane's 32 weight
+// and activation bytes of a block are exactly the 32-wide group g4, so the
+// block runs as four MFMAs whose weight operand keeps only group g's lanes,
+// each promoted by s_a[m, g] s_w[n/32, g] in fp32 (UE8M0 bytes decoded to
+// their powers of two); the extra MFMAs are free in this HBM-bound kernel.
+template <int FMT, bool FUSED, bool W4 = false, bool B32 = false>
 __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
     const uint8_t* __restrict__ xq, const void* __restrict__ xs,
     const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ wq,
@@ -689,6 +698,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
   const int64_t nblk = n0 >> 7;
   const int64_t KW = W4 ? K / 2 : K;       // W bytes per row
   const int64_t G32 = K / 32;
+  const int64_t GS = (K + 31) / 32;        // B32: scale groups per row
+  const int64_t nb32 = n0 >> 5;            // B32: this tile's weight block row
   const uint8_t* wrow = wq + nrow * KW;
   // this lane's X elements of a block: two runs of 16 starting at kx0, kx1
   const int kx0 = W4 ? 16 * g4 : 32 * g4;
@@ -703,6 +714,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
     float swb[DEPTH];
     uint4 xa[XD], xb[XD];
     float sx[XD];
+    // B32: the four groups' scales (fp32), or this lane's group's bytes
+    float sx4[B32 ? DEPTH : 1][4], sw32[B32 ? DEPTH : 1][4];
 #pragma unroll
     for (int u = 0; u < DEPTH; ++u) {
       const int kb = kb0 + u * kDecodeWaves;
@@ -712,7 +725,23 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
       // the weight block scale: with fp32 scales it multiplies this lane's
       // OUTPUT column (token l16), so every lane needs it, whatever its row
       swb[u] = (FMT == 0) ? 0.f : __int_as_float(127);
-      if (!W4 && kb < KB) swb[u] = load_scale<FMT>(wsc, nblk * KB + kb);
+      if (!W4 && !B32 && kb < KB) swb[u] = load_scale<FMT>(wsc, nblk * KB + kb);
+      if constexpr (B32) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int64_t gi = (int64_t)kb * 4 + g;
+          const bool ok = kb < KB && gi < GS;
+          float w = 0.f, x = 0.f;
+          if (ok) w = load_scale<FMT>(wsc, nb32 * GS + gi);
+          if (ok && mvalid) x = load_scale<FMT>(xs, (int64_t)l16 * GS + gi);
+          if (FMT == 1) {
+            w = ok ? e8m0_f32(__float_as_uint(w)) : 0.f;
+            x = (ok && mvalid) ? e8m0_f32(__float_as_uint(x)) : 0.f;
+          }
+          sw32[u][g] = w;
+          sx4[u][g] = x;
+        }
+      }
       if (kb < KB && nvalid) {
         if constexpr (W4) {
           // this lane's 32 weights (group 4 kb + g4) and their scale byte
@@ -737,7 +766,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
           const int64_t k0 = (int64_t)kb * 128 + kx0, k1 = (int64_t)kb * 128 + kx1;
           if (k0 < K) xa[u] = *(const uint4*)(xq + (int64_t)l16 * K + k0);
           if (k1 < K) xb[u] = *(const uint4*)(xq + (int64_t)l16 * K + k1);
-          sx[u] = load_scale<FMT>(xs, (int64_t)l16 * KB + kb);
+          if (!B32) sx[u] = load_scale<FMT>(xs, (int64_t)l16 * KB + kb);
         }
       }
     }
@@ -781,10 +810,20 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
         sa = sx[u < XD ? u : 0];
         bx = join(xa[u < XD ? u : 0], xb[u < XD ? u : 0]);
       }
-      if constexpr (W4)
+      if constexpr (W4) {
         acc = mfma_step_w4<FMT>(acc, join(wa[u], make_uint4(0, 0, 0, 0)), bx, sa, sw4[u]);
-      else
+      } else if constexpr (B32) {
+        const v8i a = join(wa[u], wb[u]);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          v8i ag;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) ag[i] = g4 == g ? a[i] : 0;
+          acc = mfma_step<0>(acc, ag, bx, sx4[u][g], sw32[u][g]);   // fp32 promotion
+        }
+      } else {
         acc = mfma_step<FMT>(acc, join(wa[u], wb[u]), bx, sa, swb[u]);
+      }
     }
   }
   red[wave][lane] = acc;
@@ -812,10 +851,6 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
 // takes for group g is half (u & 1) of logical chunk u >> 1, u = 4 g + g4,
 // and the chunk swizzle keeps those reads free of bank conflicts.
 // ------------------------------------------------------------------------
-__device__ __forceinline__ float e8m0_f32(uint32_t b) {
-  return __uint_as_float(b == 0 ? 0x00400000u : b << 23);   // 2^(b - 127)
-}
-
 template <int FMT>
 __global__ __launch_bounds__(256, 2) void gemm_b32_kernel(
     const uint8_t* __restrict__ xq, const void* __restrict__ xs, const uint8_t* __restrict__ wq,
@@ -1160,6 +1195,9 @@ hipError_t launch_decode(const GemmArgs& a, hipStream_t st) {
   if (a.x_bf16)
     hipLaunchKernelGGL((gemm_decode_kernel<FMT, true>), grid, block, 0, st, nullptr, nullptr,
                        a.x_bf16, a.ldx, a.wq, a.ws, a.bias, a.y, (int)a.M, a.N, a.K);
+  else if (a.blk == 32)
+    hipLaunchKernelGGL((gemm_decode_kernel<FMT, false, false, true>), grid, block, 0, st, a.xq,
+                       a.xs, nullptr, (int64_t)0, a.wq, a.ws, a.bias, a.y, (int)a.M, a.N, a.K);
   else if (a.w4)
     hipLaunchKernelGGL((gemm_decode_kernel<FMT, false, true>), grid, block, 0, st, a.xq, a.xs,
                        nullptr, (int64_t)0, a.wq, a.ws, a.bias, a.y, (int)a.M, a.N, a.K);
@@ -1182,7 +1220,7 @@ hipError_t launch_b32(const GemmArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_block_gemm(const GemmArgs& a, hipStream_t st) {
-  if (a.blk == 32) return launch_b32(a, st);
+  if (a.blk == 32 && a.M > kDecodeMaxM) return launch_b32(a, st);
   if (a.M <= kDecodeMaxM) return a.fmt == 0 ? launch_decode<0>(a, st) : launch_decode<1>(a, st);
   return a.fmt == 0 ? launch_lds<0, false>(a, st) : launch_lds<1, false>(a, st);
 }

@@ -95,7 +95,7 @@ def _gemm(M, N, K, fmt, bias, seed):
 @pytest.mark.parametrize("fmt", [0, 1])
 @pytest.mark.parametrize("M,N,K,bias", [
     (1, 256, 256, False), (16, 264, 400, True), (130, 520, 640, False), (300, 1000, 1040, True),
-    (257, 136, 4112, False),
+    (257, 136, 4112, False), (5, 136, 4112, True),
 ])
 def test_block32_gemm_parity(M, N, K, bias, fmt):
     say(f"gemm 32x32 M={M} N={N} K={K} fmt={fmt}")
