@@ -9,7 +9,7 @@ What the pages fix ([FG-FP8] §四, §五, §七):
 * power-of-two UE8M0 scales stored in float32 containers are converted
   exactly to the float8_e8m0fnu dtype the kernels read.
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
  12. static: one calibrated per-tensor activation scale supplied by the
      caller; float: codes = E4M3(fl32(x / s)); ue8m0: the scale is the byte b
      (s = 2^(b-127)) and codes = E4M3(x * 2^-(b-127)); every 1 x 128 group's

@@ -6,7 +6,7 @@ groups of 16 elements (``group_size: 16``), while attention projections stay
 FP8.  The pages give nothing more; the scale structure (an E4M3 scale per
 16-element group times one fp32 scale per tensor) is the one the task states.
 
-Readings taken (pages silent; each also listed in the design doc):
+Readings taken (pages silent):
  1. tensor scale g = fl32(A_t / 2688), A_t = max |x| over the tensor,
     2688 = 6 * 448, so that the largest group scale is the E4M3 maximum;
     g = 1.0 when A_t = 0.  For activations g is recomputed on every call

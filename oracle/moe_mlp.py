@@ -8,7 +8,7 @@ matmuls on the FP8 path ([FG-FP8] §一 FP8Experts, §6.4); the down
 projection's input is an activation like any other, quantized per token in
 1 x 128 groups along its input channels ([FG-FP8] §一).
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
  19. expert e's gate and up projections are the two halves of one (2I, K)
      weight -- rows [0, I) gate, [I, 2I) up -- with I a multiple of 128, so
      each half starts on a 128-row weight block; both halves use the same

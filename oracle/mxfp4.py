@@ -7,7 +7,7 @@ FP4-packed expert weights, and the fast backend has an FP8-activation x
 FP4-weight linear next to the FP8 x FP8 one; V4-style scales are UE8M0
 ([FG-FP8] §七).
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
  16. weight values are E2M1 (the 4-bit float of the NVFP4 page), two per
      byte, element 2i in the low nibble;
  17. one UE8M0 scale per 1 x 32 group along K of each weight row (the

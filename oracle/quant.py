@@ -10,7 +10,7 @@ What the pages fix ([FG-FP8] §一; [HF-PT] opening list):
 * values are stored as float8_e4m3fn; scales as fp32, or as packed
   float8_e8m0fnu when ``scale_fmt="ue8m0"`` ([FG-FP8] §七).
 
-Readings taken where the pages are silent (each also listed in the design doc):
+Readings taken where the pages are silent:
  1. a scale maps the group's largest magnitude onto the E4M3 maximum 448;
  2. ``float``: s = fl32(amax / 448), codes = E4M3(fl32(x / s)) with IEEE fp32
     division and one round-to-nearest-even into E4M3; the stored scale is the
