@@ -20,7 +20,6 @@
 namespace bsfp8 {
 namespace detail {
 
-constexpr int kActRows = 8;     // rows per quarter-wave per workgroup
 constexpr int kActUnroll = 4;   // loads in flight per lane
 
 struct Unpacked { float f[8]; };
@@ -58,13 +57,14 @@ __device__ __forceinline__ uint2 encode8(const Unpacked& u, float amax, float* s
 // One 16-lane quarter-wave owns 128 consecutive values of one row: each lane
 // holds eight consecutive bf16 values (one 16-byte load).  A workgroup of 16
 // quarters covers QG consecutive 128-value chunks of RQ rows (QG * RQ = 16)
-// and walks kActRows such row sets, with kActUnroll loads issued before use.
+// and walks ROWS such row sets (8, or 2 for small activations so that more
+// workgroups share the work), with up to kActUnroll loads issued before use.
 // GK is the group width: 128 (the quarter-wave is one group) or 32 (four
 // lanes per group, for (32, 32) weight blocks); G counts 128-value chunks,
 // GS the stored scales per row.
 // STATIC: one calibrated scale for the whole tensor, read from `sscale`
 // (fp32, or the E8M0 byte), replaces the group amax.
-template <int FMT, bool STATIC, int GK = 128>
+template <int FMT, bool STATIC, int GK, int ROWS>
 __global__ __launch_bounds__(256) void quant_act_kernel(
     const uint16_t* __restrict__ x, int M, int K, int64_t ldx, int G, int qg_log2,
     uint8_t* __restrict__ xq, void* __restrict__ scale, const void* sscale) {
@@ -80,20 +80,21 @@ __global__ __launch_bounds__(256) void quant_act_kernel(
   const int k0 = g * kBlock + l16 * 8;
   const bool gvalid = g < G;
   const bool kvalid = gvalid && k0 < K;
-  for (int mb = blockIdx.y; mb * (RQ * kActRows) < M; mb += gridDim.y) {
-  const int mbase = mb * (RQ * kActRows) + (q >> qg_log2);
+  constexpr int UN = ROWS < kActUnroll ? ROWS : kActUnroll;
+  for (int mb = blockIdx.y; mb * (RQ * ROWS) < M; mb += gridDim.y) {
+  const int mbase = mb * (RQ * ROWS) + (q >> qg_log2);
 #pragma unroll
-  for (int jb = 0; jb < kActRows; jb += kActUnroll) {
-    uint4 v[kActUnroll];
+  for (int jb = 0; jb < ROWS; jb += UN) {
+    uint4 v[UN];
 #pragma unroll
-    for (int u = 0; u < kActUnroll; ++u) {
+    for (int u = 0; u < UN; ++u) {
       const int m = mbase + RQ * (jb + u);
       v[u] = make_uint4(0, 0, 0, 0);
       if (kvalid && m < M)
         v[u] = ld_stream16(x + (int64_t)m * ldx + k0);
     }
 #pragma unroll
-    for (int u = 0; u < kActUnroll; ++u) {
+    for (int u = 0; u < UN; ++u) {
       const int m = mbase + RQ * (jb + u);
       const Unpacked f = unpack8(v[u]);
       float sf = 0.0f;
@@ -207,12 +208,21 @@ hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx
   int qg_log2 = 0;
   while ((1 << qg_log2) < G && qg_log2 < 4) ++qg_log2;
   const int QG = 1 << qg_log2, RQ = 16 >> qg_log2;
-  int64_t gy = (M + RQ * kActRows - 1) / (RQ * kActRows);
+  // small activations: two rows per quarter-wave, four times the workgroups
+  const bool few = M * G <= 65536;
+  const int rows = few ? 2 : 8;
+  int64_t gy = (M + RQ * rows - 1) / (RQ * rows);
   if (gy > 65535) gy = 65535;
   dim3 grid((G + QG - 1) / QG, (unsigned)gy);
-#define BSFP8_ACT(F, S, GK)                                                                    \
-  hipLaunchKernelGGL((quant_act_kernel<F, S, GK>), grid, dim3(256), 0, s, x, (int)M, (int)K, ldx, \
-                     G, qg_log2, xq, scale, static_scale)
+#define BSFP8_ACT(F, S, GK)                                                                        \
+  do {                                                                                             \
+    if (few)                                                                                       \
+      hipLaunchKernelGGL((quant_act_kernel<F, S, GK, 2>), grid, dim3(256), 0, s, x, (int)M,      \
+                         (int)K, ldx, G, qg_log2, xq, scale, static_scale);                       \
+    else                                                                                           \
+      hipLaunchKernelGGL((quant_act_kernel<F, S, GK, 8>), grid, dim3(256), 0, s, x, (int)M,      \
+                         (int)K, ldx, G, qg_log2, xq, scale, static_scale);                       \
+  } while (0)
   if (static_scale) {
     if (fmt == 0) BSFP8_ACT(0, true, 128); else BSFP8_ACT(1, true, 128);
   } else if (group_k == 32) {
