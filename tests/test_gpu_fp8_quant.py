@@ -65,6 +65,40 @@ def test_act_quant_parity(M, K, gen, fmt):
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
+def test_act_quant_parity_many_rows(fmt):
+    """Above 65536 groups the quantizer walks eight rows per quarter-wave
+    (two below): ragged M on that path, checked in full."""
+    x = synth.llama_acts(2101, 4096, seed=5) if fmt == 0 else synth.deepseek_acts(2101, 4096, seed=5)
+    _check_act(x, fmt)
+
+
+@pytest.mark.parametrize("M,K,fmt,gen", [(8192, 14336, 0, "llama"), (4096, 7168, 1, "deepseek")])
+def test_act_quant_full_size_sampled(M, K, fmt, gen):
+    """The largest activations of the Llama and DeepSeek workloads, drawn on
+    the device; 96 rows (first, last and random) checked against the oracle."""
+    import torch
+    from block_scaled_precision_fp8_amd import lib as L
+    say(f"act quant full size M={M} K={K} fmt={fmt}")
+    x = synth.device_llama_acts(M, K, seed=1) if gen == "llama" else \
+        synth.device_deepseek_acts(M, K, seed=1)
+    xq = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    xs = torch.empty((M, K // 128), dtype=torch.float32 if fmt == 0 else torch.uint8,
+                     device="cuda")
+    L.fp8_quant_act(x, xq, xs, scale_fmt=fmt)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(2).integers(0, M, 94)]))
+    ridx = torch.from_numpy(rows).cuda()
+    xb = x[ridx].view(torch.int16).cpu().numpy().view(np.uint16)
+    rq, rs = Q.quant_act(xb, 128, fmt)
+    assert np.array_equal(u8(xq[ridx]), rq)
+    got_s = xs[ridx].cpu().numpy()
+    if fmt == 0:
+        assert np.array_equal(got_s.view(np.uint32), rs.view(np.uint32))
+    else:
+        assert np.array_equal(got_s, rs)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
 def test_act_quant_row_stride(fmt):
     _check_act(synth.llama_acts(9, 384, seed=3), fmt, ldx_pad=72)
 
