@@ -7,8 +7,9 @@ outlier channels x50, weights N(0, 0.02), 1x128 dynamic act groups, 128x128
 weight blocks, fp32 scales.  One step = one FP8 linear forward for every run:
 dynamic activation quantization (fp8_quant_act) then the block-scaled GEMM
 (fp8_block_gemm).  Weights are quantized once before timing (load-time step)
-and two quantized copies alternate step by step, so decode-sized runs read
-their weights from HBM rather than from the 256 MB Infinity Cache.
+into four copies per shape, rotated so that consecutive runs of one shape
+never share a copy: decode-sized runs read their weights from HBM rather
+than from the 256 MB Infinity Cache.
 value = GEMM flops of the step / step time (TFLOP/s, act quant included).
 Inside the timed steps HIP events bracket only the 256 x 256-tile GEMM
 launches (the roofline below); the per-run breakdown in ``detail`` comes
@@ -55,6 +56,7 @@ LLAMA_SHAPES = [(4096, 4096), (4096, 6144), (4096, 28672), (14336, 4096)]   # (K
 LLAMA_MS = [1, 16, 128, 2048, 8192]
 DEEPSEEK_SHAPES = [(7168, 1536), (1536, 24576), (7168, 18432), (18432, 7168)]
 DEEPSEEK_MS = [1, 64, 4096]
+WEIGHT_COPIES = 4         # weight sets rotated through the linear runs
 PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 MFMA
 PEAK_F16_TFLOPS = 2500.0  # MI355X dense fp16 / bf16 MFMA
 PEAK_HBM_GBS = 8000.0
@@ -88,6 +90,11 @@ def read_traffic():
         return float(kv["hbm bytes per launch (scaled)"])
     except (KeyError, ValueError):
         return None
+
+
+def copies_for(nbytes):
+    """weight copies to rotate so that the rotation spans 2x the 256 MB cache"""
+    return max(2, -(-(512 << 20) // nbytes))
 
 
 def act_bytes(M, K, sb):
@@ -126,7 +133,7 @@ def run_linears(torch, L, synth, shapes, ms, fmt, workload, steps, warmup, dev, 
     weights = {}
     for i, (K, N) in enumerate(shapes):
         copies = []
-        for c in range(2):
+        for c in range(WEIGHT_COPIES):
             sigma = 0.02 if workload == "llama" else 0.01
             wb = synth.device_normal_bf16((N, K), sigma, workload, "w", index=10 * i + c)
             wq = torch.empty((N, K), dtype=torch.uint8, device=dev)
@@ -160,7 +167,9 @@ def run_linears(torch, L, synth, shapes, ms, fmt, workload, steps, warmup, dev, 
         """one pass over every run; tm marks around every launch, or with
         big_only around the 256 x 256-tile GEMM launches only"""
         for j, r in enumerate(runs):
-            wq, wsc = weights[(r["K"], r["N"])][s & 1]
+            # consecutive runs of one shape read different copies, so no run
+            # finds its weights in the 256 MB last-level cache
+            wq, wsc = weights[(r["K"], r["N"])][(s + j) % WEIGHT_COPIES]
             every = tm is not None and not big_only
             if every:
                 tm.mark(("q", j))
@@ -332,7 +341,7 @@ def run_nvfp4(torch, L, synth, steps, warmup, dev, sp):
     mats = {}
     for name, N, K in (("gate_up", INTER, HID), ("down", HID, INTER)):
         copies = []
-        for c in range(2):
+        for c in range(copies_for(N * (K // 2 + K // 16))):
             wb = synth.device_normal_bf16((N, K), 0.015, "nvfp4", "w", index=N + c)
             q = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
             s = torch.empty((N, K // 16), dtype=torch.uint8, device=dev)
@@ -342,7 +351,7 @@ def run_nvfp4(torch, L, synth, steps, warmup, dev, sp):
             copies.append((q, s, t))
         mats[name] = (N, K, copies)
     attn = []
-    for c in range(2):
+    for c in range(copies_for(HID * HID)):
         wb = synth.device_normal_bf16((HID, HID), 0.015, "nvfp4", "w", index=7 + c)
         wq = torch.empty((HID, HID), dtype=torch.uint8, device=dev)
         ws = torch.empty((HID // 128, HID // 128), dtype=torch.float32, device=dev)
@@ -365,7 +374,7 @@ def run_nvfp4(torch, L, synth, steps, warmup, dev, sp):
                 def call(s, tm=None):
                     if tm:
                         tm.mark("a")
-                    wq, wsc = attn[s & 1]
+                    wq, wsc = attn[s % len(attn)]
                     L.fp8_linear(x, wq, wsc, y, workspace=wsp, stream=sp)
                     if tm:
                         tm.mark("b")
@@ -380,7 +389,7 @@ def run_nvfp4(torch, L, synth, steps, warmup, dev, sp):
                 wsg = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
 
                 def call(s, tm=None):
-                    q, sc, t = copies[s & 1]
+                    q, sc, t = copies[s % len(copies)]
                     if tm:
                         tm.mark("a")
                     L.fp4_quant(x, qx, sx, tx, workspace=wqs, stream=sp)
@@ -422,12 +431,13 @@ def run_mxfp4(torch, L, synth, steps, warmup, dev, sp):
     """FP8 activations (1x128 groups, UE8M0 scales) x MXFP4 weights (E2M1 in
     1x32 groups with UE8M0 scales) at the DeepSeek-V3 expert-sized shapes
     (7168 -> 18432, 18432 -> 7168), M in {1, 64, 4096}: act quant then
-    fp8_fp4_gemm.  Two weight copies alternate so decode reads HBM."""
+    fp8_fp4_gemm.  Weight copies rotate over more than twice the 256 MB cache
+    so decode reads HBM."""
     out = []
     stream = torch.cuda.current_stream()
     for K, N in ((7168, 18432), (18432, 7168)):
         copies = []
-        for c in range(2):
+        for c in range(copies_for(N * (K // 2 + K // 32))):
             wb = synth.device_normal_bf16((N, K), 0.01, "deepseek", "w", index=N + 17 * c)
             q = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
             s = torch.empty((N, K // 32), dtype=torch.uint8, device=dev)
@@ -443,7 +453,7 @@ def run_mxfp4(torch, L, synth, steps, warmup, dev, sp):
             wsp = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
 
             def call(i, tm=None):
-                q, sc = copies[i & 1]
+                q, sc = copies[i % len(copies)]
                 if tm:
                     tm.mark("a")
                 L.fp8_quant_act(x, xq, xs, scale_fmt=L.SCALE_UE8M0, stream=sp)
@@ -486,7 +496,7 @@ def run_block32(torch, L, synth, steps, warmup, dev, sp):
     for M, K, N in ((16, 4096, 4096), (2048, 4096, 4096), (8192, 4096, 28672)):
         wb = synth.device_normal_bf16((N, K), 0.02, "llama", "w", index=N + 32)
         copies = []
-        for c in range(2):
+        for c in range(copies_for(N * K)):
             wq = torch.empty((N, K), dtype=torch.uint8, device=dev)
             ws = torch.empty((N // 32, K // 32), dtype=torch.float32, device=dev)
             L.fp8_quant_weight(wb, wq, ws, block_n=32, block_k=32, stream=sp)
@@ -498,7 +508,7 @@ def run_block32(torch, L, synth, steps, warmup, dev, sp):
                           device=dev)
 
         def call(i):
-            wq, ws = copies[i & 1]
+            wq, ws = copies[i % len(copies)]
             L.fp8_linear(x, wq, ws, y, block_n=32, block_k=32, workspace=wsp, stream=sp)
         for i in range(warmup):
             call(i)

@@ -9,6 +9,10 @@ launches, each scaled by true bytes / counter reading of the plain copy
 kernel of N MiB that `bench.py --copy-calib-mib N` runs first; records the
 sha256 of the GEMM source so bench.py only uses it for the same kernel.
 `stats`: the kernel table of a --kernel-trace --stats run.
+`mfma`: MFMA busy share and counted FP8 flops of the large-M GEMM from a
+--pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_F8 run.
+`decode`: HBM bytes per decode-GEMM dispatch over its duration, from the
+FETCH_SIZE run (scaled by the same copy calibration).
 `summary`: the text form of one bench.py JSON line.
 """
 
@@ -76,6 +80,69 @@ def traffic(a):
     print("\n".join(lines))
 
 
+def dispatches(path):
+    """Dispatch_Id -> {name, grid, ns, counter values} from a counter CSV"""
+    out = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            d = out.setdefault(r["Dispatch_Id"], {
+                "name": r["Kernel_Name"], "grid": int(r["Grid_Size"]),
+                "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return out
+
+
+def mfma(a):
+    """MFMA busy share of SIMD cycles and counted FP8 flops of the large-M GEMM"""
+    simds = 256 * 4
+    rows = [d for d in dispatches(a.pmc).values() if GEMM_KERNEL in d["name"]]
+    if not rows:
+        sys.exit("no large-M GEMM dispatches found")
+    util = [d["SQ_VALU_MFMA_BUSY_CYCLES"] / (d["GRBM_GUI_ACTIVE"] * simds) for d in rows]
+    tf = [d["SQ_INSTS_VALU_MFMA_MOPS_F8"] * 512 / d["ns"] / 1e3 for d in rows]
+    lines = [
+        "# MFMA utilisation of the large-M block-scaled GEMM (fp32 scales), Llama-3-8B linears",
+        f"# command: {a.cmd}",
+        f"kernel: {GEMM_KERNEL}",
+        f"dispatches: {len(rows)}",
+        "MFMA busy / (GRBM_GUI_ACTIVE x 1024 SIMDs), mean over dispatches: "
+        f"{100 * sum(util) / len(util):.1f}% (min {100 * min(util):.1f}%, max {100 * max(util):.1f}%)",
+        "FP8 flops counted (SQ_INSTS_VALU_MFMA_MOPS_F8 x 512) / dispatch time, mean: "
+        f"{sum(tf) / len(tf):.0f} TFLOP/s (dense FP8 peak 5000)",
+    ]
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def decode(a):
+    """HBM bytes fetched per decode-kernel dispatch over its duration"""
+    ds = dispatches(a.fetch)
+    copy = [d for d in ds.values() if "copy" in d["name"]]
+    if not copy:
+        sys.exit("no copy kernel found")
+    sf = a.copy_mib * 1024.0 / max(d["FETCH_SIZE"] for d in copy)
+    groups = {}
+    for d in ds.values():
+        if "gemm_decode_kernel" not in d["name"]:
+            continue
+        mb = d["FETCH_SIZE"] * sf * 1024 / 1e6
+        key = (d["name"].split("(")[0].replace("void bsfp8::detail::", ""), d["grid"] // 1024,
+               round(mb))
+        groups.setdefault(key, []).append((mb, d["ns"]))
+    lines = ["# HBM reads of the decode GEMM (M <= 16) per dispatch, Llama-3-8B linears",
+             f"# command: {a.cmd}",
+             f"FETCH_SIZE scale (true / counter, {a.copy_mib} MiB copy): {sf:.4f}",
+             "# kernel | workgroups (N/16) | dispatches | MB fetched | us | GB/s"]
+    for (name, wg, _), v in sorted(groups.items(), key=lambda t: (t[0][1], t[0][2])):
+        mb = sum(x for x, _ in v) / len(v)
+        us = sum(t for _, t in v) / len(v) / 1e3
+        lines.append(f"{name} | {wg} | {len(v)} | {mb:.1f} | {us:.1f} | {mb * 1e3 / us:.0f}")
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def stats(a):
     rows = list(csv.DictReader(open(a.stats)))
     lines = [f"# rocprofv3 kernel statistics; command: {a.cmd}",
@@ -124,12 +191,22 @@ def main():
     s.add_argument("--cmd", required=True)
     s.add_argument("--out", required=True)
     s.add_argument("--top", type=int, default=12)
+    m = sub.add_parser("mfma")
+    m.add_argument("--pmc", required=True)
+    m.add_argument("--cmd", required=True)
+    m.add_argument("--out", required=True)
+    d = sub.add_parser("decode")
+    d.add_argument("--fetch", required=True)
+    d.add_argument("--copy-mib", type=int, required=True)
+    d.add_argument("--cmd", required=True)
+    d.add_argument("--out", required=True)
     b = sub.add_parser("summary")
     b.add_argument("--json", required=True)
     b.add_argument("--cmd", required=True)
     b.add_argument("--out", required=True)
     a = ap.parse_args()
-    {"traffic": traffic, "stats": stats, "summary": summary}[a.what](a)
+    {"traffic": traffic, "stats": stats, "summary": summary, "mfma": mfma,
+     "decode": decode}[a.what](a)
 
 
 if __name__ == "__main__":
