@@ -81,8 +81,8 @@ def read_traffic():
     kv = {}
     with open(TRAFFIC_FILE) as f:
         for line in f:
-            if ":" in line and not line.lstrip().startswith("#"):
-                k, v = line.split(":", 1)
+            if ": " in line and not line.lstrip().startswith("#"):
+                k, v = line.rsplit(": ", 1)     # keys may hold a colon themselves
                 kv[k.strip()] = v.strip()
     if kv.get("gemm_fp8.hip sha256[:16]") != source_hash():
         return None

@@ -94,19 +94,24 @@ def dispatches(path):
 
 def mfma(a):
     """MFMA busy share of SIMD cycles and counted FP8 flops of the large-M GEMM"""
-    simds = 256 * 4
+    simds, xcds = 256 * 4, 8
     rows = [d for d in dispatches(a.pmc).values() if GEMM_KERNEL in d["name"]]
     if not rows:
         sys.exit("no large-M GEMM dispatches found")
-    util = [d["SQ_VALU_MFMA_BUSY_CYCLES"] / (d["GRBM_GUI_ACTIVE"] * simds) for d in rows]
+    # the CSV sums GRBM_GUI_ACTIVE over the 8 XCDs: one XCD's count is the
+    # kernel's active cycles (dividing by the dispatch time gives the clock)
+    cyc = [d["GRBM_GUI_ACTIVE"] / xcds for d in rows]
+    util = [d["SQ_VALU_MFMA_BUSY_CYCLES"] / (c * simds) for d, c in zip(rows, cyc)]
+    ghz = [c / d["ns"] for d, c in zip(rows, cyc)]
     tf = [d["SQ_INSTS_VALU_MFMA_MOPS_F8"] * 512 / d["ns"] / 1e3 for d in rows]
     lines = [
         "# MFMA utilisation of the large-M block-scaled GEMM (fp32 scales), Llama-3-8B linears",
         f"# command: {a.cmd}",
         f"kernel: {GEMM_KERNEL}",
         f"dispatches: {len(rows)}",
-        "MFMA busy / (GRBM_GUI_ACTIVE x 1024 SIMDs), mean over dispatches: "
+        "MFMA busy / (GRBM_GUI_ACTIVE per XCD x 1024 SIMDs), mean over dispatches: "
         f"{100 * sum(util) / len(util):.1f}% (min {100 * min(util):.1f}%, max {100 * max(util):.1f}%)",
+        f"clock implied by GRBM_GUI_ACTIVE per XCD / dispatch time: {sum(ghz) / len(ghz):.2f} GHz",
         "FP8 flops counted (SQ_INSTS_VALU_MFMA_MOPS_F8 x 512) / dispatch time, mean: "
         f"{sum(tf) / len(tf):.0f} TFLOP/s (dense FP8 peak 5000)",
     ]
