@@ -25,7 +25,8 @@
 //   fp4_gemm_stream_kernel M <= 64: weight-streaming split-K, W dequantized
 //                          straight from global memory
 //   fp4_gemm_lds_kernel    larger M: 128 x 128 tiles, both operands
-//                          dequantized once per workgroup into fp16 LDS tiles
+//                          dequantized once per workgroup into fp16 LDS tiles,
+//                          eight waves (two per SIMD)
 //   fp4_splitk_reduce      fp32 partials -> bf16
 #include <type_traits>
 
@@ -249,19 +250,30 @@ __global__ __launch_bounds__(256) void fp4_splitk_reduce(const float* __restrict
   store4_bf16(y, N, m, n, v4f{s.x, s.y, s.z, s.w});
 }
 
-// Large-M kernel: 128 x 128 output tile, 4 waves of 64 x 64, K step 128.
-// Every K block: each thread loads half a row of codes + scales of X and of
-// W (global -> registers, one block ahead), dequantizes them to fp16 and
-// stores them to LDS; rows are 256 bytes (16 chunks of 8 halves) with chunk
-// c stored at c ^ (row & 15), so the 16 rows of a fragment read hit 16
-// different bank groups.
+// Large-M kernel: 128 x 128 output tile, WAVES_M x WAVES_N waves (wave tile
+// (128 / WAVES_M) x (128 / WAVES_N)), K step 128.  Every K block: each
+// thread loads a slice of one row of codes + scales of X and of W (global ->
+// registers, two blocks ahead), dequantizes them to fp16 and stores them to
+// LDS; rows are 256 bytes (16 chunks of 8 halves) with chunk c stored at
+// c ^ (row & 15), so the 16 rows of a fragment read hit 16 different bank
+// groups.  The fp16 tiles take 128 KB of LDS (one workgroup per CU); eight
+// waves put two on each SIMD, so one wave's dequantization, LDS traffic and
+// barrier wait overlap the other's MFMAs.
 constexpr int kLdsBM = 128, kLdsBN = 128;
 
-__global__ __launch_bounds__(256, 1) void fp4_gemm_lds_kernel(
+template <int WAVES_M, int WAVES_N>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void fp4_gemm_lds_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
     const float* __restrict__ xt, const uint8_t* __restrict__ wq,
     const uint8_t* __restrict__ ws, const float* __restrict__ wt, uint16_t* __restrict__ y,
     int64_t M, int64_t N, int64_t K) {
+  constexpr int THREADS = 64 * WAVES_M * WAVES_N;
+  constexpr int WM = kLdsBM / WAVES_M, WN = kLdsBN / WAVES_N;
+  constexpr int MI = WM / 16, NI = WN / 16;
+  constexpr int LPR = THREADS / 128;          // loader threads per row
+  constexpr int KPT = 128 / LPR;              // K elements per loader thread
+  constexpr int CPT = KPT / 8;                // 8-value chunks (code words) per thread
+  static_assert(LPR == 2 || LPR == 4 || LPR == 8, "loader layout");
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][(kLdsBM + kLdsBN) * 256];
   const int64_t MT = (M + kLdsBM - 1) / kLdsBM;
   const int64_t NT = (N + kLdsBN - 1) / kLdsBN;
@@ -281,108 +293,132 @@ __global__ __launch_bounds__(256, 1) void fp4_gemm_lds_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % WAVES_M, wn = wave / WAVES_M;
   const int64_t KB = (K + 127) / 128;
 
-  // loader role: row r (0..127), half h (0..1): K [64 h, 64 h + 64) of the block
-  const int lr = tid >> 1, lh = tid & 1;
+  // loader role: row r (0..127), slice h: K [KPT h, KPT h + KPT) of the block
+  const int lr = tid / LPR, lh = tid % LPR;
   const bool xrow_ok = m0 + lr < M, wrow_ok = n0 + lr < N;
-  uint4 xc[2], wc[2];
-  uint32_t xsc = 0, wsc = 0;
-  auto gload = [&](int64_t kb) {
-    const int64_t k0 = kb * 128 + 64 * lh;
-    const bool kok = k0 < K;
+  // two register sets of loaded codes (one 32-bit word per 8 values) and
+  // group-scale bytes (one per 16 values), for blocks kb and kb + 1
+  uint32_t xcs[2][CPT], wcs[2][CPT];
+  uint32_t xscs[2] = {0, 0}, wscs[2] = {0, 0};
+  auto gload = [&](int64_t kb, auto set_c) {
+    constexpr int st = decltype(set_c)::value;
+    uint32_t* xc = xcs[st];
+    uint32_t* wc = wcs[st];
+    uint32_t& xsc = xscs[st];
+    uint32_t& wsc = wscs[st];
+    const int64_t k0 = kb * 128 + KPT * lh;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      xc[i] = make_uint4(0, 0, 0, 0);
-      wc[i] = make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < CPT; ++i) xc[i] = wc[i] = 0;
     xsc = wsc = 0;
-    // K % 32 == 0: each 32-element quarter is wholly in or out of range
-    if (xrow_ok && kok) {
-      const uint8_t* p = xq + (m0 + lr) * (K / 2) + k0 / 2;
-      xc[0] = *(const uint4*)p;
-      if (k0 + 32 < K) xc[1] = *(const uint4*)(p + 16);
-      const uint8_t* s = xs + (m0 + lr) * (K / 16) + k0 / 16;
-      xsc = s[0] | (s[1] << 8);
-      if (k0 + 32 < K) xsc |= (s[2] << 16) | (s[3] << 24);
-    }
-    if (wrow_ok && kok) {
-      const uint8_t* p = wq + (n0 + lr) * (K / 2) + k0 / 2;
-      wc[0] = *(const uint4*)p;
-      if (k0 + 32 < K) wc[1] = *(const uint4*)(p + 16);
-      const uint8_t* s = ws + (n0 + lr) * (K / 16) + k0 / 16;
-      wsc = s[0] | (s[1] << 8);
-      if (k0 + 32 < K) wsc |= (s[2] << 16) | (s[3] << 24);
-    }
+    // K % 32 == 0: each 32-value quarter (and so each 16-value slice) is
+    // wholly in or out of range; a 64-value slice may end after its first
+    // quarter
+    if (kb >= KB || k0 >= K) return;
+    auto ld = [&](const uint8_t* q, const uint8_t* gs, int64_t row, uint32_t* c, uint32_t& sc) {
+      const uint8_t* p = q + row * (K / 2) + k0 / 2;
+      const uint8_t* sp = gs + row * (K / 16) + k0 / 16;
+      if constexpr (CPT >= 4) {
+#pragma unroll
+        for (int i = 0; i < CPT / 4; ++i) {
+          if (k0 + 32 * i >= K) break;
+          const uint4 v = *(const uint4*)(p + 16 * i);
+          c[4 * i] = v.x; c[4 * i + 1] = v.y; c[4 * i + 2] = v.z; c[4 * i + 3] = v.w;
+          sc |= (uint32_t)(sp[2 * i] | (sp[2 * i + 1] << 8)) << (16 * i);
+        }
+      } else {
+        const uint2 v = *(const uint2*)p;
+        c[0] = v.x; c[1] = v.y;
+        sc = sp[0];
+      }
+    };
+    if (xrow_ok) ld(xq, xs, m0 + lr, xc, xsc);
+    if (wrow_ok) ld(wq, ws, n0 + lr, wc, wsc);
   };
-  // dequantize this thread's 64 elements of each operand into LDS buffer b
-  auto dstore = [&](int b) {
+  // dequantize this thread's KPT elements of each operand into LDS buffer b
+  auto dstore = [&](int b, auto set_c) {
+    constexpr int st = decltype(set_c)::value;
+    const uint32_t* xc = xcs[st];
+    const uint32_t* wc = wcs[st];
+    const uint32_t xsc = xscs[st], wsc = wscs[st];
     uint8_t* sx = lds[b];
     uint8_t* sw = lds[b] + kLdsBM * 256;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {          // chunk c: 8 values, group c / 2
-      const uint32_t xw = c < 4 ? (&xc[0].x)[c] : (&xc[1].x)[c - 4];
-      const uint32_t ww = c < 4 ? (&wc[0].x)[c] : (&wc[1].x)[c - 4];
+    for (int c = 0; c < CPT; ++c) {        // chunk c: 8 values, group c / 2
+      const uint32_t xw = xc[c];
+      const uint32_t ww = wc[c];
       const half8 hx = dequant8(xw, e4m3_to_f16((xsc >> (8 * (c >> 1))) & 0xffu));
       const half8 hw = dequant8(ww, e4m3_to_f16((wsc >> (8 * (c >> 1))) & 0xffu));
-      const int chunk = lh * 8 + c;
+      const int chunk = lh * CPT + c;
       const int phys = chunk ^ (lr & 15);
       *(half8*)(sx + lr * 256 + phys * 16) = hx;
       *(half8*)(sw + lr * 256 + phys * 16) = hw;
     }
   };
 
-  v4f acc[4][4];
+  v4f acc[NI][MI];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < MI; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  gload(0);
-  dstore(0);
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  gload(0, S0{});
+  gload(1, S1{});
+  dstore(0, S0{});
   __syncthreads();
-  for (int64_t kb = 0; kb < KB; ++kb) {
-    const int b = (int)(kb & 1);
-    if (kb + 1 < KB) gload(kb + 1);
+  // block kb: LDS buffer kb & 1 holds it, register set kb & 1 refills with
+  // block kb + 2, register set (kb + 1) & 1 holds block kb + 1 for the store
+  auto iter = [&](int64_t kb, auto b_c) {
+    constexpr int b = decltype(b_c)::value;
+    gload(kb + 2, b_c);
     const uint8_t* sx = lds[b];
     const uint8_t* sw = lds[b] + kLdsBM * 256;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {        // MFMA K step: chunks 4 ks + g4
-      half8 bx[4], aw[4];
+      half8 bx[MI], aw[NI];
       const int chunk = 4 * ks + g4;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = wm * 64 + j * 16 + l16;
+      for (int j = 0; j < MI; ++j) {
+        const int r = wm * WM + j * 16 + l16;
         bx[j] = *(const half8*)(sx + r * 256 + ((chunk ^ (r & 15)) * 16));
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = wn * 64 + i * 16 + l16;
+      for (int i = 0; i < NI; ++i) {
+        const int r = wn * WN + i * 16 + l16;
         aw[i] = *(const half8*)(sw + r * 256 + ((chunk ^ (r & 15)) * 16));
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < NI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < MI; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw[i], bx[j], acc[i][j], 0, 0, 0);
     }
-    if (kb + 1 < KB) dstore(b ^ 1);
+    if (kb + 1 < KB) dstore(b ^ 1, std::integral_constant<int, b ^ 1>{});
     __syncthreads();
+  };
+  for (int64_t kb = 0; kb < KB; kb += 2) {
+    iter(kb, S0{});
+    if (kb + 1 < KB) iter(kb + 1, S1{});
   }
 
   const float gg = (*xt) * (*wt);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t n = n0 + wn * 64 + i * 16 + 4 * g4;
+  for (int i = 0; i < NI; ++i) {
+    const int64_t n = n0 + wn * WN + i * 16 + 4 * g4;
     if (n >= N) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t m = m0 + wm * 64 + j * 16 + l16;
+    for (int j = 0; j < MI; ++j) {
+      const int64_t m = m0 + wm * WM + j * 16 + l16;
       if (m < M) store4_bf16(y, N, m, n, acc[i][j] * gg);
     }
   }
 }
+
+constexpr int kFp4WavesN = 4;   // 2 x 4 waves of 64 x 32 (two per SIMD)
 
 constexpr int64_t kStreamMaxM = 64;
 
@@ -445,8 +481,8 @@ hipError_t launch_fp4_gemm(const uint8_t* xq, const uint8_t* xs, const float* xt
   if (M > kStreamMaxM) {
     int64_t tiles = ((M + kLdsBM - 1) / kLdsBM) * ((N + kLdsBN - 1) / kLdsBN);
     tiles = (tiles + 7) / 8 * 8;
-    hipLaunchKernelGGL(fp4_gemm_lds_kernel, dim3((unsigned)tiles), dim3(256), 0, s, xq, xs, xt,
-                       wq, wsc, wt, y, M, N, K);
+    hipLaunchKernelGGL((fp4_gemm_lds_kernel<2, kFp4WavesN>), dim3((unsigned)tiles),
+                       dim3(64 * 2 * kFp4WavesN), 0, s, xq, xs, xt, wq, wsc, wt, y, M, N, K);
     return hipGetLastError();
   }
   int kbps, real;

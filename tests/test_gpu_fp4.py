@@ -78,6 +78,7 @@ def _gemm_dev(h, M, N):
 @pytest.mark.parametrize("M,N,K", [
     (1, 256, 256), (5, 264, 288), (16, 1000, 1024), (33, 512, 640), (64, 256, 2048),
     (65, 256, 256), (130, 520, 640), (300, 1000, 1056), (256, 256, 128),
+    (200, 264, 2144), (129, 136, 96),     # K blocks ending after 96 of 128 values
 ])
 def test_fp4_gemm_parity(M, N, K):
     say(f"fp4 gemm M={M} N={N} K={K}")
