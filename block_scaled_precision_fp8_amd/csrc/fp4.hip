@@ -183,6 +183,7 @@ __device__ __forceinline__ half8 frag_step(const Frag128& f, int t) {
 }
 
 constexpr int kStreamWaves = 4;
+template <int MT> constexpr int kStreamBlocks = MT == 4 ? 2 : 4;
 
 template <int MT>
 __global__ __launch_bounds__(64 * kStreamWaves) void fp4_gemm_stream_kernel(
@@ -201,25 +202,30 @@ __global__ __launch_bounds__(64 * kStreamWaves) void fp4_gemm_stream_kernel(
   v4f acc[MT];
 #pragma unroll
   for (int j = 0; j < MT; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
-  constexpr int U = 2;
+  // K blocks per round of loads: each wave walks its split in rounds whose
+  // latency is exposed, so fewer, wider rounds where registers allow
+  constexpr int U = kStreamBlocks<MT>;
   for (int64_t kb = kb0; kb < kb1; kb += U) {
-    Frag128 fw[U];
+    // the weight fragments (HBM) and the activation fragments (L2) of U
+    // blocks, all issued before any is used so their latencies overlap
+    Frag128 fw[U], fx[U][MT];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < U; ++u) {
       fw[u] = load_frag128(wq, ws, n0 + l16, K, kb + u, g4, nvalid && kb + u < kb1);
+#pragma unroll
+      for (int j = 0; j < MT; ++j)
+        fx[u][j] = load_frag128(xq, xs, j * 16 + l16, K, kb + u, g4,
+                                j * 16 + l16 < M && kb + u < kb1);
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (kb + u >= kb1) break;
-      Frag128 fx[MT];
-#pragma unroll
-      for (int j = 0; j < MT; ++j)
-        fx[j] = load_frag128(xq, xs, j * 16 + l16, K, kb + u, g4, j * 16 + l16 < M);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const half8 a = frag_step(fw[u], t);
 #pragma unroll
         for (int j = 0; j < MT; ++j)
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, frag_step(fx[j], t), acc[j], 0, 0, 0);
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, frag_step(fx[u][j], t), acc[j], 0, 0, 0);
       }
     }
   }
