@@ -234,7 +234,8 @@ BSFP8_API int32_t fp8_grouped_gemm(const void* xq, const void* x_scale, const vo
  *                w_scale_inv [E][2I/128][ceil(K/128)] (fp32 | UE8M0).
  *   seg_offsets  DEVICE int32 [E+1], the same precondition as
  *                fp8_grouped_gemm.
- *   hq           out, E4M3 [T][I];  h_scale out, [T][I/128] fp32 | UE8M0.
+ *   hq           out, E4M3 [T][I] (16-byte aligned);  h_scale out,
+ *                [T][I/128] fp32 | UE8M0.
  *   h_bf16       out, bf16 [T][I] (the rounded h), or NULL.
  *   I            intermediate size, a positive multiple of 128.
  * No workspace.  Errors: those of fp8_grouped_gemm with N = 2I; EINVAL for
@@ -365,7 +366,9 @@ BSFP8_API size_t bsfp8_workspace_size(int32_t op, int64_t M, int64_t N, int64_t 
 
 /*
  * Which kernel (a bsfp8_gemm_kind) fp8_block_gemm and fp8_linear launch for
- * an M x N x K problem, and into how many K splits it cuts K (*splits, may
+ * an M x N x K problem with 128 x 128 blocks (fp8_fp4_gemm follows the same
+ * choice; (32, 32) blocks run their own kernel, the decode kernel up to
+ * M = 16), and into how many K splits it cuts K (*splits, may
  * be NULL; 1 when K is not split: splits above 1 write fp32 partial sums to
  * the workspace and add one reduction launch).  The grouped GEMM does not
  * split K: experts with more than 128 rows run on 256 x 256 tiles and the

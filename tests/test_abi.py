@@ -224,3 +224,28 @@ def test_mxfp4_argument_checks():
     assert L.workspace_size(L.OP_FP8_FP4_GEMM, 16, 28672, 4096) == 0
     a = list(args); a[6:9] = [128, 4096, 4096]; a[10] = FAKE; a[11] = need - 1
     assert g(*a) == L.ENOSPC
+
+
+def test_silu_mul_quant_argument_checks():
+    f = L.load().fp8_grouped_gemm_silu_mul_quant
+    #       xq    xs    wq    ws    seg   E  hq    hs    hb    T   I    K    fmt stream
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, FAKE, None, 64, 256, 256, 0, None]
+    for i, v, code in [(10, 0, L.EINVAL), (10, 192, L.EINVAL), (10, -128, L.EINVAL),
+                       (5, 0, L.EINVAL), (5, 1025, L.EINVAL), (7, None, L.EINVAL),
+                       (7, 0x100002, L.EINVAL), (8, MIS, L.EINVAL), (4, None, L.EINVAL),
+                       (6, None, L.EINVAL), (6, MIS, L.EINVAL), (11, 200, L.EINVAL),
+                       (12, 2, L.EINVAL), (11, 2**22 + 16, L.ENOTSUP), (9, 0, L.OK)]:
+        a = list(args); a[i] = v
+        assert f(*a) == code, (i, v)
+
+
+def test_block32_argument_checks():
+    lib = L.load()
+    # (32, 32) is accepted by the quantizers and the GEMM; mixed sizes are not
+    assert _qw(bn=32, bk=128) == L.ENOTSUP and _qw(bn=64, bk=64) == L.ENOTSUP
+    assert _qa(gk=32, sch=1) == L.ENOTSUP          # static scheme: 128 only
+    assert _gemm(bn=32, bk=32, M=0) == L.OK and _gemm(bn=32, bk=64) == L.ENOTSUP
+    g = lib.fp8_grouped_gemm
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, 64, 256, 256, 32, 32, 0, None, 0, None]
+    assert g(*args) == L.ENOTSUP                   # experts: 128 x 128 blocks only
+    assert L.workspace_size(L.OP_LINEAR_B32, 64, 256, 256) >= 64 * 256 + 64 * 8 * 4
