@@ -13,6 +13,10 @@ sha256 of the GEMM source so bench.py only uses it for the same kernel.
 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_F8 run.
 `decode`: HBM bytes per decode-GEMM dispatch over its duration, from the
 FETCH_SIZE run (scaled by the same copy calibration).
+`l1`: what bounds the operand loads of the large-M GEMM, from two --pmc
+runs: texture-data stalls on L1, L1 pending and tag-conflict stalls, address
+stalls, and the L1-to-L2 request count and average latency, with the
+concurrency they imply (Little's law).
 `summary`: the text form of one bench.py JSON line.
 """
 
@@ -148,6 +152,50 @@ def decode(a):
     print("\n".join(lines))
 
 
+def l1(a):
+    """L1-miss concurrency bound of the large-M GEMM's LDS-DMA operand loads"""
+    cus = 256
+    rows = {}
+    for path in (a.pmc1, a.pmc2):
+        for k, d in dispatches(path).items():
+            if GEMM_KERNEL in d["name"]:
+                rows.setdefault(path, []).append(d)
+    r1, r2 = rows.get(a.pmc1), rows.get(a.pmc2)
+    if not r1 or not r2:
+        sys.exit("no large-M GEMM dispatches found")
+
+    def mean_per_cu_cycle(rs, key):
+        return sum(d[key] / (d["GRBM_GUI_ACTIVE"] / 8 * cus) for d in rs) / len(rs)
+
+    req = sum(d["TCP_TCC_READ_REQ_sum"] for d in r2)
+    lat = sum(d["TCP_TCC_READ_REQ_LATENCY_sum"] for d in r2) / req
+    waves = sum(d["TA_BUFFER_READ_LDS_WAVEFRONTS_sum"] for d in r2)
+    cyc = sum(d["GRBM_GUI_ACTIVE"] / 8 for d in r2)
+    # bytes the DMA moves: 64 lanes x 16 bytes per LDS-load wavefront
+    bpc = waves * 1024.0 / (cyc * cus)
+    lines = [
+        "# What bounds the operand loads of the large-M block-scaled GEMM (fp32 scales), Llama-3-8B linears",
+        f"# commands: {a.cmd}",
+        f"kernel: {GEMM_KERNEL}",
+        f"dispatches: {len(r1)} (stall pass), {len(r2)} (request pass)",
+        "fractions of CU cycles (counter sum / (GRBM_GUI_ACTIVE per XCD x 256 CUs)):",
+        f"  TD busy {mean_per_cu_cycle(r2, 'TD_TD_BUSY_sum'):.3f}, of which stalled on L1 data "
+        f"(TD_TC_STALL) {mean_per_cu_cycle(r1, 'TD_TC_STALL_sum'):.3f}",
+        f"  L1 pending stall {mean_per_cu_cycle(r1, 'TCP_PENDING_STALL_CYCLES_sum'):.3f}, "
+        f"L1 read tag-conflict stall {mean_per_cu_cycle(r1, 'TCP_READ_TAGCONFLICT_STALL_CYCLES_sum'):.3f}",
+        f"  TA address stalled by L1 {mean_per_cu_cycle(r1, 'TA_ADDR_STALLED_BY_TC_CYCLES_sum'):.3f}",
+        f"LDS-DMA wavefronts: {waves:.0f}; L1-to-L2 read requests per wavefront: {req / waves:.1f}",
+        f"average L1-to-L2 read latency: {lat:.0f} cycles",
+        f"operand bytes through L1 per CU cycle: {bpc:.1f}",
+        f"implied L2 requests in flight per CU (Little's law, 64-byte requests): {bpc * lat / 64:.0f}",
+        f"bytes per CU cycle the 256x256 tile needs at the full FP8 MFMA rate "
+        f"(4 SIMDs x 2048 flop/cycle / 256 flop/byte): 32.0",
+    ]
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def stats(a):
     rows = list(csv.DictReader(open(a.stats)))
     lines = [f"# rocprofv3 kernel statistics; command: {a.cmd}",
@@ -205,13 +253,18 @@ def main():
     d.add_argument("--copy-mib", type=int, required=True)
     d.add_argument("--cmd", required=True)
     d.add_argument("--out", required=True)
+    l = sub.add_parser("l1")
+    l.add_argument("--pmc1", required=True)
+    l.add_argument("--pmc2", required=True)
+    l.add_argument("--cmd", required=True)
+    l.add_argument("--out", required=True)
     b = sub.add_parser("summary")
     b.add_argument("--json", required=True)
     b.add_argument("--cmd", required=True)
     b.add_argument("--out", required=True)
     a = ap.parse_args()
     {"traffic": traffic, "stats": stats, "summary": summary, "mfma": mfma,
-     "decode": decode}[a.what](a)
+     "decode": decode, "l1": l1}[a.what](a)
 
 
 if __name__ == "__main__":
