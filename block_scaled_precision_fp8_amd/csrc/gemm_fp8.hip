@@ -235,6 +235,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ v8i read_frag(const uint8_t* __restrict__ row, int ch0, int ch1) {
   return join(*(const uint4*)(row + ch0), *(const uint4*)(row + ch1));
 }
+// a staged scale, read the same way (no wait for the in-flight DMA)
+__device__ __forceinline__ float read_scale(const float* __restrict__ p, int idx) { return p[idx]; }
 
 // SiLU(gate) * up with the 1 x 128 requantization, for a gate/up tile of
 // the grouped GEMM (the step between an MoE expert's gate/up and down
@@ -386,8 +388,17 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
   constexpr int XBYTES = BM * kRowBytes;
   constexpr int STAGE = BM * kRowBytes + BN * kWRow;
   constexpr int SB = FMT == 0 ? 4 : 1;      // bytes per scale
-  constexpr int LOADS = XJ + WJ + MI + 1;   // vector-memory ops per stage per lane
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES * STAGE];
+  // fp32 activation scales of tiles of at least 128 rows are staged through
+  // LDS, SCH K blocks per chunk: one row's chunk is one 32-byte request,
+  // where loading each row's scale block by block costs a request per row
+  // and K block (the rows of one K block are a row stride apart).
+  constexpr bool SCL = FMT == 0 && BM >= 128;
+  constexpr int SCH = 8;
+  constexpr int SBUF = BM * SCH * 4;        // bytes per chunk buffer
+  constexpr int SJ = SCL ? BM * SCH / (64 * WAVES) : 0;   // chunk DMA loads per lane
+  static_assert(!SCL || SJ * 64 * WAVES == BM * SCH, "scale chunk / thread mismatch");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES * STAGE + (SCL ? 2 * SBUF : 0)];
+  uint8_t* const sbuf = lds + STAGES * STAGE;
   static_assert(!GROUPED || STAGES * STAGE >= 1025 * 4, "tile table fits the stage buffers");
   static_assert(!SWIGLU || WAVES_M * (WAVES_N / 2) * MI * NI * 1024 +
                                (WAVES_N > 2 ? WAVES_M * (WAVES_N / 2) * MI * 64 : 0) <=
@@ -487,11 +498,29 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
           W4 ? dma_src4(q, nrows, kb) : SWIGLU ? dma_src_gu(q, kbyte) : dma_src(q, nrows, kbyte),
           0, 0, 0);
     }
+    if constexpr (SCL) {
+      // at the first K block of a chunk: rows x SCH scales into its buffer,
+      // row-major (lane q: row q / SCH, block kb + q % SCH; blocks past the
+      // end load other rows' scales or zeros and are never read)
+      const int rel = kb - kb_begin;
+      if (rel % SCH == 0) {
+        uint8_t* dst = sbuf + ((rel / SCH) & 1) * SBUF;
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      const uint32_t off = saoff[i] == kOOB ? kOOB : saoff[i] + kb * SB;
-      if (FMT == 0) sa_reg[buf][i] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsa, off, 0, 0));
-      else sa_reg[buf][i] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b8(rsa, off, 0, 0));
+        for (int j = 0; j < SJ; ++j) {
+          const int q = (j * WAVES + wave) * 64 + lane;
+          const int row = q / SCH;
+          const uint32_t off = row < mrows ? (uint32_t)((row * KB + kb + q % SCH) * 4) : kOOB;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, BSFP8_LDS(dst + (j * WAVES + wave) * 256), 4,
+                                                   off, 0, 0, 0);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const uint32_t off = saoff[i] == kOOB ? kOOB : saoff[i] + kb * SB;
+        if (FMT == 0) sa_reg[buf][i] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsa, off, 0, 0));
+        else sa_reg[buf][i] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b8(rsa, off, 0, 0));
+      }
     }
     if constexpr (W4) {
 #pragma unroll
@@ -536,6 +565,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
   // (they may interleave freely with the MFMAs), run the MFMAs.
   auto step = [&](auto buf_c, int kb_next) {
     constexpr int buf = decltype(buf_c)::value;
+    const int kb_cur = kb_next - 1;
     const uint8_t* sx = lds + buf * STAGE + (wm * WM + l16) * kRowBytes;
     const uint8_t* swl = lds + buf * STAGE + XBYTES + (wn * WN + l16) * kWRow;
     issue(kb_next, buf ^ 1);
@@ -547,10 +577,18 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
 #pragma unroll
       for (int ii = 0; ii < NI; ++ii) sw4[ii] = sw4_reg[buf][ii] & 0xff;
     }
+    if constexpr (SCL) {
+      // this block's scales of the lane's token rows, from the chunk buffer
+      const int rel = kb_cur - kb_begin;
+      const float* sc = (const float*)(sbuf + ((rel / SCH) & 1) * SBUF) + rel % SCH;
 #pragma unroll
-    for (int j = 0; j < MI; ++j) {
-      sa[j] = sa_reg[buf][j];
-      if (FMT == 1) sa[j] = __int_as_float(__float_as_int(sa[j]) & 0xff);
+      for (int j = 0; j < MI; ++j) sa[j] = read_scale(sc, (wm * WM + j * 16 + l16) * SCH);
+    } else {
+#pragma unroll
+      for (int j = 0; j < MI; ++j) {
+        sa[j] = sa_reg[buf][j];
+        if (FMT == 1) sa[j] = __int_as_float(__float_as_int(sa[j]) & 0xff);
+      }
     }
     v8i bx[MI];
 #pragma unroll
