@@ -173,6 +173,7 @@ def l1(a):
     cyc = sum(d["GRBM_GUI_ACTIVE"] / 8 for d in r2)
     # bytes the DMA moves: 64 lanes x 16 bytes per LDS-load wavefront
     bpc = waves * 1024.0 / (cyc * cus)
+    rpc = req / (cyc * cus)                      # L1-to-L2 read requests per CU cycle
     lines = [
         "# What bounds the operand loads of the large-M block-scaled GEMM (fp32 scales), Llama-3-8B linears",
         f"# commands: {a.cmd}",
@@ -186,8 +187,10 @@ def l1(a):
         f"  TA address stalled by L1 {mean_per_cu_cycle(r1, 'TA_ADDR_STALLED_BY_TC_CYCLES_sum'):.3f}",
         f"LDS-DMA wavefronts: {waves:.0f}; L1-to-L2 read requests per wavefront: {req / waves:.1f}",
         f"average L1-to-L2 read latency: {lat:.0f} cycles",
-        f"operand bytes through L1 per CU cycle: {bpc:.1f}",
-        f"implied L2 requests in flight per CU (Little's law, 64-byte requests): {bpc * lat / 64:.0f}",
+        f"operand bytes through L1 per CU cycle: {bpc:.1f} (DMA bytes per L2 request: "
+        f"{waves * 1024.0 / req:.0f})",
+        f"L2 read requests in flight per CU (Little's law: requests per CU cycle x latency): "
+        f"{rpc * lat:.0f}",
         f"bytes per CU cycle the 256x256 tile needs at the full FP8 MFMA rate "
         f"(4 SIMDs x 2048 flop/cycle / 256 flop/byte): 32.0",
     ]
