@@ -237,6 +237,7 @@ __device__ __forceinline__ v8i read_frag(const uint8_t* __restrict__ row, int ch
 }
 // a staged scale, read the same way (no wait for the in-flight DMA)
 __device__ __forceinline__ float read_scale(const float* __restrict__ p, int idx) { return p[idx]; }
+__device__ __forceinline__ uint32_t read_byte(const uint8_t* __restrict__ p, int idx) { return p[idx]; }
 
 // SiLU(gate) * up with the 1 x 128 requantization, for a gate/up tile of
 // the grouped GEMM (the step between an MoE expert's gate/up and down
@@ -363,7 +364,7 @@ __device__ __forceinline__ void swiglu_epilogue(v4f (&acc)[WN / 16][WM / 16], ui
 // with the X chunks g4 and g4 + 4 of the FP8 operand (the lane layout of
 // the FP4 x FP8 form, checked on the GPU), and passes its own group's scale.
 template <int FMT, int WAVES_M, int WAVES_N, int WM, int WN, bool GROUPED, bool W4 = false,
-          bool SWIGLU = false>
+          bool SWIGLU = false, bool SA = false>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
     const uint8_t* __restrict__ xq, const void* __restrict__ xs, const uint8_t* __restrict__ wq,
     const void* __restrict__ wsc, const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
@@ -388,15 +389,23 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
   constexpr int XBYTES = BM * kRowBytes;
   constexpr int STAGE = BM * kRowBytes + BN * kWRow;
   constexpr int SB = FMT == 0 ? 4 : 1;      // bytes per scale
-  // fp32 activation scales of tiles of at least 128 rows are staged through
-  // LDS, SCH K blocks per chunk: one row's chunk is one 32-byte request,
-  // where loading each row's scale block by block costs a request per row
-  // and K block (the rows of one K block are a row stride apart).
-  constexpr bool SCL = FMT == 0 && BM >= 128;
-  constexpr int SCH = 8;
-  constexpr int SBUF = BM * SCH * 4;        // bytes per chunk buffer
-  constexpr int SJ = SCL ? BM * SCH / (64 * WAVES) : 0;   // chunk DMA loads per lane
-  static_assert(!SCL || SJ * 64 * WAVES == BM * SCH, "scale chunk / thread mismatch");
+  // The activation scales of tiles of at least 128 rows are staged through
+  // LDS, SCH K blocks per chunk (8 fp32 or 16 UE8M0 scales, SROW bytes): one
+  // row's chunk is one request, where loading each row's scale block by
+  // block costs a request per row and K block (the rows of one K block are
+  // a row stride apart).  UE8M0 rows are K/128 bytes apart: their chunks
+  // are dword-aligned only when K/128 and the split length are multiples of
+  // 4, so the launcher picks the staged instantiation (SA) then and the
+  // per-block loads otherwise.  (A runtime choice between the two would
+  // make the compiler wait for every load of the step before using the
+  // per-block scales, the next stage's DMA included.)
+  constexpr bool SCL = BM >= 128 && (FMT == 0 || (SA && !SWIGLU));
+  constexpr int SCH = FMT == 0 ? 8 : 16;
+  constexpr int SROW = SCH * SB;            // bytes per row per chunk
+  constexpr int SDW = SROW / 4;             // dword loads per row per chunk
+  constexpr int SBUF = BM * SROW;           // bytes per chunk buffer
+  constexpr int SJ = SCL ? BM * SDW / (64 * WAVES) : 0;   // chunk DMA loads per lane
+  static_assert(!SCL || SJ * 64 * WAVES == BM * SDW, "scale chunk / thread mismatch");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES * STAGE + (SCL ? 2 * SBUF : 0)];
   uint8_t* const sbuf = lds + STAGES * STAGE;
   static_assert(!GROUPED || STAGES * STAGE >= 1025 * 4, "tile table fits the stage buffers");
@@ -500,16 +509,18 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
     }
     if constexpr (SCL) {
       // at the first K block of a chunk: rows x SCH scales into its buffer,
-      // row-major (lane q: row q / SCH, block kb + q % SCH; blocks past the
-      // end load other rows' scales or zeros and are never read)
+      // row-major (lane q: row q / SDW, dword q % SDW of the row's chunk;
+      // blocks past the end load other rows' scales or zeros and are never
+      // read)
       const int rel = kb - kb_begin;
       if (rel % SCH == 0) {
         uint8_t* dst = sbuf + ((rel / SCH) & 1) * SBUF;
 #pragma unroll
         for (int j = 0; j < SJ; ++j) {
           const int q = (j * WAVES + wave) * 64 + lane;
-          const int row = q / SCH;
-          const uint32_t off = row < mrows ? (uint32_t)((row * KB + kb + q % SCH) * 4) : kOOB;
+          const int row = q / SDW;
+          const uint32_t off =
+              row < mrows ? (uint32_t)((row * KB + kb) * SB + (q % SDW) * 4) : kOOB;
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, BSFP8_LDS(dst + (j * WAVES + wave) * 256), 4,
                                                    off, 0, 0, 0);
         }
@@ -580,9 +591,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
     if constexpr (SCL) {
       // this block's scales of the lane's token rows, from the chunk buffer
       const int rel = kb_cur - kb_begin;
-      const float* sc = (const float*)(sbuf + ((rel / SCH) & 1) * SBUF) + rel % SCH;
+      const uint8_t* sc = sbuf + ((rel / SCH) & 1) * SBUF + (rel % SCH) * SB;
 #pragma unroll
-      for (int j = 0; j < MI; ++j) sa[j] = read_scale(sc, (wm * WM + j * 16 + l16) * SCH);
+      for (int j = 0; j < MI; ++j) {
+        const int o = (wm * WM + j * 16 + l16) * SROW;
+        sa[j] = FMT == 0 ? read_scale((const float*)sc, o / 4)
+                         : __int_as_float((int)read_byte(sc, o));
+      }
     } else {
 #pragma unroll
       for (int j = 0; j < MI; ++j) {
@@ -1050,23 +1065,32 @@ template __global__ void gemm_b32_kernel<1>(const uint8_t* __restrict__, const v
 // Explicit instantiations of every tile configuration the dispatcher below
 // can launch (the host pass does not always emit launch stubs for kernel
 // templates that are only instantiated implicitly).
-#define BSFP8_INST(FMT, WMN, WNN, WM, WN, G, W4, SW)                                          \
-  template __global__ void gemm_lds_kernel<FMT, WMN, WNN, WM, WN, G, W4, SW>(                \
+#define BSFP8_INST(FMT, WMN, WNN, WM, WN, G, W4, SW, SA)                                      \
+  template __global__ void gemm_lds_kernel<FMT, WMN, WNN, WM, WN, G, W4, SW, SA>(            \
       const uint8_t* __restrict__, const void* __restrict__, const uint8_t* __restrict__,     \
       const void* __restrict__, const uint16_t* __restrict__, uint16_t* __restrict__, int64_t, \
       int64_t, int64_t, const int32_t* __restrict__, int, int, float* __restrict__, int,      \
       uint8_t* __restrict__, void* __restrict__);
-#define BSFP8_INST_ALL(FMT)                          \
-  BSFP8_INST(FMT, 4, 2, 64, 128, false, false, false) \
-  BSFP8_INST(FMT, 2, 4, 64, 64, false, false, false)  \
-  BSFP8_INST(FMT, 2, 4, 64, 64, false, true, false)   \
-  BSFP8_INST(FMT, 4, 2, 64, 128, false, true, false)  \
-  BSFP8_INST(FMT, 1, 4, 64, 64, true, false, false)   \
-  BSFP8_INST(FMT, 4, 2, 64, 128, true, false, false)  \
-  BSFP8_INST(FMT, 1, 4, 64, 64, true, false, true)    \
-  BSFP8_INST(FMT, 4, 2, 64, 128, true, false, true)
+#define BSFP8_INST_ALL(FMT)                                 \
+  BSFP8_INST(FMT, 4, 2, 64, 128, false, false, false, false) \
+  BSFP8_INST(FMT, 2, 4, 64, 64, false, false, false, false)  \
+  BSFP8_INST(FMT, 2, 4, 64, 64, false, true, false, false)   \
+  BSFP8_INST(FMT, 4, 2, 64, 128, false, true, false, false)  \
+  BSFP8_INST(FMT, 1, 4, 64, 64, true, false, false, false)   \
+  BSFP8_INST(FMT, 4, 2, 64, 128, true, false, false, false)  \
+  BSFP8_INST(FMT, 1, 4, 64, 64, true, false, true, false)    \
+  BSFP8_INST(FMT, 4, 2, 64, 128, true, false, true, false)
+// UE8M0 tiles with staged (dword-aligned) activation scales
+#define BSFP8_INST_UE8M0_STAGED                          \
+  BSFP8_INST(1, 4, 2, 64, 128, false, false, false, true) \
+  BSFP8_INST(1, 2, 4, 64, 64, false, false, false, true)  \
+  BSFP8_INST(1, 2, 4, 64, 64, false, true, false, true)   \
+  BSFP8_INST(1, 4, 2, 64, 128, false, true, false, true)  \
+  BSFP8_INST(1, 4, 2, 64, 128, true, false, false, true)
 BSFP8_INST_ALL(0)
 BSFP8_INST_ALL(1)
+BSFP8_INST_UE8M0_STAGED
+#undef BSFP8_INST_UE8M0_STAGED
 #undef BSFP8_INST_ALL
 #undef BSFP8_INST
 
@@ -1088,7 +1112,7 @@ constexpr int64_t kDecodeFusedMaxN = 8192;
 // Two stages wait for vmcnt(0) before each K block, which does not depend
 // on the completion order of the LDS-DMA loads and the scale loads.
 template <int FMT, int WMN, int WNN, int WM, int WN, bool GROUPED, bool W4 = false,
-          bool SW = false>
+          bool SW = false, bool SA = false>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t st, int splits, int kbps, int gsel = 0) {
   constexpr int BM = WMN * WM, BN = WNN * WN;
   const int64_t NT = (a.N + BN - 1) / BN;
@@ -1105,7 +1129,7 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t st, int splits, int kbps, i
     tiles = (tiles + 7) / 8 * 8;                 // whole rounds over the 8 XCDs
   }
   float* part = splits > 1 ? (float*)a.workspace : nullptr;
-  hipLaunchKernelGGL((gemm_lds_kernel<FMT, WMN, WNN, WM, WN, GROUPED, W4, SW>),
+  hipLaunchKernelGGL((gemm_lds_kernel<FMT, WMN, WNN, WM, WN, GROUPED, W4, SW, SA>),
                      dim3((unsigned)tiles), dim3(64 * WMN * WNN), 0, st, a.xq, a.xs, a.wq, a.ws,
                      GROUPED ? nullptr : a.bias, a.y, a.M, a.N, a.K, a.seg, a.E, gsel, part,
                      kbps, a.hq, a.hs);
@@ -1156,8 +1180,16 @@ Plan plan_dense(int64_t M, int64_t N, int64_t K, bool allow_big = true) {
   return best;
 }
 
+// UE8M0 activation scales can be staged in dword chunks: every row and every
+// K split starts on a multiple of 4 scale bytes
+inline bool ue8m0_aligned(const GemmArgs& a, int splits, int kbps) {
+  const int64_t KB = (a.K + 127) / 128;
+  return a.fmt == 1 && KB % 4 == 0 && (splits == 1 || kbps % 4 == 0);
+}
+
 template <int FMT, bool GROUPED, bool SW = false>
 hipError_t launch_lds(const GemmArgs& a, hipStream_t st) {
+  constexpr bool U = FMT == 1;   // staged UE8M0 scales exist for FMT 1 only
   if constexpr (SW) {
     // gate/up tiles with the SiLU-mul requant epilogue: the same two expert
     // classes and tile shapes as the plain grouped GEMM
@@ -1172,18 +1204,26 @@ hipError_t launch_lds(const GemmArgs& a, hipStream_t st) {
     // than 128: two launches over disjoint experts, each with its own
     // device-built tile table
     const int kb = (int)((a.K + 127) / 128);
-    hipError_t e = launch_cfg<FMT, 4, 2, 64, 128, true>(a, st, 1, kb, 1);
+    const hipError_t e = ue8m0_aligned(a, 1, kb)
+                             ? launch_cfg<FMT, 4, 2, 64, 128, true, false, false, U>(a, st, 1, kb, 1)
+                             : launch_cfg<FMT, 4, 2, 64, 128, true>(a, st, 1, kb, 1);
     if (e != hipSuccess) return e;
     return launch_cfg<FMT, 1, 4, 64, 64, true>(a, st, 1, kb, 2);
   } else {
-    if (a.w4) {
-      const Plan p = plan_dense(a.M, a.N, a.K);
-      if (p.big) return launch_cfg<FMT, 4, 2, 64, 128, false, true>(a, st, p.splits, p.kbps);
-      return launch_cfg<FMT, 2, 4, 64, 64, false, true>(a, st, p.splits, p.kbps);
-    }
     const Plan p = plan_dense(a.M, a.N, a.K);
-    if (p.big) return launch_cfg<FMT, 4, 2, 64, 128, false>(a, st, p.splits, p.kbps);
-    return launch_cfg<FMT, 2, 4, 64, 64, false>(a, st, p.splits, p.kbps);
+    const bool sa = ue8m0_aligned(a, p.splits, p.kbps);
+    if (a.w4) {
+      if (p.big)
+        return sa ? launch_cfg<FMT, 4, 2, 64, 128, false, true, false, U>(a, st, p.splits, p.kbps)
+                  : launch_cfg<FMT, 4, 2, 64, 128, false, true>(a, st, p.splits, p.kbps);
+      return sa ? launch_cfg<FMT, 2, 4, 64, 64, false, true, false, U>(a, st, p.splits, p.kbps)
+                : launch_cfg<FMT, 2, 4, 64, 64, false, true>(a, st, p.splits, p.kbps);
+    }
+    if (p.big)
+      return sa ? launch_cfg<FMT, 4, 2, 64, 128, false, false, false, U>(a, st, p.splits, p.kbps)
+                : launch_cfg<FMT, 4, 2, 64, 128, false>(a, st, p.splits, p.kbps);
+    return sa ? launch_cfg<FMT, 2, 4, 64, 64, false, false, false, U>(a, st, p.splits, p.kbps)
+              : launch_cfg<FMT, 2, 4, 64, 64, false>(a, st, p.splits, p.kbps);
   }
 }
 
