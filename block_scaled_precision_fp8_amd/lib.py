@@ -76,6 +76,12 @@ def load(path=None):
     if not os.path.exists(p):
         raise BsFp8Error("load", -1, f"{p} not built; run "
                          "`python -m block_scaled_precision_fp8_amd.build`")
+    # torch first: it brings its own HIP runtime under the same soname the
+    # library links (libamdhip64.so.7), so the library then binds to that one
+    # and kernels run on the runtime that owns torch's streams and memory.
+    # Opened before torch, the library would load the system runtime and
+    # torch a second one beside it.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(p)
     for name, (res, args) in _SIGS.items():
         fn = getattr(lib, name)

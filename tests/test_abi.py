@@ -30,9 +30,21 @@ def test_header_declarations_match_binding():
 
 
 def test_every_declared_symbol_exported():
+    L.load()                      # the binding's load order (torch's HIP runtime first)
     lib = ctypes.CDLL(L.LIB_PATH)
     for name in declared():
         assert hasattr(lib, name), name
+
+
+def test_one_hip_runtime_in_process():
+    """torch ships its own HIP runtime under the soname the library links;
+    after load() the process must map exactly one libamdhip64 (two would
+    run the kernels on a runtime that does not own torch's streams)."""
+    L.load()
+    import torch  # noqa: F401
+    with open("/proc/self/maps") as f:
+        paths = {line.split()[-1] for line in f if "libamdhip64" in line}
+    assert len(paths) == 1, paths
 
 
 def test_version_and_status_strings():

@@ -64,6 +64,34 @@ def test_block_gemm_parity(M, N, K, bias, fmt):
     assert err <= TOL
 
 
+@pytest.mark.parametrize("M,N,K,fmt", [
+    (4100, 4104, 1040, 0),   # 256 x 256 tiles; the second scale chunk runs past ragged K
+    (4100, 4104, 1040, 1),   # UE8M0 rows of 9 bytes: per-block scale loads
+    (4100, 4104, 1024, 1),   # UE8M0 rows of 8 bytes: staged scale chunks
+    (512, 512, 2688, 0),     # 7 K splits of 3 blocks: chunks start at every split
+    (640, 1024, 6400, 0),    # 8 splits of 7 blocks
+    (512, 512, 2560, 1),     # UE8M0, splits of 3 blocks: per-block loads
+    (384, 1024, 4096, 1),    # UE8M0, 8 splits of 4 blocks: staged chunks
+])
+def test_block_gemm_scale_staging(M, N, K, fmt):
+    """The activation-scale chunks the large-M kernel stages through LDS
+    (fp32 always, UE8M0 when every row and split is dword-aligned), at
+    chunk, split and ragged-K boundaries, against the oracle."""
+    from block_scaled_precision_fp8_amd import lib as L
+    kind, splits = L.gemm_kernel(M, N, K)
+    say(f"scale staging M={M} N={N} K={K} fmt={fmt} kind={kind} splits={splits}")
+    assert kind in (L.GEMM_TILE_256x256, L.GEMM_TILE_128x256)
+    x = synth.deepseek_acts(M, K, seed=K) if fmt else synth.llama_acts(M, K, seed=K)
+    w = synth.normal_bf16((N, K), 0.02, "llama", "w", seed=K + 1)
+    h, d = _quant_dev(x, w, fmt)
+    y = _gemm_dev(d, M, N, None, fmt)
+    ref = G.block_gemm(*h, fmt=fmt)
+    assert np.isfinite(y).all(), "unwritten outputs"
+    err = rel_fro(y, ref)
+    say(f"  rel fro {err:.3e}")
+    assert err <= TOL
+
+
 @pytest.mark.parametrize("M,K,N,fmt,gen", [
     (2048, 4096, 28672, 0, "llama"), (16, 14336, 4096, 0, "llama"),
     (128, 4096, 6144, 0, "llama"), (4096, 7168, 18432, 1, "deepseek"),
@@ -197,6 +225,7 @@ def _grouped_case(counts, N, K, fmt, seed):
     ([3, 0, 1, 6, 2], 256, 256),
     ([0, 0, 130, 0, 1, 257, 64, 0], 512, 640),
     ([300], 264, 1040),
+    ([0, 300, 5, 140], 384, 1024),   # large experts with dword-aligned UE8M0 scale rows
     (list(np.random.default_rng(5).integers(0, 40, 33)), 384, 512),
 ])
 def test_grouped_gemm_parity(counts, N, K, fmt):

@@ -76,6 +76,7 @@ def _gemm(M, N, K, fmt, bias=False, seed=0):
     (1, 256, 256, False), (5, 264, 288, True), (16, 1000, 1024, False), (17, 520, 4128, True),
     (64, 256, 2048, False), (130, 520, 640, True), (300, 1000, 1056, False), (1024, 1024, 1024, True),
     (4100, 4104, 384, True),     # 256 x 256 tiles, ragged in M, N and K
+    (4100, 4104, 512, False),    # 256 x 256 tiles, dword-aligned UE8M0 scale rows (staged)
 ])
 def test_fp8_fp4_gemm_parity(M, N, K, bias, fmt):
     say(f"fp8 x fp4 gemm M={M} N={N} K={K} fmt={fmt}")
