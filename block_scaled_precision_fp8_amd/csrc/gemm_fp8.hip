@@ -238,6 +238,12 @@ __device__ __forceinline__ v8i read_frag(const uint8_t* __restrict__ row, int ch
 // a staged scale, read the same way (no wait for the in-flight DMA)
 __device__ __forceinline__ float read_scale(const float* __restrict__ p, int idx) { return p[idx]; }
 __device__ __forceinline__ uint32_t read_byte(const uint8_t* __restrict__ p, int idx) { return p[idx]; }
+__device__ __forceinline__ uint32_t read_u32(const uint8_t* __restrict__ p, int off) {
+  return *(const uint32_t*)(p + off);
+}
+__device__ __forceinline__ float4 read_scale4(const uint8_t* __restrict__ p, int off) {
+  return *(const float4*)(p + off);
+}
 
 // SiLU(gate) * up with the 1 x 128 requantization, for a gate/up tile of
 // the grouped GEMM (the step between an MoE expert's gate/up and down
@@ -904,7 +910,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
 // takes for group g is half (u & 1) of logical chunk u >> 1, u = 4 g + g4,
 // and the chunk swizzle keeps those reads free of bank conflicts.
 // ------------------------------------------------------------------------
-template <int FMT>
+template <int FMT, bool SA>
 __global__ __launch_bounds__(256, 2) void gemm_b32_kernel(
     const uint8_t* __restrict__ xq, const void* __restrict__ xs, const uint8_t* __restrict__ wq,
     const void* __restrict__ wsc, const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
@@ -916,7 +922,17 @@ __global__ __launch_bounds__(256, 2) void gemm_b32_kernel(
   constexpr int STAGE = (BM + BN) * kRowBytes;
   constexpr int SB = FMT == 0 ? 4 : 1;
   constexpr int J = BM * 8 / (64 * WAVES);           // DMA loads per lane per operand
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE];
+  // Activation scales are staged through LDS in chunks of 32 bytes per row
+  // (SCH K blocks: 2 of fp32, 8 of UE8M0 scales), one request per row and
+  // chunk instead of one per row and group.  UE8M0 rows (K/32 bytes) are
+  // dword-aligned only when K is a multiple of 128; the launcher picks the
+  // per-group loads (SA false) otherwise.  fp32 always stages.
+  constexpr bool SCL = FMT == 0 || SA;
+  constexpr int SCH = 32 / (4 * SB);                 // K blocks per chunk
+  constexpr int SBUF = BM * 32;                      // bytes per chunk buffer
+  constexpr int SJ = BM * 8 / (64 * WAVES);          // chunk DMA loads per lane
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE + (SCL ? 2 * SBUF : 0)];
+  uint8_t* const sbuf = lds + 2 * STAGE;
   const Tile tl = dense_tile<BM, BN>(M, N, 1);
   if (!tl.valid) return;
   const int KB = (int)((K + 127) / 128);
@@ -945,7 +961,7 @@ __global__ __launch_bounds__(256, 2) void gemm_b32_kernel(
     saoff[i] = r < mrows ? (uint32_t)(r * GS * SB) : kOOB;
   }
   const int64_t nb0 = (tl.n0 + wn * 64) >> 5;        // the wave's two weight blocks
-  float sa_reg[2][MI][4];
+  float sa_reg[SCL ? 1 : 2][MI][4];
   float sw_reg[2][2][4];
 
   auto issue = [&](int kb, int buf) {
@@ -960,15 +976,32 @@ __global__ __launch_bounds__(256, 2) void gemm_b32_kernel(
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, BSFP8_LDS(sw + (j * WAVES + wave) * 1024), 16,
                                                dma_src(q, nrows, kbyte), 0, 0, 0);
     }
+    if constexpr (SCL) {
+      // at a chunk's first K block: 32 bytes of every row (lane q: row q / 8,
+      // dword q % 8); bytes past the row's last group are never used
+      if (kb % SCH == 0) {
+        uint8_t* dst = sbuf + ((kb / SCH) & 1) * SBUF;
+#pragma unroll
+        for (int j = 0; j < SJ; ++j) {
+          const int q = (j * WAVES + wave) * 64 + lane;
+          const int row = q >> 3;
+          const uint32_t off = row < mrows ? (uint32_t)(row * GS * SB + kb * 4 * SB + (q & 7) * 4) : kOOB;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, BSFP8_LDS(dst + (j * WAVES + wave) * 256), 4,
+                                                   off, 0, 0, 0);
+        }
+      }
+    }
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int gi = kb * 4 + g;
+      if constexpr (!SCL) {
 #pragma unroll
-      for (int i = 0; i < MI; ++i) {
-        const uint32_t off = (saoff[i] == kOOB || gi >= GS) ? kOOB : saoff[i] + gi * SB;
-        sa_reg[buf][i][g] = FMT == 0
-            ? __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsa, off, 0, 0))
-            : e8m0_f32(__builtin_amdgcn_raw_buffer_load_b8(rsa, off, 0, 0));
+        for (int i = 0; i < MI; ++i) {
+          const uint32_t off = (saoff[i] == kOOB || gi >= GS) ? kOOB : saoff[i] + gi * SB;
+          sa_reg[buf][i][g] = FMT == 0
+              ? __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsa, off, 0, 0))
+              : e8m0_f32(__builtin_amdgcn_raw_buffer_load_b8(rsa, off, 0, 0));
+        }
       }
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
@@ -993,6 +1026,33 @@ __global__ __launch_bounds__(256, 2) void gemm_b32_kernel(
     const uint8_t* swl = lds + buf * STAGE + XBYTES + (wn * 64 + l16) * kRowBytes;
     issue(kb_next, buf ^ 1);
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
+    // this block's token scales (4 groups per row) from the chunk buffer;
+    // groups past K take 0 so no other row's scale meets a zero product
+    float sa[MI][4];
+    if constexpr (SCL) {
+      const int kb = kb_next - 1;
+      const uint8_t* sc = sbuf + ((kb / SCH) & 1) * SBUF + (kb % SCH) * 4 * SB;
+#pragma unroll
+      for (int j = 0; j < MI; ++j) {
+        const int o = (wm * 64 + j * 16 + l16) * 32;
+        if constexpr (FMT == 0) {
+          const float4 v = read_scale4(sc, o);
+          sa[j][0] = v.x; sa[j][1] = v.y; sa[j][2] = v.z; sa[j][3] = v.w;
+        } else {
+          const uint32_t v = read_u32(sc, o);
+#pragma unroll
+          for (int g = 0; g < 4; ++g) sa[j][g] = e8m0_f32((v >> (8 * g)) & 0xff);
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          if (kb * 4 + g >= GS) sa[j][g] = 0.0f;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < MI; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) sa[j][g] = sa_reg[buf][j][g];
+    }
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       // rows start at multiples of 16: the row swizzle is the lane's (l16 >> 1)
@@ -1007,7 +1067,7 @@ __global__ __launch_bounds__(256, 2) void gemm_b32_kernel(
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int j = 0; j < MI; ++j) sc[b][j] = sa_reg[buf][j][g] * sw_reg[buf][b][g];
+        for (int j = 0; j < MI; ++j) sc[b][j] = sa[j][g] * sw_reg[buf][b][g];
 #pragma unroll
       for (int i = 0; i < NI; ++i)
 #pragma unroll
@@ -1053,14 +1113,18 @@ __global__ __launch_bounds__(256, 2) void gemm_b32_kernel(
 #endif
 }
 
-template __global__ void gemm_b32_kernel<0>(const uint8_t* __restrict__, const void* __restrict__,
+template __global__ void gemm_b32_kernel<0, false>(const uint8_t* __restrict__, const void* __restrict__,
                                             const uint8_t* __restrict__, const void* __restrict__,
                                             const uint16_t* __restrict__, uint16_t* __restrict__,
                                             int64_t, int64_t, int64_t);
-template __global__ void gemm_b32_kernel<1>(const uint8_t* __restrict__, const void* __restrict__,
+template __global__ void gemm_b32_kernel<1, false>(const uint8_t* __restrict__, const void* __restrict__,
                                             const uint8_t* __restrict__, const void* __restrict__,
                                             const uint16_t* __restrict__, uint16_t* __restrict__,
                                             int64_t, int64_t, int64_t);
+template __global__ void gemm_b32_kernel<1, true>(const uint8_t* __restrict__, const void* __restrict__,
+                                           const uint8_t* __restrict__, const void* __restrict__,
+                                           const uint16_t* __restrict__, uint16_t* __restrict__,
+                                           int64_t, int64_t, int64_t);
 
 // Explicit instantiations of every tile configuration the dispatcher below
 // can launch (the host pass does not always emit launch stubs for kernel
@@ -1289,11 +1353,14 @@ hipError_t launch_b32(const GemmArgs& a, hipStream_t st) {
   int64_t tiles = (a.M + 127) / 128 * ((a.N + 127) / 128);
   tiles = (tiles + 7) / 8 * 8;                   // whole rounds over the 8 XCDs
   if (a.fmt == 0)
-    hipLaunchKernelGGL(gemm_b32_kernel<0>, dim3((unsigned)tiles), dim3(256), 0, st, a.xq, a.xs,
-                       a.wq, a.ws, a.bias, a.y, a.M, a.N, a.K);
+    hipLaunchKernelGGL((gemm_b32_kernel<0, false>), dim3((unsigned)tiles), dim3(256), 0, st, a.xq,
+                       a.xs, a.wq, a.ws, a.bias, a.y, a.M, a.N, a.K);
+  else if (a.K % 128 == 0)   // UE8M0 rows of K/32 bytes are dword-aligned: staged scales
+    hipLaunchKernelGGL((gemm_b32_kernel<1, true>), dim3((unsigned)tiles), dim3(256), 0, st, a.xq,
+                       a.xs, a.wq, a.ws, a.bias, a.y, a.M, a.N, a.K);
   else
-    hipLaunchKernelGGL(gemm_b32_kernel<1>, dim3((unsigned)tiles), dim3(256), 0, st, a.xq, a.xs,
-                       a.wq, a.ws, a.bias, a.y, a.M, a.N, a.K);
+    hipLaunchKernelGGL((gemm_b32_kernel<1, false>), dim3((unsigned)tiles), dim3(256), 0, st, a.xq,
+                       a.xs, a.wq, a.ws, a.bias, a.y, a.M, a.N, a.K);
   return hipGetLastError();
 }
 

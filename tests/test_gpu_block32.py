@@ -96,6 +96,7 @@ def _gemm(M, N, K, fmt, bias, seed):
 @pytest.mark.parametrize("M,N,K,bias", [
     (1, 256, 256, False), (16, 264, 400, True), (130, 520, 640, False), (300, 1000, 1040, True),
     (257, 136, 4112, False), (5, 136, 4112, True),
+    (260, 264, 2048, True),    # two staged chunks of UE8M0 scales (K a multiple of 128)
 ])
 def test_block32_gemm_parity(M, N, K, bias, fmt):
     say(f"gemm 32x32 M={M} N={N} K={K} fmt={fmt}")
