@@ -29,7 +29,7 @@ import sys
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 GEMM_SOURCE = os.path.join(ROOT, "block_scaled_precision_fp8_amd", "csrc", "gemm_fp8.hip")
-GEMM_KERNEL = "gemm_lds_kernel<0, 4, 2, 64, 128, false, false, false>"
+GEMM_KERNEL = "gemm_lds_kernel<0, 4, 2, 64, 128, false, false, false, false>"
 
 
 def per_kernel(path, counter):

@@ -45,6 +45,8 @@ def _gemm_dev(d, M, N, bias_bits=None, fmt=0):
     (130, 520, 640, False), (300, 1000, 1040, True), (256, 256, 128, False),
     (513, 768, 2048, True), (1024, 1024, 1024, False),
     (4100, 4104, 384, True),      # enough tiles for the 256 x 256 tile, ragged in M and N
+    (5, 16400, 1040, True),       # decode, N past 16K, ragged N and K
+    (16, 16384, 256, False),      # decode, N = 16K
 ])
 def test_block_gemm_parity(M, N, K, bias, fmt):
     say(f"block gemm M={M} N={N} K={K} bias={bias} fmt={fmt}")
