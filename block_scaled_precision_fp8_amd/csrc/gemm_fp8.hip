@@ -675,6 +675,49 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
     return;
   }
 
+  // bf16 epilogue through LDS when the stage buffers hold the whole output
+  // tile: waves write their tiles (bias added, rounded) row-major with 16-byte
+  // chunks swizzled by row, then every thread stores whole 16-byte chunks, 32
+  // lanes to a 512-byte row, so the output leaves in full lines
+  constexpr int CPR = BN / 8;                 // 16-byte chunks per output row
+  if constexpr (BM * BN * 2 <= STAGES * STAGE) {
+    if (part == nullptr) {
+      __syncthreads();                        // every fragment read of the last stage done
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int col = wn * WN + i * 16 + 4 * g4;
+        const int64_t n = tl.n0 + col;
+#pragma unroll
+        for (int j = 0; j < MI; ++j) {
+          const int row = wm * WM + j * 16 + l16;
+          v4f v = acc[i][j];
+          if (bias && n < N) {
+            const uint2 b = *(const uint2*)(bias + n);
+            v[0] += bf16_lo(b.x); v[1] += bf16_hi(b.x);
+            v[2] += bf16_lo(b.y); v[3] += bf16_hi(b.y);
+          }
+          uint2 o;
+          o.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+          o.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+          const int c = col >> 3;
+          *(uint2*)(lds + row * (BN * 2) + ((c ^ (row & (CPR - 1))) << 4) + ((col >> 2) & 1) * 8) = o;
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int p = 0; p < BM * CPR / THREADS; ++p) {
+        const int L = p * THREADS + (int)threadIdx.x;
+        const int row = L / CPR, c = L % CPR;
+        const int64_t n = tl.n0 + c * 8;
+        if (row < mrows && n < N) {
+          const uint4 v = *(const uint4*)(lds + row * (BN * 2) + ((c ^ (row & (CPR - 1))) << 4));
+          *(uint4*)(y + (tl.m0 + row) * N + n) = v;
+        }
+      }
+      return;
+    }
+  }
+
   // epilogue: lane holds n = nwave + 16 i + 4 g4 + {0..3} for token m_j
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
