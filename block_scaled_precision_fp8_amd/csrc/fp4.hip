@@ -411,16 +411,35 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void fp4_gemm_lds_kernel
     if (kb + 1 < KB) iter(kb + 1, S1{});
   }
 
+  // bf16 epilogue through LDS (the loop ended with a barrier after its last
+  // fragment reads): waves write their tiles row-major, 16-byte chunks
+  // swizzled by row, then every thread stores whole chunks, 16 lanes to a
+  // 256-byte row, so the output leaves in full lines
   const float gg = (*xt) * (*wt);
+  constexpr int CPR = kLdsBN / 8;              // 16-byte chunks per output row
+  uint8_t* ot = lds[0];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const int64_t n = n0 + wn * WN + i * 16 + 4 * g4;
-    if (n >= N) continue;
+    const int col = wn * WN + i * 16 + 4 * g4;
 #pragma unroll
     for (int j = 0; j < MI; ++j) {
-      const int64_t m = m0 + wm * WM + j * 16 + l16;
-      if (m < M) store4_bf16(y, N, m, n, acc[i][j] * gg);
+      const int row = wm * WM + j * 16 + l16;
+      const v4f v = acc[i][j] * gg;
+      uint2 o;
+      o.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+      o.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+      const int c = col >> 3;
+      *(uint2*)(ot + row * (kLdsBN * 2) + ((c ^ (row & (CPR - 1))) << 4) + ((col >> 2) & 1) * 8) = o;
     }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < kLdsBM * CPR / THREADS; ++p) {
+    const int L = p * THREADS + tid;
+    const int row = L / CPR, c = L % CPR;
+    const int64_t m = m0 + row, n = n0 + c * 8;
+    if (m < M && n < N)
+      *(uint4*)(y + m * N + n) = *(const uint4*)(ot + row * (kLdsBN * 2) + ((c ^ (row & (CPR - 1))) << 4));
   }
 }
 

@@ -1142,16 +1142,40 @@ __global__ __launch_bounds__(256, 2) void gemm_b32_kernel(
   }
   wait_vmcnt<0>();
 
-  // lane holds n = 16 i + 4 g4 + {0..3} of its wave's columns, token m_j
+  // bf16 epilogue through the first stage buffer: lane holds n = 16 i + 4 g4
+  // + {0..3} of its wave's columns for token m_j; the tile is written row-
+  // major with 16-byte chunks swizzled by row, then stored whole chunks at a
+  // time, 16 lanes to a 256-byte row
+  constexpr int CPR = BN / 8;
+  __syncthreads();                           // every fragment read of the last stage done
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const int64_t n = tl.n0 + wn * 64 + i * 16 + 4 * g4;
-    if (n >= N) continue;
+    const int col = wn * 64 + i * 16 + 4 * g4;
+    const int64_t n = tl.n0 + col;
 #pragma unroll
     for (int j = 0; j < MI; ++j) {
-      const int64_t m = tl.m0 + wm * 64 + j * 16 + l16;
-      if (m < M) store_out4(y, N, m, n, acc[i][j], bias);
+      const int row = wm * 64 + j * 16 + l16;
+      v4f v = acc[i][j];
+      if (bias && n < N) {
+        const uint2 b = *(const uint2*)(bias + n);
+        v[0] += bf16_lo(b.x); v[1] += bf16_hi(b.x);
+        v[2] += bf16_lo(b.y); v[3] += bf16_hi(b.y);
+      }
+      uint2 o;
+      o.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+      o.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+      const int c = col >> 3;
+      *(uint2*)(lds + row * (BN * 2) + ((c ^ (row & (CPR - 1))) << 4) + ((col >> 2) & 1) * 8) = o;
     }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < BM * CPR / (64 * WAVES); ++p) {
+    const int L = p * 64 * WAVES + (int)threadIdx.x;
+    const int row = L / CPR, c = L % CPR;
+    const int64_t m = tl.m0 + row, n = tl.n0 + c * 8;
+    if (m < M && n < N)
+      *(uint4*)(y + m * N + n) = *(const uint4*)(lds + row * (BN * 2) + ((c ^ (row & (CPR - 1))) << 4));
   }
 #endif
 }
