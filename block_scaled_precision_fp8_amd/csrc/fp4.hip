@@ -185,7 +185,12 @@ __device__ __forceinline__ half8 frag_step(const Frag128& f, int t) {
 constexpr int kStreamWaves = 4;
 template <int MT> constexpr int kStreamBlocks = MT == 4 ? 2 : 4;
 
-template <int MT>
+// S8 (K a multiple of 128, so a row's 8 scale bytes of a K block are 8-byte
+// aligned): lane g4 < U loads all 8 weight-scale bytes of block kb + g4 in
+// one load and the lanes of a row exchange them, one request per row per
+// round of U blocks instead of one per row and block (the scales' own lines
+// would otherwise double the requests of the weight stream)
+template <int MT, bool S8>
 __global__ __launch_bounds__(64 * kStreamWaves) void fp4_gemm_stream_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
     const float* __restrict__ xt, const uint8_t* __restrict__ wq,
@@ -209,13 +214,57 @@ __global__ __launch_bounds__(64 * kStreamWaves) void fp4_gemm_stream_kernel(
     // the weight fragments (HBM) and the activation fragments (L2) of U
     // blocks, all issued before any is used so their latencies overlap
     Frag128 fw[U], fx[U][MT];
+    uint2 wsc8 = make_uint2(0, 0), xsc8[MT];
+    if constexpr (S8) {
+      if (nvalid && g4 < U && kb + g4 < kb1)
+        wsc8 = *(const uint2*)(ws + (n0 + l16) * (K / 16) + (kb + g4) * 8);
+#pragma unroll
+      for (int j = 0; j < MT; ++j) {
+        xsc8[j] = make_uint2(0, 0);
+        if (j * 16 + l16 < M && g4 < U && kb + g4 < kb1)
+          xsc8[j] = *(const uint2*)(xs + (int64_t)(j * 16 + l16) * (K / 16) + (kb + g4) * 8);
+      }
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      fw[u] = load_frag128(wq, ws, n0 + l16, K, kb + u, g4, nvalid && kb + u < kb1);
+      if constexpr (S8) {
+        fw[u].codes = make_uint4(0, 0, 0, 0);
+        fw[u].scales = 0;
+        const int64_t k0 = (kb + u) * 128 + 32 * g4;
+        if (nvalid && kb + u < kb1 && k0 < K)
+          fw[u].codes = *(const uint4*)(wq + (n0 + l16) * (K / 2) + k0 / 2);
+      } else {
+        fw[u] = load_frag128(wq, ws, n0 + l16, K, kb + u, g4, nvalid && kb + u < kb1);
+      }
 #pragma unroll
-      for (int j = 0; j < MT; ++j)
-        fx[u][j] = load_frag128(xq, xs, j * 16 + l16, K, kb + u, g4,
-                                j * 16 + l16 < M && kb + u < kb1);
+      for (int j = 0; j < MT; ++j) {
+        if constexpr (S8) {
+          fx[u][j].codes = make_uint4(0, 0, 0, 0);
+          fx[u][j].scales = 0;
+          const int64_t k0 = (kb + u) * 128 + 32 * g4;
+          if (j * 16 + l16 < M && kb + u < kb1 && k0 < K)
+            fx[u][j].codes = *(const uint4*)(xq + (int64_t)(j * 16 + l16) * (K / 2) + k0 / 2);
+        } else {
+          fx[u][j] = load_frag128(xq, xs, j * 16 + l16, K, kb + u, g4,
+                                  j * 16 + l16 < M && kb + u < kb1);
+        }
+      }
+    }
+    if constexpr (S8) {
+      // this lane's two bytes of block kb + u: bytes 2 g4, 2 g4 + 1 of the
+      // 8 held by lane (l16, u)
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t lo = __shfl(wsc8.x, l16 + 16 * u);
+        const uint32_t hi = __shfl(wsc8.y, l16 + 16 * u);
+        fw[u].scales = ((g4 < 2 ? lo : hi) >> (16 * (g4 & 1))) & 0xffffu;
+#pragma unroll
+        for (int j = 0; j < MT; ++j) {
+          const uint32_t xl = __shfl(xsc8[j].x, l16 + 16 * u);
+          const uint32_t xh = __shfl(xsc8[j].y, l16 + 16 * u);
+          fx[u][j].scales = ((g4 < 2 ? xl : xh) >> (16 * (g4 & 1))) & 0xffffu;
+        }
+      }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -515,12 +564,20 @@ hipError_t launch_fp4_gemm(const uint8_t* xq, const uint8_t* xs, const float* xt
   float* part = real > 1 ? (float*)ws : nullptr;
   dim3 grid((unsigned)((N + 16 * kStreamWaves - 1) / (16 * kStreamWaves)), real);
   const int Mi = (int)M;
-#define BSFP8_FP4S(MT)                                                                          \
-  hipLaunchKernelGGL((fp4_gemm_stream_kernel<MT>), grid, dim3(64 * kStreamWaves), 0, s, xq, xs, \
-                     xt, wq, wsc, wt, y, part, Mi, N, K, kbps)
-  if (M <= 16) BSFP8_FP4S(1);
-  else if (M <= 32) BSFP8_FP4S(2);
-  else BSFP8_FP4S(4);
+#define BSFP8_FP4S(MT)                                                                         \
+  if (K % 128 == 0)                                                                            \
+    hipLaunchKernelGGL((fp4_gemm_stream_kernel<MT, true>), grid, dim3(64 * kStreamWaves), 0, s, \
+                       xq, xs, xt, wq, wsc, wt, y, part, Mi, N, K, kbps);                       \
+  else                                                                                         \
+    hipLaunchKernelGGL((fp4_gemm_stream_kernel<MT, false>), grid, dim3(64 * kStreamWaves), 0,   \
+                       s, xq, xs, xt, wq, wsc, wt, y, part, Mi, N, K, kbps)
+  if (M <= 16) {
+    BSFP8_FP4S(1);
+  } else if (M <= 32) {
+    BSFP8_FP4S(2);
+  } else {
+    BSFP8_FP4S(4);
+  }
 #undef BSFP8_FP4S
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || part == nullptr) return e;
