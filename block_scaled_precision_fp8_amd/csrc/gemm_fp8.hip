@@ -782,13 +782,21 @@ constexpr int kDecodeDepth = 2;
 // block runs as four MFMAs whose weight operand keeps only group g's lanes,
 // each promoted by s_a[m, g] s_w[n/32, g] in fp32 (UE8M0 bytes decoded to
 // their powers of two); the extra MFMAs are free in this HBM-bound kernel.
-template <int FMT, bool FUSED, bool W4 = false, bool B32 = false>
+// the activation scales of at most 16 tokens, staged whole (SXL) when they fit
+constexpr int kDecodeXsBytes = 16384;
+
+template <int FMT, bool FUSED, bool W4 = false, bool B32 = false, bool SXL = false>
 __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
     const uint8_t* __restrict__ xq, const void* __restrict__ xs,
     const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ wq,
     const void* __restrict__ wsc, const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
     int M, int64_t N, int64_t K) {
+  static_assert(!SXL || (!FUSED && !B32), "staged activation scales: quantized X, 128-wide groups");
   __shared__ v4f red[kDecodeWaves][64];
+  // SXL: the M x KB activation scales, read once (contiguous) instead of one
+  // scale per token row per K block, which cost as many requests as the
+  // X codes themselves
+  __shared__ __attribute__((aligned(16))) uint8_t sxs[SXL ? kDecodeXsBytes : 16];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
@@ -798,6 +806,18 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
   const bool mvalid = l16 < M;             // this lane's token row (B column)
   const int KB = (int)((K + 127) / 128);
   const int64_t nblk = n0 >> 7;
+  constexpr int SBX = FMT == 0 ? 4 : 1;
+  if constexpr (SXL) {
+    const int nbytes = M * KB * SBX;               // <= kDecodeXsBytes (launcher)
+    for (int i = threadIdx.x * 4; i < nbytes; i += 64 * kDecodeWaves * 4) {
+      if (i + 4 <= nbytes) {
+        *(uint32_t*)(sxs + i) = *(const uint32_t*)((const uint8_t*)xs + i);
+      } else {
+        for (int b = i; b < nbytes; ++b) sxs[b] = ((const uint8_t*)xs)[b];
+      }
+    }
+    __syncthreads();
+  }
   const int64_t KW = W4 ? K / 2 : K;       // W bytes per row
   const int64_t G32 = K / 32;
   const int64_t GS = (K + 31) / 32;        // B32: scale groups per row
@@ -868,7 +888,12 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
           const int64_t k0 = (int64_t)kb * 128 + kx0, k1 = (int64_t)kb * 128 + kx1;
           if (k0 < K) xa[u] = *(const uint4*)(xq + (int64_t)l16 * K + k0);
           if (k1 < K) xb[u] = *(const uint4*)(xq + (int64_t)l16 * K + k1);
-          if (!B32) sx[u] = load_scale<FMT>(xs, (int64_t)l16 * KB + kb);
+          if constexpr (SXL) {
+            sx[u] = FMT == 0 ? ((const float*)sxs)[l16 * KB + kb]
+                             : __int_as_float((int)sxs[l16 * KB + kb]);
+          } else if (!B32) {
+            sx[u] = load_scale<FMT>(xs, (int64_t)l16 * KB + kb);
+          }
         }
       }
     }
@@ -1401,18 +1426,33 @@ template <int FMT>
 hipError_t launch_decode(const GemmArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)((a.N + 15) / 16));
   const dim3 block(64 * kDecodeWaves);
-  if (a.x_bf16)
+  // staged activation scales when the M x KB scales fit the LDS slot and
+  // several token rows share the staging (at M = 1 its prologue costs more
+  // than the one scale row's loads it saves)
+  const bool sxl = a.M >= 4 && a.M * ((a.K + 127) / 128) * (a.fmt == 0 ? 4 : 1) <= kDecodeXsBytes;
+  if (a.x_bf16) {
     hipLaunchKernelGGL((gemm_decode_kernel<FMT, true>), grid, block, 0, st, nullptr, nullptr,
                        a.x_bf16, a.ldx, a.wq, a.ws, a.bias, a.y, (int)a.M, a.N, a.K);
-  else if (a.blk == 32)
+  } else if (a.blk == 32) {
     hipLaunchKernelGGL((gemm_decode_kernel<FMT, false, false, true>), grid, block, 0, st, a.xq,
                        a.xs, nullptr, (int64_t)0, a.wq, a.ws, a.bias, a.y, (int)a.M, a.N, a.K);
-  else if (a.w4)
-    hipLaunchKernelGGL((gemm_decode_kernel<FMT, false, true>), grid, block, 0, st, a.xq, a.xs,
-                       nullptr, (int64_t)0, a.wq, a.ws, a.bias, a.y, (int)a.M, a.N, a.K);
-  else
-    hipLaunchKernelGGL((gemm_decode_kernel<FMT, false>), grid, block, 0, st, a.xq, a.xs, nullptr,
-                       (int64_t)0, a.wq, a.ws, a.bias, a.y, (int)a.M, a.N, a.K);
+  } else if (a.w4) {
+    if (sxl)
+      hipLaunchKernelGGL((gemm_decode_kernel<FMT, false, true, false, true>), grid, block, 0, st,
+                         a.xq, a.xs, nullptr, (int64_t)0, a.wq, a.ws, a.bias, a.y, (int)a.M, a.N,
+                         a.K);
+    else
+      hipLaunchKernelGGL((gemm_decode_kernel<FMT, false, true>), grid, block, 0, st, a.xq, a.xs,
+                         nullptr, (int64_t)0, a.wq, a.ws, a.bias, a.y, (int)a.M, a.N, a.K);
+  } else {
+    if (sxl)
+      hipLaunchKernelGGL((gemm_decode_kernel<FMT, false, false, false, true>), grid, block, 0, st,
+                         a.xq, a.xs, nullptr, (int64_t)0, a.wq, a.ws, a.bias, a.y, (int)a.M, a.N,
+                         a.K);
+    else
+      hipLaunchKernelGGL((gemm_decode_kernel<FMT, false>), grid, block, 0, st, a.xq, a.xs, nullptr,
+                         (int64_t)0, a.wq, a.ws, a.bias, a.y, (int)a.M, a.N, a.K);
+  }
   return hipGetLastError();
 }
 
