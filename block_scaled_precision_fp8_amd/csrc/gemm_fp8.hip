@@ -370,7 +370,7 @@ __device__ __forceinline__ void swiglu_epilogue(v4f (&acc)[WN / 16][WM / 16], ui
 // with the X chunks g4 and g4 + 4 of the FP8 operand (the lane layout of
 // the FP4 x FP8 form, checked on the GPU), and passes its own group's scale.
 template <int FMT, int WAVES_M, int WAVES_N, int WM, int WN, bool GROUPED, bool W4 = false,
-          bool SWIGLU = false, bool SA = false>
+          bool SWIGLU = false, bool SA = false, bool SW4 = false>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
     const uint8_t* __restrict__ xq, const void* __restrict__ xs, const uint8_t* __restrict__ wq,
     const void* __restrict__ wsc, const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
@@ -412,8 +412,19 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
   constexpr int SBUF = BM * SROW;           // bytes per chunk buffer
   constexpr int SJ = SCL ? BM * SDW / (64 * WAVES) : 0;   // chunk DMA loads per lane
   static_assert(!SCL || SJ * 64 * WAVES == BM * SDW, "scale chunk / thread mismatch");
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES * STAGE + (SCL ? 2 * SBUF : 0)];
+  // MXFP4 weight scales (SW4, K a multiple of 128 so every row's 4 bytes per
+  // K block are dword-aligned) are staged the same way, 8 K blocks (32 bytes)
+  // per weight row per chunk, instead of one byte load per lane, subtile and
+  // K block (16 rows, so 16 requests, per load)
+  static_assert(!SW4 || W4, "staged MXFP4 scales need MXFP4 weights");
+  constexpr int WCH = 8;
+  constexpr int WBUF = BN * 32;
+  constexpr int WSJ = SW4 ? BN * 8 / (64 * WAVES) : 0;
+  static_assert(!SW4 || WSJ * 64 * WAVES == BN * 8, "weight-scale chunk / thread mismatch");
+  __shared__ __attribute__((aligned(1024)))
+  uint8_t lds[STAGES * STAGE + (SCL ? 2 * SBUF : 0) + (SW4 ? 2 * WBUF : 0)];
   uint8_t* const sbuf = lds + STAGES * STAGE;
+  uint8_t* const wbuf = sbuf + (SCL ? 2 * SBUF : 0);
   static_assert(!GROUPED || STAGES * STAGE >= 1025 * 4, "tile table fits the stage buffers");
   static_assert(!SWIGLU || WAVES_M * (WAVES_N / 2) * MI * NI * 1024 +
                                (WAVES_N > 2 ? WAVES_M * (WAVES_N / 2) * MI * 64 : 0) <=
@@ -491,7 +502,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
 
   float sa_reg[STAGES][MI];
   float sw_reg[STAGES];
-  int sw4_reg[STAGES][W4 ? NI : 1];
+  int sw4_reg[STAGES][W4 && !SW4 ? NI : 1];
 
   // issue one stage: X and W tiles into LDS buffer `buf`, scales into
   // registers; exactly LOADS vector-memory ops per lane, in this order.
@@ -539,7 +550,20 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
         else sa_reg[buf][i] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b8(rsa, off, 0, 0));
       }
     }
-    if constexpr (W4) {
+    if constexpr (SW4) {
+      const int rel = kb - kb_begin;
+      if (rel % WCH == 0) {
+        uint8_t* dst = wbuf + ((rel / WCH) & 1) * WBUF;
+#pragma unroll
+        for (int j = 0; j < WSJ; ++j) {
+          const int q = (j * WAVES + wave) * 64 + lane;
+          const int row = q >> 3;
+          const uint32_t off = row < nrows ? (uint32_t)(row * G32 + kb * 4 + (q & 7) * 4) : kOOB;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw4, BSFP8_LDS(dst + (j * WAVES + wave) * 256), 4,
+                                                   off, 0, 0, 0);
+        }
+      }
+    } else if constexpr (W4) {
 #pragma unroll
       for (int ii = 0; ii < NI; ++ii) {
         const int r = wn * WN + ii * 16 + l16;
@@ -590,7 +614,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
     float sw = W4 ? 0.0f : sw_reg[buf];
     if (FMT == 1) sw = __int_as_float(__float_as_int(sw) & 0xff);
     int sw4[W4 ? NI : 1];
-    if constexpr (W4) {
+    if constexpr (SW4) {
+      // this lane's group byte (g4) of K block kb_cur for each of its subtile rows
+      const int rel = kb_cur - kb_begin;
+      const uint8_t* wsc4 = wbuf + ((rel / WCH) & 1) * WBUF + (rel % WCH) * 4 + g4;
+#pragma unroll
+      for (int ii = 0; ii < NI; ++ii) sw4[ii] = (int)read_byte(wsc4, (wn * WN + ii * 16 + l16) * 32);
+    } else if constexpr (W4) {
 #pragma unroll
       for (int ii = 0; ii < NI; ++ii) sw4[ii] = sw4_reg[buf][ii] & 0xff;
     }
@@ -1222,7 +1252,9 @@ template __global__ void gemm_b32_kernel<1, true>(const uint8_t* __restrict__, c
 // can launch (the host pass does not always emit launch stubs for kernel
 // templates that are only instantiated implicitly).
 #define BSFP8_INST(FMT, WMN, WNN, WM, WN, G, W4, SW, SA)                                      \
-  template __global__ void gemm_lds_kernel<FMT, WMN, WNN, WM, WN, G, W4, SW, SA>(            \
+  BSFP8_INST2(FMT, WMN, WNN, WM, WN, G, W4, SW, SA, false)
+#define BSFP8_INST2(FMT, WMN, WNN, WM, WN, G, W4, SW, SA, SW4)                                \
+  template __global__ void gemm_lds_kernel<FMT, WMN, WNN, WM, WN, G, W4, SW, SA, SW4>(       \
       const uint8_t* __restrict__, const void* __restrict__, const uint8_t* __restrict__,     \
       const void* __restrict__, const uint16_t* __restrict__, uint16_t* __restrict__, int64_t, \
       int64_t, int64_t, const int32_t* __restrict__, int, int, float* __restrict__, int,      \
@@ -1246,7 +1278,16 @@ template __global__ void gemm_b32_kernel<1, true>(const uint8_t* __restrict__, c
 BSFP8_INST_ALL(0)
 BSFP8_INST_ALL(1)
 BSFP8_INST_UE8M0_STAGED
+// MXFP4 tiles with staged weight scales (K a multiple of 128; the 256 x 256
+// tile with fp32 activation scales keeps the per-subtile loads: staged, the
+// compiler spills it heavily)
+BSFP8_INST2(0, 2, 4, 64, 64, false, true, false, false, true)
+BSFP8_INST2(1, 4, 2, 64, 128, false, true, false, false, true)
+BSFP8_INST2(1, 2, 4, 64, 64, false, true, false, false, true)
+BSFP8_INST2(1, 4, 2, 64, 128, false, true, false, true, true)
+BSFP8_INST2(1, 2, 4, 64, 64, false, true, false, true, true)
 #undef BSFP8_INST_UE8M0_STAGED
+#undef BSFP8_INST2
 #undef BSFP8_INST_ALL
 #undef BSFP8_INST
 
@@ -1268,7 +1309,7 @@ constexpr int64_t kDecodeFusedMaxN = 8192;
 // Two stages wait for vmcnt(0) before each K block, which does not depend
 // on the completion order of the LDS-DMA loads and the scale loads.
 template <int FMT, int WMN, int WNN, int WM, int WN, bool GROUPED, bool W4 = false,
-          bool SW = false, bool SA = false>
+          bool SW = false, bool SA = false, bool SW4 = false>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t st, int splits, int kbps, int gsel = 0) {
   constexpr int BM = WMN * WM, BN = WNN * WN;
   const int64_t NT = (a.N + BN - 1) / BN;
@@ -1285,7 +1326,7 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t st, int splits, int kbps, i
     tiles = (tiles + 7) / 8 * 8;                 // whole rounds over the 8 XCDs
   }
   float* part = splits > 1 ? (float*)a.workspace : nullptr;
-  hipLaunchKernelGGL((gemm_lds_kernel<FMT, WMN, WNN, WM, WN, GROUPED, W4, SW, SA>),
+  hipLaunchKernelGGL((gemm_lds_kernel<FMT, WMN, WNN, WM, WN, GROUPED, W4, SW, SA, SW4>),
                      dim3((unsigned)tiles), dim3(64 * WMN * WNN), 0, st, a.xq, a.xs, a.wq, a.ws,
                      GROUPED ? nullptr : a.bias, a.y, a.M, a.N, a.K, a.seg, a.E, gsel, part,
                      kbps, a.hq, a.hs);
@@ -1369,6 +1410,18 @@ hipError_t launch_lds(const GemmArgs& a, hipStream_t st) {
     const Plan p = plan_dense(a.M, a.N, a.K);
     const bool sa = ue8m0_aligned(a, p.splits, p.kbps);
     if (a.w4) {
+      if (a.K % 128 == 0 && (FMT == 1 || !p.big)) {   // staged MXFP4 weight scales
+        if constexpr (FMT == 1) {
+          if (p.big)
+            return sa ? launch_cfg<FMT, 4, 2, 64, 128, false, true, false, U, true>(a, st, p.splits,
+                                                                                    p.kbps)
+                      : launch_cfg<FMT, 4, 2, 64, 128, false, true, false, false, true>(a, st, p.splits,
+                                                                                    p.kbps);
+        }
+        return sa ? launch_cfg<FMT, 2, 4, 64, 64, false, true, false, U, true>(a, st, p.splits, p.kbps)
+                  : launch_cfg<FMT, 2, 4, 64, 64, false, true, false, false, true>(a, st, p.splits,
+                                                                                 p.kbps);
+      }
       if (p.big)
         return sa ? launch_cfg<FMT, 4, 2, 64, 128, false, true, false, U>(a, st, p.splits, p.kbps)
                   : launch_cfg<FMT, 4, 2, 64, 128, false, true>(a, st, p.splits, p.kbps);
