@@ -815,7 +815,8 @@ constexpr int kDecodeDepth = 2;
 // the activation scales of at most 16 tokens, staged whole (SXL) when they fit
 constexpr int kDecodeXsBytes = 16384;
 
-template <int FMT, bool FUSED, bool W4 = false, bool B32 = false, bool SXL = false>
+template <int FMT, bool FUSED, bool W4 = false, bool B32 = false, bool SXL = false,
+          bool SWL = false>
 __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
     const uint8_t* __restrict__ xq, const void* __restrict__ xs,
     const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ wq,
@@ -827,6 +828,11 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
   // scale per token row per K block, which cost as many requests as the
   // X codes themselves
   __shared__ __attribute__((aligned(16))) uint8_t sxs[SXL ? kDecodeXsBytes : 16];
+  // SWL (MXFP4 weights, K a multiple of 128): the workgroup's 16 rows of E8M0
+  // group scales are one contiguous span of 16 K/32 bytes, copied once
+  // instead of one byte per lane per K block (as many requests as the codes)
+  static_assert(!SWL || W4, "staged weight scales: MXFP4 weights");
+  __shared__ __attribute__((aligned(16))) uint8_t sws[SWL ? kDecodeXsBytes : 16];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
@@ -851,6 +857,12 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
   const int64_t KW = W4 ? K / 2 : K;       // W bytes per row
   const int64_t G32 = K / 32;
   const int64_t GS = (K + 31) / 32;        // B32: scale groups per row
+  if constexpr (SWL) {
+    const int nwords = (int)(min((int64_t)16, N - n0) * G32 / 4);   // K % 128 == 0
+    const uint32_t* src = (const uint32_t*)((const uint8_t*)wsc + n0 * G32);
+    for (int i = threadIdx.x; i < nwords; i += 64 * kDecodeWaves) ((uint32_t*)sws)[i] = src[i];
+    __syncthreads();
+  }
   const int64_t nb32 = n0 >> 5;            // B32: this tile's weight block row
   const uint8_t* wrow = wq + nrow * KW;
   // this lane's X elements of a block: two runs of 16 starting at kx0, kx1
@@ -900,7 +912,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
           const int64_t kw = (int64_t)kb * 64 + g4 * 16;
           if (kw < KW) {
             wa[u] = ld_stream16(wrow + kw);
-            sw4[u] = (int)((const uint8_t*)wsc)[nrow * G32 + (int64_t)kb * 4 + g4];
+            sw4[u] = SWL ? (int)sws[l16 * G32 + (int64_t)kb * 4 + g4]
+                         : (int)((const uint8_t*)wsc)[nrow * G32 + (int64_t)kb * 4 + g4];
           }
         } else {
           const int64_t k = (int64_t)kb * 128 + g4 * 32;
@@ -1490,13 +1503,16 @@ hipError_t launch_decode(const GemmArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((gemm_decode_kernel<FMT, false, false, true>), grid, block, 0, st, a.xq,
                        a.xs, nullptr, (int64_t)0, a.wq, a.ws, a.bias, a.y, (int)a.M, a.N, a.K);
   } else if (a.w4) {
-    if (sxl)
-      hipLaunchKernelGGL((gemm_decode_kernel<FMT, false, true, false, true>), grid, block, 0, st,
-                         a.xq, a.xs, nullptr, (int64_t)0, a.wq, a.ws, a.bias, a.y, (int)a.M, a.N,
-                         a.K);
-    else
-      hipLaunchKernelGGL((gemm_decode_kernel<FMT, false, true>), grid, block, 0, st, a.xq, a.xs,
-                         nullptr, (int64_t)0, a.wq, a.ws, a.bias, a.y, (int)a.M, a.N, a.K);
+    // staged MXFP4 weight scales when 16 rows of them fit and rows are dword-aligned
+    const bool swl = a.K % 128 == 0 && 16 * (a.K / 32) <= kDecodeXsBytes;
+#define BSFP8_DEC4(SX, SW)                                                                      \
+  hipLaunchKernelGGL((gemm_decode_kernel<FMT, false, true, false, SX, SW>), grid, block, 0, st, \
+                     a.xq, a.xs, nullptr, (int64_t)0, a.wq, a.ws, a.bias, a.y, (int)a.M, a.N, a.K)
+    if (sxl && swl) BSFP8_DEC4(true, true);
+    else if (sxl) BSFP8_DEC4(true, false);
+    else if (swl) BSFP8_DEC4(false, true);
+    else BSFP8_DEC4(false, false);
+#undef BSFP8_DEC4
   } else {
     if (sxl)
       hipLaunchKernelGGL((gemm_decode_kernel<FMT, false, false, false, true>), grid, block, 0, st,
