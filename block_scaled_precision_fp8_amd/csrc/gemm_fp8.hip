@@ -822,7 +822,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ wq,
     const void* __restrict__ wsc, const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
     int M, int64_t N, int64_t K) {
-  static_assert(!SXL || (!FUSED && !B32), "staged activation scales: quantized X, 128-wide groups");
+  static_assert(!SXL || !FUSED, "staged activation scales: quantized X");
   __shared__ v4f red[kDecodeWaves][64];
   // SXL: the M x KB activation scales, read once (contiguous) instead of one
   // scale per token row per K block, which cost as many requests as the
@@ -831,7 +831,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
   // SWL (MXFP4 weights, K a multiple of 128): the workgroup's 16 rows of E8M0
   // group scales are one contiguous span of 16 K/32 bytes, copied once
   // instead of one byte per lane per K block (as many requests as the codes)
-  static_assert(!SWL || W4, "staged weight scales: MXFP4 weights");
+  // (B32: the tile's one row of (32, 32)-block scales, GS entries)
+  static_assert(!SWL || W4 || B32, "staged weight scales: MXFP4 or (32, 32) blocks");
   __shared__ __attribute__((aligned(16))) uint8_t sws[SWL ? kDecodeXsBytes : 16];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -843,8 +844,10 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
   const int KB = (int)((K + 127) / 128);
   const int64_t nblk = n0 >> 7;
   constexpr int SBX = FMT == 0 ? 4 : 1;
+  const int64_t GS = (K + 31) / 32;        // B32: scale groups per row
   if constexpr (SXL) {
-    const int nbytes = M * KB * SBX;               // <= kDecodeXsBytes (launcher)
+    // M x KB scales (M x GS with 1 x 32 groups), <= kDecodeXsBytes (launcher)
+    const int nbytes = M * (int)(B32 ? GS : KB) * SBX;
     for (int i = threadIdx.x * 4; i < nbytes; i += 64 * kDecodeWaves * 4) {
       if (i + 4 <= nbytes) {
         *(uint32_t*)(sxs + i) = *(const uint32_t*)((const uint8_t*)xs + i);
@@ -856,14 +859,18 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
   }
   const int64_t KW = W4 ? K / 2 : K;       // W bytes per row
   const int64_t G32 = K / 32;
-  const int64_t GS = (K + 31) / 32;        // B32: scale groups per row
-  if constexpr (SWL) {
+  const int64_t nb32 = n0 >> 5;            // B32: this tile's weight block row
+  if constexpr (SWL && W4) {
     const int nwords = (int)(min((int64_t)16, N - n0) * G32 / 4);   // K % 128 == 0
     const uint32_t* src = (const uint32_t*)((const uint8_t*)wsc + n0 * G32);
     for (int i = threadIdx.x; i < nwords; i += 64 * kDecodeWaves) ((uint32_t*)sws)[i] = src[i];
     __syncthreads();
+  } else if constexpr (SWL && B32) {
+    const int nbytes = (int)GS * SBX;
+    const uint8_t* src = (const uint8_t*)wsc + nb32 * GS * SBX;
+    for (int i = threadIdx.x; i < nbytes; i += 64 * kDecodeWaves) sws[i] = src[i];
+    __syncthreads();
   }
-  const int64_t nb32 = n0 >> 5;            // B32: this tile's weight block row
   const uint8_t* wrow = wq + nrow * KW;
   // this lane's X elements of a block: two runs of 16 starting at kx0, kx1
   const int kx0 = W4 ? 16 * g4 : 32 * g4;
@@ -896,8 +903,18 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
           const int64_t gi = (int64_t)kb * 4 + g;
           const bool ok = kb < KB && gi < GS;
           float w = 0.f, x = 0.f;
-          if (ok) w = load_scale<FMT>(wsc, nb32 * GS + gi);
-          if (ok && mvalid) x = load_scale<FMT>(xs, (int64_t)l16 * GS + gi);
+          if (ok) {
+            if constexpr (SWL)
+              w = FMT == 0 ? ((const float*)sws)[gi] : __int_as_float((int)sws[gi]);
+            else
+              w = load_scale<FMT>(wsc, nb32 * GS + gi);
+          }
+          if (ok && mvalid) {
+            if constexpr (SXL)
+              x = FMT == 0 ? ((const float*)sxs)[l16 * GS + gi] : __int_as_float((int)sxs[l16 * GS + gi]);
+            else
+              x = load_scale<FMT>(xs, (int64_t)l16 * GS + gi);
+          }
           if (FMT == 1) {
             w = ok ? e8m0_f32(__float_as_uint(w)) : 0.f;
             x = (ok && mvalid) ? e8m0_f32(__float_as_uint(x)) : 0.f;
@@ -1500,8 +1517,18 @@ hipError_t launch_decode(const GemmArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((gemm_decode_kernel<FMT, true>), grid, block, 0, st, nullptr, nullptr,
                        a.x_bf16, a.ldx, a.wq, a.ws, a.bias, a.y, (int)a.M, a.N, a.K);
   } else if (a.blk == 32) {
-    hipLaunchKernelGGL((gemm_decode_kernel<FMT, false, false, true>), grid, block, 0, st, a.xq,
-                       a.xs, nullptr, (int64_t)0, a.wq, a.ws, a.bias, a.y, (int)a.M, a.N, a.K);
+    // (32, 32) blocks: the M x K/32 activation scales (M >= 4) and the tile's
+    // row of weight-block scales from LDS
+    const int64_t gbytes = (a.K + 31) / 32 * (a.fmt == 0 ? 4 : 1);
+    const bool sx32 = a.M >= 4 && a.M * gbytes <= kDecodeXsBytes;
+    const bool sw32 = a.M >= 4 && gbytes <= kDecodeXsBytes;   // at M = 1 the copy costs more
+#define BSFP8_DEC32(SX, SW)                                                                     \
+  hipLaunchKernelGGL((gemm_decode_kernel<FMT, false, false, true, SX, SW>), grid, block, 0, st, \
+                     a.xq, a.xs, nullptr, (int64_t)0, a.wq, a.ws, a.bias, a.y, (int)a.M, a.N, a.K)
+    if (sx32 && sw32) BSFP8_DEC32(true, true);
+    else if (sw32) BSFP8_DEC32(false, true);
+    else BSFP8_DEC32(false, false);
+#undef BSFP8_DEC32
   } else if (a.w4) {
     // staged MXFP4 weight scales when 16 rows of them fit and rows are dword-aligned
     const bool swl = a.K % 128 == 0 && 16 * (a.K / 32) <= kDecodeXsBytes;
