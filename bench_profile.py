@@ -29,7 +29,8 @@ import sys
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 GEMM_SOURCE = os.path.join(ROOT, "block_scaled_precision_fp8_amd", "csrc", "gemm_fp8.hip")
-GEMM_KERNEL = "gemm_lds_kernel<0, 4, 2, 64, 128, false, false, false, false>"
+# the dense fp32-scale 256x256 tile (grouped, W4, SiLU-mul off), whatever follows
+GEMM_KERNEL = "gemm_lds_kernel<0, 4, 2, 64, 128, false, false, false,"
 
 
 def per_kernel(path, counter):
