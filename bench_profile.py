@@ -9,8 +9,11 @@ launches, each scaled by true bytes / counter reading of the plain copy
 kernel of N MiB that `bench.py --copy-calib-mib N` runs first; records the
 sha256 of the GEMM source so bench.py only uses it for the same kernel.
 `stats`: the kernel table of a --kernel-trace --stats run.
-`mfma`: MFMA busy share and counted FP8 flops of the large-M GEMM from a
---pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_F8 run.
+`mfma`: MFMA busy share and counted flops of the large-M GEMM from a
+--pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_F8 run
+(--kernel, --mops, --peak and --title select another kernel, other MOPS
+counters -- summed -- and their peak, e.g. the FP8 x MXFP4 tile with
+SQ_INSTS_VALU_MFMA_MOPS_F8,SQ_INSTS_VALU_MFMA_MOPS_F6F4).
 `decode`: HBM bytes per decode-GEMM dispatch over its duration, from the
 FETCH_SIZE run (scaled by the same copy calibration).
 `l1`: what bounds the operand loads of the large-M GEMM, from two --pmc
@@ -98,28 +101,34 @@ def dispatches(path):
 
 
 def mfma(a):
-    """MFMA busy share of SIMD cycles and counted FP8 flops of the large-M GEMM"""
+    """MFMA busy share of SIMD cycles and counted MFMA flops of one kernel"""
     simds, xcds = 256 * 4, 8
-    rows = [d for d in dispatches(a.pmc).values() if GEMM_KERNEL in d["name"]]
+    rows = [d for d in dispatches(a.pmc).values() if a.kernel in d["name"]]
     if not rows:
-        sys.exit("no large-M GEMM dispatches found")
+        sys.exit(f"no dispatches of {a.kernel} found")
+    mops = a.mops.split(",")
     # the CSV sums GRBM_GUI_ACTIVE over the 8 XCDs: one XCD's count is the
     # kernel's active cycles (dividing by the dispatch time gives the clock)
     cyc = [d["GRBM_GUI_ACTIVE"] / xcds for d in rows]
     util = [d["SQ_VALU_MFMA_BUSY_CYCLES"] / (c * simds) for d, c in zip(rows, cyc)]
     ghz = [c / d["ns"] for d, c in zip(rows, cyc)]
-    tf = [d["SQ_INSTS_VALU_MFMA_MOPS_F8"] * 512 / d["ns"] / 1e3 for d in rows]
+    tf = [sum(d.get(c, 0.0) for c in mops) * 512 / d["ns"] / 1e3 for d in rows]
+    per = {c: sum(d.get(c, 0.0) for d in rows) for c in mops}
     lines = [
-        "# MFMA utilisation of the large-M block-scaled GEMM (fp32 scales), Llama-3-8B linears",
+        f"# MFMA utilisation of {a.title}",
         f"# command: {a.cmd}",
-        f"kernel: {GEMM_KERNEL}",
+        f"kernel: {a.kernel}",
         f"dispatches: {len(rows)}",
         "MFMA busy / (GRBM_GUI_ACTIVE per XCD x 1024 SIMDs), mean over dispatches: "
         f"{100 * sum(util) / len(util):.1f}% (min {100 * min(util):.1f}%, max {100 * max(util):.1f}%)",
         f"clock implied by GRBM_GUI_ACTIVE per XCD / dispatch time: {sum(ghz) / len(ghz):.2f} GHz",
-        "FP8 flops counted (SQ_INSTS_VALU_MFMA_MOPS_F8 x 512) / dispatch time, mean: "
-        f"{sum(tf) / len(tf):.0f} TFLOP/s (dense FP8 peak 5000)",
+        f"flops counted ({' + '.join(mops)}) x 512 / dispatch time, mean: "
+        f"{sum(tf) / len(tf):.0f} TFLOP/s (dense peak {a.peak:.0f})",
     ]
+    if len(mops) > 1:
+        tot = sum(per.values()) or 1.0
+        lines.append("share of the counted MOPS: " +
+                     ", ".join(f"{c} {100 * v / tot:.1f}%" for c, v in per.items()))
     with open(a.out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -252,6 +261,10 @@ def main():
     m.add_argument("--pmc", required=True)
     m.add_argument("--cmd", required=True)
     m.add_argument("--out", required=True)
+    m.add_argument("--kernel", default=GEMM_KERNEL)
+    m.add_argument("--mops", default="SQ_INSTS_VALU_MFMA_MOPS_F8")
+    m.add_argument("--peak", type=float, default=5000.0)
+    m.add_argument("--title", default="the large-M block-scaled GEMM (fp32 scales), Llama-3-8B linears")
     d = sub.add_parser("decode")
     d.add_argument("--fetch", required=True)
     d.add_argument("--copy-mib", type=int, required=True)
