@@ -147,7 +147,7 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 size_t fp8_fp4_workspace_bytes(int64_t M, int64_t N, int64_t K);
 int gemm_kind(int64_t M, int64_t N, int64_t K, int* splits);   // a bsfp8_gemm_kind
 size_t linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int blk = 128);
-bool linear_fused(int64_t M, int64_t N);   // fp8_linear quantizes inside the GEMM
+bool linear_fused(int64_t M, int64_t N, int64_t K);   // fp8_linear quantizes inside the GEMM
 size_t grouped_workspace_bytes(int64_t T, int64_t N, int64_t K, int E);
 hipError_t launch_block_gemm(const GemmArgs& a, hipStream_t s);
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t s);

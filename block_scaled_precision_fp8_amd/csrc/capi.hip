@@ -268,7 +268,7 @@ int32_t fp8_linear(const void* x, int64_t ldx, const void* wq, const void* w_sca
   a.bias = (const uint16_t*)bias; a.y = (uint16_t*)y; a.M = M; a.N = N; a.K = K;
   a.fmt = scale_fmt;
   a.blk = blk;
-  if (blk == 128 && linear_fused(M, N)) {
+  if (blk == 128 && linear_fused(M, N, K)) {
     // one launch: the decode kernel quantizes the activations itself
     if (!al16(x)) return BSFP8_EINVAL;
     a.x_bf16 = (const uint16_t*)x; a.ldx = ldx;

@@ -797,7 +797,10 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 // lanes that share its row, to the codes fp8_quant_act writes (the fp32
 // division by the scale done as a multiply by the correctly rounded
 // reciprocal plus one exact correction).  Every workgroup quantizes all of
-// X, so the fused form is used up to kDecodeFusedMaxN outputs only.
+// X, so the re-quantization grows with N K: the fused form is used up to
+// N K = 2^24 and K = 6144 only (measured against the separate quantization
+// launch plus the unfused kernel, which wins from N K = 6144 x 4096 and at
+// K = 7168 with 16 tokens).
 // ------------------------------------------------------------------------
 constexpr int kDecodeWaves = 16;
 constexpr int kDecodeDepth = 2;
@@ -1325,7 +1328,8 @@ BSFP8_INST2(1, 2, 4, 64, 64, false, true, false, true, true)
 // host side
 // ------------------------------------------------------------------------
 constexpr int64_t kDecodeMaxM = 16;
-constexpr int64_t kDecodeFusedMaxN = 8192;
+constexpr int64_t kDecodeFusedMaxNK = int64_t(1) << 24;
+constexpr int64_t kDecodeFusedMaxK = 6144;
 
 // Large-M tile configurations (WAVES_M x WAVES_N waves, wave tile WM x WN,
 // two LDS stages): BM = WM WAVES_M, BN = WN WAVES_N.
@@ -1481,15 +1485,15 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return p.splits > 1 ? (size_t)p.splits * M * N * sizeof(float) : 0;
 }
 
-bool linear_fused(int64_t M, int64_t N) {
-  return M > 0 && M <= kDecodeMaxM && N <= kDecodeFusedMaxN;
+bool linear_fused(int64_t M, int64_t N, int64_t K) {
+  return M > 0 && M <= kDecodeMaxM && K <= kDecodeFusedMaxK && N * K <= kDecodeFusedMaxNK;
 }
 
 size_t linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int blk) {
   if (M <= 0) return 0;
   auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
   if (blk == 32) return up((size_t)M * K) + up((size_t)M * ((K + 31) / 32) * 4);
-  if (linear_fused(M, N)) return 0;   // quantization inside the decode kernel
+  if (linear_fused(M, N, K)) return 0;   // quantization inside the decode kernel
   const int64_t G = (K + 127) / 128;
   return up((size_t)M * K) + up((size_t)M * G * 4) + gemm_workspace_bytes(M, N, K);
 }

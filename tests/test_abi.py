@@ -120,11 +120,16 @@ def test_block_gemm_workspace_too_small():
 
 def test_decode_needs_no_workspace():
     """M <= 16 runs in one launch with no workspace; fp8_linear fuses the
-    activation quantization there up to N = 8192 and stages it above."""
+    activation quantization there up to N K = 2^24 with K <= 6144 and stages
+    it beyond (every workgroup would re-quantize all of X)."""
     for M in (1, 16):
         assert L.workspace_size(L.OP_BLOCK_GEMM, M, 28672, 4096) == 0
-        assert L.workspace_size(L.OP_LINEAR, M, 8192, 4096) == 0
-        assert L.workspace_size(L.OP_LINEAR, M, 8200, 4096) > 0
+        assert L.workspace_size(L.OP_LINEAR, M, 4096, 4096) == 0
+        assert L.workspace_size(L.OP_LINEAR, M, 2728, 6144) == 0
+        assert L.workspace_size(L.OP_LINEAR, M, 4104, 4096) > 0
+        assert L.workspace_size(L.OP_LINEAR, M, 1536, 7168) > 0
+        assert L.workspace_size(L.OP_LINEAR, M, 8192, 4096) > 0
+    assert L.workspace_size(L.OP_LINEAR, 17, 256, 256) > 0
 
 
 def test_linear_argument_checks():
