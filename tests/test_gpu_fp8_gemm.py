@@ -171,7 +171,10 @@ def test_linear_fused_quant_every_bf16_pattern(fmt):
 
 @pytest.mark.parametrize("fmt", [0, 1])
 @pytest.mark.parametrize("M,N,K", [(1, 256, 256), (16, 520, 384), (200, 512, 1040),
-                                   (1, 8200, 256), (5, 264, 4112)])
+                                   (1, 8200, 256), (5, 264, 4112),
+                                   # either side of the fused-quantization bound
+                                   # (N K <= 2^24, K <= 6144)
+                                   (1, 2728, 6144), (16, 4104, 4096), (4, 1536, 7168)])
 def test_linear_matches_two_calls(M, N, K, fmt):
     import torch
     from block_scaled_precision_fp8_amd import lib as L
