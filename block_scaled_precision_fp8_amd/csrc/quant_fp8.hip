@@ -21,6 +21,7 @@ namespace bsfp8 {
 namespace detail {
 
 constexpr int kActUnroll = 4;   // loads in flight per lane
+constexpr int kActRows = 2;     // row sets per workgroup
 
 struct Unpacked { float f[8]; };
 
@@ -57,8 +58,10 @@ __device__ __forceinline__ uint2 encode8(const Unpacked& u, float amax, float* s
 // One 16-lane quarter-wave owns 128 consecutive values of one row: each lane
 // holds eight consecutive bf16 values (one 16-byte load).  A workgroup of 16
 // quarters covers QG consecutive 128-value chunks of RQ rows (QG * RQ = 16)
-// and walks ROWS such row sets (8, or 2 for small activations so that more
-// workgroups share the work), with up to kActUnroll loads issued before use.
+// and walks ROWS such row sets (kActRows = 2: many small workgroups keep more
+// loads in flight across the chip than 8 row sets did -- 12-14% faster at
+// 8192 x 4096 and 2048 x 14336 with fp32 scales, within 3% either way with
+// UE8M0), with up to kActUnroll loads issued before use.
 // GK is the group width: 128 (the quarter-wave is one group) or 32 (four
 // lanes per group, for (32, 32) weight blocks); G counts 128-value chunks,
 // GS the stored scales per row.
@@ -208,21 +211,12 @@ hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx
   int qg_log2 = 0;
   while ((1 << qg_log2) < G && qg_log2 < 4) ++qg_log2;
   const int QG = 1 << qg_log2, RQ = 16 >> qg_log2;
-  // small activations: two rows per quarter-wave, four times the workgroups
-  const bool few = M * G <= 65536;
-  const int rows = few ? 2 : 8;
-  int64_t gy = (M + RQ * rows - 1) / (RQ * rows);
+  int64_t gy = (M + RQ * kActRows - 1) / (RQ * kActRows);
   if (gy > 65535) gy = 65535;
   dim3 grid((G + QG - 1) / QG, (unsigned)gy);
 #define BSFP8_ACT(F, S, GK)                                                                        \
-  do {                                                                                             \
-    if (few)                                                                                       \
-      hipLaunchKernelGGL((quant_act_kernel<F, S, GK, 2>), grid, dim3(256), 0, s, x, (int)M,      \
-                         (int)K, ldx, G, qg_log2, xq, scale, static_scale);                       \
-    else                                                                                           \
-      hipLaunchKernelGGL((quant_act_kernel<F, S, GK, 8>), grid, dim3(256), 0, s, x, (int)M,      \
-                         (int)K, ldx, G, qg_log2, xq, scale, static_scale);                       \
-  } while (0)
+  hipLaunchKernelGGL((quant_act_kernel<F, S, GK, kActRows>), grid, dim3(256), 0, s, x, (int)M,  \
+                     (int)K, ldx, G, qg_log2, xq, scale, static_scale)
   if (static_scale) {
     if (fmt == 0) BSFP8_ACT(0, true, 128); else BSFP8_ACT(1, true, 128);
   } else if (group_k == 32) {
