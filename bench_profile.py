@@ -17,7 +17,7 @@ SQ_INSTS_VALU_MFMA_MOPS_F8,SQ_INSTS_VALU_MFMA_MOPS_F6F4).
 `decode`: HBM bytes per decode-GEMM dispatch over its duration, from the
 FETCH_SIZE run (scaled by the same copy calibration).
 `l1`: what bounds the operand loads of the large-M GEMM, from two --pmc
-runs: texture-data stalls on L1, L1 pending and tag-conflict stalls, address
+runs (a third, TCC_HIT_sum TCC_MISS_sum, adds the L2 hit rate): texture-data stalls on L1, L1 pending and tag-conflict stalls, address
 stalls, and the L1-to-L2 request count and average latency, with the
 concurrency they imply (Little's law).
 `summary`: the text form of one bench.py JSON line.
@@ -204,6 +204,15 @@ def l1(a):
         f"bytes per CU cycle the 256x256 tile needs at the full FP8 MFMA rate "
         f"(4 SIMDs x 2048 flop/cycle / 256 flop/byte): 32.0",
     ]
+    if a.pmc3:
+        # L2 hits and misses of the same launches (reads and the epilogue's
+        # writes): the misses are the requests whose operand lines no other
+        # concurrent tile has brought into this XCD's L2 yet
+        r3 = [d for d in dispatches(a.pmc3).values() if GEMM_KERNEL in d["name"]]
+        hit = sum(d["TCC_HIT_sum"] for d in r3)
+        miss = sum(d["TCC_MISS_sum"] for d in r3)
+        lines.append(f"L2 hit rate (TCC_HIT / (TCC_HIT + TCC_MISS)) over {len(r3)} launches: "
+                     f"{100 * hit / max(hit + miss, 1.0):.1f}%")
     with open(a.out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -273,6 +282,7 @@ def main():
     l = sub.add_parser("l1")
     l.add_argument("--pmc1", required=True)
     l.add_argument("--pmc2", required=True)
+    l.add_argument("--pmc3", default=None, help="optional TCC_HIT_sum TCC_MISS_sum run")
     l.add_argument("--cmd", required=True)
     l.add_argument("--out", required=True)
     b = sub.add_parser("summary")
