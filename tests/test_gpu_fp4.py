@@ -36,6 +36,8 @@ def _quant_dev(x_bits, g=None):
 @pytest.mark.parametrize("R,K,sigma,seed", [
     (4, 64, 1.0, 0), (33, 12288, 1.0, 1), (1000, 1024, 0.015, 2), (7, 28672, 1.0, 3),
     (1, 32, 1.0, 4), (129, 96, 0.015, 5),
+    # decode-sized activations (one or two tokens of the MLP's K)
+    (1, 28672, 1.0, 6), (2, 12288, 0.015, 7), (2, 32768, 1.0, 8), (1, 65568, 1.0, 9),
 ])
 def test_fp4_quant_parity(R, K, sigma, seed):
     say(f"fp4 quant R={R} K={K}")
