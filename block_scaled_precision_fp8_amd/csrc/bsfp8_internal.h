@@ -81,12 +81,17 @@ __device__ __forceinline__ uint32_t act_encode4(float a, float b, float c, float
   return e4m3x4(ldexpf(a, -e), ldexpf(b, -e), ldexpf(c, -e), ldexpf(d, -e));
 }
 
+constexpr float kMinNormal = 0x1p-126f;   // smallest normal fp32
+
 // fl32(x / s) from r = fl32(1 / s) in three operations (Markstein's
 // correction step: q = RN(x r), the residual x - q s is exact with an FMA,
 // and RN(q + residual r) is the correctly rounded quotient when r is the
-// correctly rounded reciprocal and no intermediate underflows).  Quotients
-// small enough to underflow are far below the smallest E4M3 subnormal and
-// encode to a signed zero either way, so the codes equal those of x / s.
+// correctly rounded reciprocal and no intermediate underflows).  Valid for a
+// NORMAL scale s only: a subnormal s (group amax below 448 * 2^-126) can
+// make 1 / s overflow (s < 2^-128) and the residual round, so callers divide
+// directly there.  With s normal, quotients small enough to underflow are
+// far below the smallest E4M3 subnormal and encode to a signed zero either
+// way, so the codes equal those of x / s.
 __device__ __forceinline__ float div_by_rcp(float x, float s, float r) {
   const float q = x * r;
   const float res = fmaf(-q, s, x);
@@ -130,9 +135,12 @@ struct GemmArgs {
   int E;
   void* workspace;
   size_t workspace_bytes;
-  // fused act quant (fp8_linear decode path): bf16 input, else null
+  // fused act quant (fp8_linear decode path): bf16 input, else null; xstat
+  // is the static scheme's calibrated scale (device fp32 or E8M0 byte), or
+  // null for dynamic 1 x 128 groups
   const uint16_t* x_bf16;
   int64_t ldx;
+  const void* xstat;
   // MXFP4 weights: wq (N, K/2) E2M1 codes, ws (N, K/32) E8M0 bytes
   bool w4;
   // grouped gate/up GEMM with the SiLU-mul requant epilogue: h codes
@@ -152,6 +160,19 @@ size_t grouped_workspace_bytes(int64_t T, int64_t N, int64_t K, int E);
 hipError_t launch_block_gemm(const GemmArgs& a, hipStream_t s);
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t s);
 hipError_t launch_grouped_silu_mul_quant(const GemmArgs& a, hipStream_t s);
+
+// C-ABI helpers shared by the entry points of capi.hip and noalloc.hip:
+// the once-per-device gfx950 / stream-device check, and fp8_linear's
+// host-only argument checks (*need: its workspace bytes) and launches.
+int32_t check_device(void* stream);
+int32_t linear_checks(const void* x, int64_t ldx, const void* wq, const void* w_scale_inv,
+                      const void* bias, const void* y, int64_t M, int64_t N, int64_t K,
+                      int32_t block_n, int32_t block_k, int32_t act_scheme, int32_t scale_fmt,
+                      const void* act_scale, size_t* need);
+int32_t linear_launch(const void* x, int64_t ldx, const void* wq, const void* w_scale_inv,
+                      const void* bias, void* y, int64_t M, int64_t N, int64_t K, int32_t blk,
+                      int32_t act_scheme, int32_t scale_fmt, const void* act_scale,
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 size_t fp4_quant_workspace_bytes(int64_t R, int64_t K);
 size_t fp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);

@@ -21,32 +21,12 @@ bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool fits_i32(int64_t v) { return v >= 0 && v <= 0x7fffffffLL; }
 bool valid_fmt(int32_t f) { return f == BSFP8_SCALE_FLOAT || f == BSFP8_SCALE_UE8M0; }
 
-// block sizes: the pages allow any positive pair ([FG-FP8] §四); only 128
-// is provided here.
-// Supported weight blocks: 128 x 128, and 32 x 32 (with 1 x 32 act groups).
+// Block sizes: the pages allow any positive pair ([FG-FP8] §四); 128 x 128
+// and 32 x 32 (with 1 x 32 act groups, §九) are provided, other positive
+// sizes return ENOTSUP.
 int32_t check_blocks(int32_t bn, int32_t bk) {
   if (bn <= 0 || bk <= 0) return BSFP8_EINVAL;
   if (!((bn == 128 && bk == 128) || (bn == 32 && bk == 32))) return BSFP8_ENOTSUP;
-  return BSFP8_OK;
-}
-
-int32_t check_device(void* stream) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return BSFP8_EHIP;
-  if (dev < 0 || dev >= kMaxDevices) return BSFP8_ENOTSUP;
-  int st = g_arch_state[dev].load(std::memory_order_relaxed);
-  if (st == 0) {
-    hipDeviceProp_t prop;
-    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return BSFP8_EHIP;
-    st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
-    g_arch_state[dev].store(st, std::memory_order_relaxed);
-  }
-  if (st != 1) return BSFP8_ENOTSUP;
-  if (stream != nullptr) {
-    hipDevice_t sdev = -1;
-    if (hipStreamGetDevice((hipStream_t)stream, &sdev) != hipSuccess) return BSFP8_EHIP;
-    if (sdev != dev) return BSFP8_ENOTSUP;
-  }
   return BSFP8_OK;
 }
 
@@ -77,7 +57,92 @@ int32_t check_gemm(const void* xq, const void* xs, const void* wq, const void* w
   return BSFP8_OK;
 }
 
+
 }  // namespace
+
+namespace bsfp8 {
+
+int32_t check_device(void* stream) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return BSFP8_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return BSFP8_ENOTSUP;
+  int st = g_arch_state[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return BSFP8_EHIP;
+    st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_arch_state[dev].store(st, std::memory_order_relaxed);
+  }
+  if (st != 1) return BSFP8_ENOTSUP;
+  if (stream != nullptr) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice((hipStream_t)stream, &sdev) != hipSuccess) return BSFP8_EHIP;
+    if (sdev != dev) return BSFP8_ENOTSUP;
+  }
+  return BSFP8_OK;
+}
+
+// ---- fp8_linear: host-only argument checks, then the launches
+
+// *need: the workspace bytes the call takes
+int32_t linear_checks(const void* x, int64_t ldx, const void* wq, const void* w_scale_inv,
+                      const void* bias, const void* y, int64_t M, int64_t N, int64_t K,
+                      int32_t block_n, int32_t block_k, int32_t act_scheme, int32_t scale_fmt,
+                      const void* act_scale, size_t* need) {
+  *need = 0;
+  if (act_scheme != BSFP8_ACT_DYNAMIC && act_scheme != BSFP8_ACT_STATIC) return BSFP8_EINVAL;
+  // the staged activations stand in for xq / x_scale in the operand checks
+  static const uint8_t dummy[16] __attribute__((aligned(16))) = {0};
+  int32_t r = check_gemm(x, dummy, wq, w_scale_inv, bias, y, M, N, K, block_n, block_k,
+                         scale_fmt);
+  if (r != BSFP8_OK) return r;
+  const bool stat = act_scheme == BSFP8_ACT_STATIC;
+  if (stat && block_k != 128) return BSFP8_ENOTSUP;   // as fp8_quant_act
+  if (M == 0) return BSFP8_OK;
+  if (stat && (!act_scale || (scale_fmt == BSFP8_SCALE_FLOAT && ((uintptr_t)act_scale & 3u))))
+    return BSFP8_EINVAL;
+  if (ldx < K || ldx % 8 != 0) return BSFP8_EINVAL;
+  const int blk = block_k;                  // 128, or 32 for (32, 32) blocks
+  if (!fits_i32(M * ((K + blk - 1) / blk))) return BSFP8_EINVAL;
+  *need = linear_workspace_bytes(M, N, K, blk);
+  return BSFP8_OK;
+}
+
+// after the checks and the device check: quantization (fused into the
+// decode kernel, or staged in the workspace), then the GEMM
+int32_t linear_launch(const void* x, int64_t ldx, const void* wq, const void* w_scale_inv,
+                      const void* bias, void* y, int64_t M, int64_t N, int64_t K, int32_t blk,
+                      int32_t act_scheme, int32_t scale_fmt, const void* act_scale,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  const bool stat = act_scheme == BSFP8_ACT_STATIC;
+  hipStream_t st = (hipStream_t)stream;
+  GemmArgs a{};
+  a.wq = (const uint8_t*)wq; a.ws = w_scale_inv;
+  a.bias = (const uint16_t*)bias; a.y = (uint16_t*)y; a.M = M; a.N = N; a.K = K;
+  a.fmt = scale_fmt;
+  a.blk = blk;
+  if (blk == 128 && linear_fused(M, N, K)) {
+    // one launch: the decode kernel quantizes the activations itself
+    a.x_bf16 = (const uint16_t*)x; a.ldx = ldx;
+    a.xstat = stat ? act_scale : nullptr;
+    return hip_status(launch_block_gemm(a, st));
+  }
+  // workspace: [xq M*K][x_scale M*G*4][gemm workspace], 256-byte aligned parts
+  const int64_t G = (K + blk - 1) / blk;
+  auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  uint8_t* ws = (uint8_t*)workspace;
+  uint8_t* xq = ws;
+  void* xs = ws + up((size_t)M * K);
+  void* gw = ws + up((size_t)M * K) + up((size_t)M * G * 4);
+  hipError_t e = launch_quant_act((const uint16_t*)x, M, K, ldx, scale_fmt, xq, xs, st,
+                                  stat ? act_scale : nullptr, blk);
+  if (e != hipSuccess) return BSFP8_EHIP;
+  a.xq = xq; a.xs = xs; a.workspace = gw;
+  a.workspace_bytes = workspace_bytes - (size_t)((uint8_t*)gw - ws);
+  return hip_status(launch_block_gemm(a, st));
+}
+
+}  // namespace bsfp8
 
 extern "C" {
 
@@ -244,49 +309,19 @@ int32_t fp8_block_gemm(const void* xq, const void* x_scale, const void* wq,
 
 int32_t fp8_linear(const void* x, int64_t ldx, const void* wq, const void* w_scale_inv,
                    const void* bias, void* y, int64_t M, int64_t N, int64_t K, int32_t block_n,
-                   int32_t block_k, int32_t act_scheme, int32_t scale_fmt, void* workspace,
-                   size_t workspace_bytes, void* stream) {
-  if (act_scheme != BSFP8_ACT_DYNAMIC && act_scheme != BSFP8_ACT_STATIC) return BSFP8_EINVAL;
-  // the staged activations stand in for xq / x_scale in the operand checks
-  static const uint8_t dummy[16] __attribute__((aligned(16))) = {0};
-  int32_t r = check_gemm(x, dummy, wq, w_scale_inv, bias, y, M, N, K, block_n, block_k,
-                         scale_fmt);
-  if (r != BSFP8_OK) return r;
-  if (act_scheme == BSFP8_ACT_STATIC) return BSFP8_ENOTSUP;
-  if (M == 0) return BSFP8_OK;
-  if (ldx < K || ldx % 8 != 0) return BSFP8_EINVAL;
-  const int blk = block_k;                  // 128, or 32 for (32, 32) blocks
-  if (!fits_i32(M * ((K + blk - 1) / blk))) return BSFP8_EINVAL;
-  const size_t need = linear_workspace_bytes(M, N, K, blk);
+                   int32_t block_k, int32_t act_scheme, int32_t scale_fmt,
+                   const void* act_scale, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  size_t need = 0;
+  int32_t r = linear_checks(x, ldx, wq, w_scale_inv, bias, y, M, N, K, block_n, block_k,
+                            act_scheme, scale_fmt, act_scale, &need);
+  if (r != BSFP8_OK || M == 0) return r;
   if (workspace_bytes < need) return BSFP8_ENOSPC;
   if (need && (!workspace || !al16(workspace))) return BSFP8_EINVAL;
   r = check_device(stream);
   if (r != BSFP8_OK) return r;
-  hipStream_t st = (hipStream_t)stream;
-  GemmArgs a{};
-  a.wq = (const uint8_t*)wq; a.ws = w_scale_inv;
-  a.bias = (const uint16_t*)bias; a.y = (uint16_t*)y; a.M = M; a.N = N; a.K = K;
-  a.fmt = scale_fmt;
-  a.blk = blk;
-  if (blk == 128 && linear_fused(M, N, K)) {
-    // one launch: the decode kernel quantizes the activations itself
-    if (!al16(x)) return BSFP8_EINVAL;
-    a.x_bf16 = (const uint16_t*)x; a.ldx = ldx;
-    return hip_status(launch_block_gemm(a, st));
-  }
-  // workspace: [xq M*K][x_scale M*G*4][gemm workspace], 256-byte aligned parts
-  const int64_t G = (K + blk - 1) / blk;
-  auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
-  uint8_t* ws = (uint8_t*)workspace;
-  uint8_t* xq = ws;
-  void* xs = ws + up((size_t)M * K);
-  void* gw = ws + up((size_t)M * K) + up((size_t)M * G * 4);
-  hipError_t e = launch_quant_act((const uint16_t*)x, M, K, ldx, scale_fmt, xq, xs, st, nullptr,
-                                  blk);
-  if (e != hipSuccess) return BSFP8_EHIP;
-  a.xq = xq; a.xs = xs; a.workspace = gw;
-  a.workspace_bytes = workspace_bytes - (size_t)((uint8_t*)gw - ws);
-  return hip_status(launch_block_gemm(a, st));
+  return linear_launch(x, ldx, wq, w_scale_inv, bias, y, M, N, K, block_k, act_scheme,
+                       scale_fmt, act_scale, workspace, workspace_bytes, stream);
 }
 
 int32_t fp8_grouped_gemm(const void* xq, const void* x_scale, const void* wq,
@@ -330,6 +365,9 @@ int32_t fp8_grouped_gemm_silu_mul_quant(const void* xq, const void* x_scale, con
   if (!h_scale || ((uintptr_t)h_scale & 3u)) return BSFP8_EINVAL;
   if (h_bf16 && !al16(h_bf16)) return BSFP8_EINVAL;
   if (!fits_i32(((T + 127) / 128 + E) * (I / 128))) return BSFP8_EINVAL;
+  // a gate/up tile addresses rows of both halves of one expert's weight
+  // through one buffer resource with 32-bit byte offsets
+  if (2 * I * K > 0x7fffffffLL) return BSFP8_ENOTSUP;
   r = check_device(stream);
   if (r != BSFP8_OK) return r;
   GemmArgs a{};

@@ -824,7 +824,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
     const uint8_t* __restrict__ xq, const void* __restrict__ xs,
     const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ wq,
     const void* __restrict__ wsc, const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
-    int M, int64_t N, int64_t K) {
+    int M, int64_t N, int64_t K, const void* __restrict__ xstat) {
   static_assert(!SXL || !FUSED, "staged activation scales: quantized X");
   __shared__ v4f red[kDecodeWaves][64];
   // SXL: the M x KB activation scales, read once (contiguous) instead of one
@@ -983,18 +983,35 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
           f[8 * i + 4] = bf16_lo(v[i].z); f[8 * i + 5] = bf16_hi(v[i].z);
           f[8 * i + 6] = bf16_lo(v[i].w); f[8 * i + 7] = bf16_hi(v[i].w);
         }
-        float amax = 0.0f;
+        float s = 0.0f;
+        int e = 0;
+        if (xstat) {
+          // static scheme: the one calibrated per-tensor scale
+          if (FMT == 0) s = *(const float*)xstat;
+          else e = (int)*(const uint8_t*)xstat - 127;
+        } else {
+          float amax = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(f[i]));
-        amax = fmaxf(amax, __shfl_xor(amax, 16));
-        amax = fmaxf(amax, __shfl_xor(amax, 32));
-        const float s = FMT == 0 ? act_scale_f32(amax) : 0.0f;
-        const float r = FMT == 0 ? 1.0f / s : 0.0f;
-        const int e = FMT == 0 ? 0 : ue8m0_exp(amax);
+          for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(f[i]));
+          amax = fmaxf(amax, __shfl_xor(amax, 16));
+          amax = fmaxf(amax, __shfl_xor(amax, 32));
+          if (FMT == 0) s = act_scale_f32(amax);
+          else e = ue8m0_exp(amax);
+        }
+        if (FMT == 0 && (xstat || !(s >= kMinNormal))) {
+          // a subnormal scale (1 / s can overflow and the residual of the
+          // reciprocal form can round) or a static one (x / s is not bounded
+          // by 448 and may overflow): divide directly
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          bx[i] = (int)act_encode4_rcp<FMT>(f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3], s,
-                                            r, e);
+          for (int i = 0; i < 8; ++i)
+            bx[i] = (int)act_encode4<FMT>(f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3], s, e);
+        } else {
+          const float r = FMT == 0 ? 1.0f / s : 0.0f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            bx[i] = (int)act_encode4_rcp<FMT>(f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3],
+                                              s, r, e);
+        }
         sa = FMT == 0 ? s : __int_as_float(e + 127);
       } else {
         sa = sx[u < XD ? u : 0];
@@ -1519,7 +1536,7 @@ hipError_t launch_decode(const GemmArgs& a, hipStream_t st) {
   const bool sxl = a.M >= 4 && a.M * ((a.K + 127) / 128) * (a.fmt == 0 ? 4 : 1) <= kDecodeXsBytes;
   if (a.x_bf16) {
     hipLaunchKernelGGL((gemm_decode_kernel<FMT, true>), grid, block, 0, st, nullptr, nullptr,
-                       a.x_bf16, a.ldx, a.wq, a.ws, a.bias, a.y, (int)a.M, a.N, a.K);
+                       a.x_bf16, a.ldx, a.wq, a.ws, a.bias, a.y, (int)a.M, a.N, a.K, a.xstat);
   } else if (a.blk == 32) {
     // (32, 32) blocks: the M x K/32 activation scales (M >= 4) and the tile's
     // row of weight-block scales from LDS
@@ -1528,7 +1545,8 @@ hipError_t launch_decode(const GemmArgs& a, hipStream_t st) {
     const bool sw32 = a.M >= 4 && gbytes <= kDecodeXsBytes;   // at M = 1 the copy costs more
 #define BSFP8_DEC32(SX, SW)                                                                     \
   hipLaunchKernelGGL((gemm_decode_kernel<FMT, false, false, true, SX, SW>), grid, block, 0, st, \
-                     a.xq, a.xs, nullptr, (int64_t)0, a.wq, a.ws, a.bias, a.y, (int)a.M, a.N, a.K)
+                     a.xq, a.xs, nullptr, (int64_t)0, a.wq, a.ws, a.bias, a.y, (int)a.M, a.N, a.K, \
+                     nullptr)
     if (sx32 && sw32) BSFP8_DEC32(true, true);
     else if (sw32) BSFP8_DEC32(false, true);
     else BSFP8_DEC32(false, false);
@@ -1538,7 +1556,8 @@ hipError_t launch_decode(const GemmArgs& a, hipStream_t st) {
     const bool swl = a.K % 128 == 0 && 16 * (a.K / 32) <= kDecodeXsBytes;
 #define BSFP8_DEC4(SX, SW)                                                                      \
   hipLaunchKernelGGL((gemm_decode_kernel<FMT, false, true, false, SX, SW>), grid, block, 0, st, \
-                     a.xq, a.xs, nullptr, (int64_t)0, a.wq, a.ws, a.bias, a.y, (int)a.M, a.N, a.K)
+                     a.xq, a.xs, nullptr, (int64_t)0, a.wq, a.ws, a.bias, a.y, (int)a.M, a.N, a.K, \
+                     nullptr)
     if (sxl && swl) BSFP8_DEC4(true, true);
     else if (sxl) BSFP8_DEC4(true, false);
     else if (swl) BSFP8_DEC4(false, true);
@@ -1548,10 +1567,10 @@ hipError_t launch_decode(const GemmArgs& a, hipStream_t st) {
     if (sxl)
       hipLaunchKernelGGL((gemm_decode_kernel<FMT, false, false, false, true>), grid, block, 0, st,
                          a.xq, a.xs, nullptr, (int64_t)0, a.wq, a.ws, a.bias, a.y, (int)a.M, a.N,
-                         a.K);
+                         a.K, nullptr);
     else
       hipLaunchKernelGGL((gemm_decode_kernel<FMT, false>), grid, block, 0, st, a.xq, a.xs, nullptr,
-                         (int64_t)0, a.wq, a.ws, a.bias, a.y, (int)a.M, a.N, a.K);
+                         (int64_t)0, a.wq, a.ws, a.bias, a.y, (int)a.M, a.N, a.K, nullptr);
   }
   return hipGetLastError();
 }

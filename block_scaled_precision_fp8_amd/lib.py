@@ -58,7 +58,7 @@ _SIGS = {
     "fp8_block_gemm": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32,
                               _P, _SZ, _P]),
     "fp8_linear": (_I32, [_P, _I64, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _I32,
-                          _P, _SZ, _P]),
+                          _P, _P, _SZ, _P]),
     "fp8_grouped_gemm": (_I32, [_P, _P, _P, _P, _P, _I32, _P, _I64, _I64, _I64, _I32, _I32,
                                 _I32, _P, _SZ, _P]),
     "fp4_quant": (_I32, [_P, _I64, _I64, _I32, _P, _P, _P, _P, _SZ, _P]),
@@ -207,14 +207,18 @@ def fp8_block_gemm(xq, x_scale, wq, w_scale_inv, y, bias=None, block_n=128, bloc
 
 
 def fp8_linear(x, wq, w_scale_inv, y, bias=None, block_n=128, block_k=128,
-               act_scheme=ACT_DYNAMIC, scale_fmt=SCALE_FLOAT, workspace=None, stream=None):
+               act_scheme=ACT_DYNAMIC, scale_fmt=SCALE_FLOAT, act_scale=None, workspace=None,
+               stream=None):
+    """act_scale: device tensor holding the static scheme's calibrated scale
+    (fp32, or one E8M0 byte); None for the dynamic scheme."""
     M = x.shape[0]
     N, K = wq.shape
     ws, wsb = _workspace(OP_LINEAR_B32 if block_k == 32 else OP_LINEAR, M, N, K, 0, workspace,
                          x.device)
     _check("fp8_linear", load().fp8_linear(
         _ptr(x), x.stride(0), _ptr(wq), _ptr(w_scale_inv), _ptr(bias), _ptr(y), M, N, K,
-        block_n, block_k, act_scheme, scale_fmt, _ptr(ws), wsb, _stream(stream)))
+        block_n, block_k, act_scheme, scale_fmt, _ptr(act_scale), _ptr(ws), wsb,
+        _stream(stream)))
 
 
 def fp8_grouped_gemm(xq, x_scale, wq, w_scale_inv, seg_offsets, y, block_n=128, block_k=128,

@@ -59,9 +59,12 @@ typedef enum {
    as float8_e8m0fnu bytes. */
 typedef enum { BSFP8_SCALE_FLOAT = 0, BSFP8_SCALE_UE8M0 = 1 } bsfp8_scale_fmt;
 
-/* activation_scheme: [FG-FP8] §四 allows "dynamic" or "static"; the static
-   scheme is served by a separate kernel path on the pages (§6.1, §6.3) and is
-   not provided here (ENOTSUP). */
+/* activation_scheme: [FG-FP8] §四 allows "dynamic" or "static" (the pages
+   keep static on a separate kernel path, §6.1, §6.3, and give no formula).
+   Static here is one calibrated per-tensor scale supplied by the caller:
+   fp8_quant_act (in x_scale[0]) and fp8_linear (through act_scale) take it
+   with 128 x 128 blocks; the other entry points consume quantized operands
+   and do not depend on the scheme. */
 typedef enum { BSFP8_ACT_DYNAMIC = 0, BSFP8_ACT_STATIC = 1 } bsfp8_act_scheme;
 
 /* Operation ids for bsfp8_workspace_size. */
@@ -186,14 +189,23 @@ BSFP8_API int32_t fp8_block_gemm(const void* xq, const void* x_scale, const void
  * points in sequence.  For small M the quantization runs inside the GEMM
  * launch; otherwise the quantized activations are staged in `workspace`.
  *
- *   x      bf16 [M][ldx];  other arguments as above.
- *   workspace  >= bsfp8_workspace_size(BSFP8_OP_LINEAR, M, N, K, 0) bytes.
+ *   x          bf16 [M][ldx];  other arguments as above.
+ *   act_scheme BSFP8_ACT_DYNAMIC (act_scale ignored, may be NULL) or
+ *              BSFP8_ACT_STATIC: act_scale is a DEVICE pointer to the
+ *              calibrated per-tensor scale (fp32 s > 0, 4-byte aligned, or
+ *              the E8M0 byte), read-only; the result equals fp8_quant_act
+ *              with the static scheme and that scale, then fp8_block_gemm.
+ *              STATIC takes 128 x 128 blocks only (ENOTSUP otherwise);
+ *              a NULL act_scale is EINVAL.
+ *   workspace  >= bsfp8_workspace_size(BSFP8_OP_LINEAR, M, N, K, 0) bytes
+ *              (the same for both schemes).
  */
 BSFP8_API int32_t fp8_linear(const void* x, int64_t ldx, const void* wq,
                    const void* w_scale_inv, const void* bias, void* y,
                    int64_t M, int64_t N, int64_t K, int32_t block_n,
                    int32_t block_k, int32_t act_scheme, int32_t scale_fmt,
-                   void* workspace, size_t workspace_bytes, void* stream);
+                   const void* act_scale, void* workspace, size_t workspace_bytes,
+                   void* stream);
 
 /*
  * fp8_grouped_gemm -- MoE expert GEMM over contiguous per-expert row
@@ -240,7 +252,8 @@ BSFP8_API int32_t fp8_grouped_gemm(const void* xq, const void* x_scale, const vo
  *   I            intermediate size, a positive multiple of 128.
  * No workspace.  Errors: those of fp8_grouped_gemm with N = 2I; EINVAL for
  * I <= 0 or I % 128 != 0, a null or misaligned h_scale (4 bytes) or a
- * misaligned h_bf16 (16 bytes).
+ * misaligned h_bf16 (16 bytes); ENOTSUP when one expert's weight (2 I K
+ * bytes) exceeds 2^31 - 1 bytes.
  */
 BSFP8_API int32_t fp8_grouped_gemm_silu_mul_quant(const void* xq, const void* x_scale,
                                         const void* wq, const void* w_scale_inv,

@@ -135,14 +135,26 @@ def test_decode_needs_no_workspace():
 def test_linear_argument_checks():
     lib = L.load()
     f = lib.fp8_linear
-    assert f(FAKE, 256, FAKE, FAKE, None, FAKE, 16, 256, 256, 128, 128, 1, 0, FAKE, 1 << 20,
-             None) == L.ENOTSUP
-    assert f(FAKE, 128, FAKE, FAKE, None, FAKE, 16, 256, 256, 128, 128, 0, 0, FAKE, 1 << 20,
-             None) == L.EINVAL
+    # static scheme: a calibrated scale is required (device pointer; fp32
+    # scales 4-byte aligned), and it takes 128 x 128 blocks only
+    assert f(FAKE, 256, FAKE, FAKE, None, FAKE, 16, 256, 256, 128, 128, 1, 0, None, FAKE,
+             1 << 20, None) == L.EINVAL
+    assert f(FAKE, 256, FAKE, FAKE, None, FAKE, 16, 256, 256, 128, 128, 1, 0, FAKE + 2, FAKE,
+             1 << 20, None) == L.EINVAL
+    assert f(FAKE, 256, FAKE, FAKE, None, FAKE, 16, 256, 256, 32, 32, 1, 0, FAKE, FAKE,
+             1 << 20, None) == L.ENOTSUP
+    assert f(FAKE, 256, FAKE, FAKE, None, FAKE, 16, 256, 256, 128, 128, 2, 0, FAKE, FAKE,
+             1 << 20, None) == L.EINVAL
+    assert f(FAKE, 256, FAKE, FAKE, None, FAKE, 0, 256, 256, 128, 128, 1, 0, None, FAKE,
+             1 << 20, None) == L.OK
+    assert f(FAKE, 128, FAKE, FAKE, None, FAKE, 16, 256, 256, 128, 128, 0, 0, None, FAKE,
+             1 << 20, None) == L.EINVAL
     need = L.workspace_size(L.OP_LINEAR, 64, 256, 256)
     assert need > 0
-    assert f(FAKE, 256, FAKE, FAKE, None, FAKE, 64, 256, 256, 128, 128, 0, 0, FAKE, need - 1,
-             None) == L.ENOSPC
+    assert f(FAKE, 256, FAKE, FAKE, None, FAKE, 64, 256, 256, 128, 128, 0, 0, None, FAKE,
+             need - 1, None) == L.ENOSPC
+    assert f(FAKE, 256, FAKE, FAKE, None, FAKE, 64, 256, 256, 128, 128, 1, 1, FAKE + 1, FAKE,
+             need - 1, None) == L.ENOSPC
 
 
 def test_grouped_argument_checks():
@@ -254,6 +266,12 @@ def test_silu_mul_quant_argument_checks():
                        (12, 2, L.EINVAL), (11, 2**22 + 16, L.ENOTSUP), (9, 0, L.OK)]:
         a = list(args); a[i] = v
         assert f(*a) == code, (i, v)
+    # one expert's gate/up weight (2 I K bytes) must stay below 2^31 bytes:
+    # its rows are addressed with 32-bit offsets from one base
+    a = list(args); a[10] = 2**17; a[11] = 2**13
+    assert f(*a) == L.ENOTSUP
+    a[11] = 2**13 - 16
+    assert f(*a) != L.ENOTSUP
 
 
 def test_block32_argument_checks():

@@ -282,3 +282,167 @@ def test_grouped_gemm_moe_shape_sampled():
     err = rel_fro(np.concatenate(got_all), np.concatenate(ref_all))
     say(f"  sampled rel fro {err:.3e}")
     assert err <= TOL
+
+
+def _tiny_amax_acts(M, K, seed=11):
+    """bf16 activations whose 1x128 groups have tiny amaxes: row r takes the
+    r-th magnitude class below for every group (a few groups zero), so the
+    fp32 scale fl32(amax / 448) runs from 0 through subnormal values (1 / s
+    overflows below 2^-128) up to normal ones.  Values are uniform in
+    [-amax, amax] (bf16 subnormals included) with one element = +-amax."""
+    # 448 = 1.75 * 2^8, so amax = 1.75 * 2^k gives s = 2^(k - 8) exactly
+    mags = [0.0, 2.0**-133, 2.0**-130, 2.0**-127,
+            1.75 * 2.0**-121,          # s = 2^-129
+            1.75 * 2.0**-120,          # s = 2^-128 exactly: 1 / s overflows
+            1.7578125 * 2.0**-120,     # s just above 2^-128, still subnormal
+            1.75 * 2.0**-119,          # s = 2^-127
+            1.7421875 * 2.0**-118,     # s just below the smallest normal
+            1.75 * 2.0**-118,          # s = 2^-126, the smallest normal
+            2.0**-110, 1.0,
+            "alt0", "alt1", "single", 2.0**-126]
+    g = np.random.default_rng(seed)
+    G = K // 128
+    x = np.zeros((M, K), np.float32)
+    for r in range(M):
+        kind = mags[r % len(mags)]
+        for gi in range(G):
+            if isinstance(kind, str):
+                if kind == "alt0":
+                    a = 2.0**-125 if gi % 2 else 0.0
+                elif kind == "alt1":
+                    a = 2.0**-125 if gi % 2 else 2.0**-120
+                else:
+                    a = -1.0                       # one nonzero element, 2^-128
+            else:
+                a = kind if gi % 7 != 3 else 0.0   # a few zero groups per row
+            seg = x[r, gi * 128:(gi + 1) * 128]
+            if a == -1.0:
+                seg[g.integers(0, 128)] = (2.0**-128) * (1 if gi % 2 else -1)
+                continue
+            if a == 0.0:
+                continue
+            seg[:] = (g.random(128) * 2 - 1) * a
+            seg[g.integers(0, 128)] = a if g.random() < 0.5 else -a
+    return synth.f32_to_bf16_bits(x)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("M", [16, 5, 1])
+def test_linear_fused_quant_tiny_scales(fmt, M):
+    """fp8_linear's in-launch quantization on groups whose scale is subnormal
+    (amax below, at and above 448 * 2^-128, where 1 / s overflows, and
+    around 448 * 2^-126), all-zero and mixed groups: bit-identical to
+    fp8_quant_act + fp8_block_gemm, whose codes and scales match the oracle
+    bit for bit; each row's output within the acceptance bound of the
+    oracle's product."""
+    import torch
+    from block_scaled_precision_fp8_amd import lib as L
+    K, N = 4096, 512
+    assert L.workspace_size(L.OP_LINEAR, M, N, K) == 0          # the fused path
+    # 16 tokens: every class; 5: the subnormal-scale classes; 1: s = 2^-128
+    rows = {16: list(range(16)), 5: [1, 3, 5, 6, 8], 1: [5]}[M]
+    x = np.ascontiguousarray(_tiny_amax_acts(16, K)[rows])
+    # large weights keep the products of the tiny activations normal
+    w = synth.normal_bf16((N, K), 2.0**100, "llama", "w", seed=12)
+    xd, wd = to_dev_bf16(x), to_dev_bf16(w)
+    sdt = torch.float32 if fmt == 0 else torch.uint8
+    xq = torch.empty((M, K), dtype=torch.uint8, device=xd.device)
+    xs = torch.empty((M, K // 128), dtype=sdt, device=xd.device)
+    wq = torch.empty((N, K), dtype=torch.uint8, device=xd.device)
+    ws = torch.empty((N // 128, K // 128), dtype=sdt, device=xd.device)
+    L.fp8_quant_act(xd, xq, xs, scale_fmt=fmt)
+    L.fp8_quant_weight(wd, wq, ws, scale_fmt=fmt)
+    y1 = torch.empty((M, N), dtype=torch.bfloat16, device=xd.device)
+    y2 = torch.empty_like(y1)
+    L.fp8_block_gemm(xq, xs, wq, ws, y1, scale_fmt=fmt)
+    L.fp8_linear(xd, wq, ws, y2, scale_fmt=fmt)
+    torch.cuda.synchronize()
+    hq, hs = Q.quant_act(x, 128, fmt)
+    assert np.array_equal(xq.cpu().numpy(), hq), "act codes differ from the oracle"
+    assert np.array_equal(xs.cpu().numpy().view(np.uint8), hs.view(np.uint8)), \
+        "act scales differ from the oracle"
+    b1, b2 = bf16_bits(y1), bf16_bits(y2)
+    bad = np.argwhere(b1 != b2)
+    assert bad.size == 0, f"fused linear differs from quant + gemm at rows {np.unique(bad[:, 0])}"
+    ref = G.block_gemm(hq, hs, *Q.quant_weight(w, 128, 128, fmt), fmt=fmt)
+    got = F.bf16_decode(b2)
+    assert np.isfinite(got).all()
+    for r in range(M):
+        if not np.any(ref[r]):
+            assert not np.any(got[r]), f"row {r}: zero activations, nonzero output"
+            continue
+        e = rel_fro(got[r], ref[r])
+        assert e <= TOL, f"row {r}: rel fro {e:.3e}"
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("M,N,K", [(1, 512, 4096), (16, 1024, 4096), (16, 4104, 4096),
+                                   (64, 1024, 1536), (300, 520, 640)])
+@pytest.mark.parametrize("scale", ["plain", "tiny"])
+def test_linear_static_matches_two_calls(M, N, K, fmt, scale):
+    """fp8_linear with the static scheme (one calibrated per-tensor scale
+    passed by pointer) equals fp8_quant_act with that static scale followed
+    by fp8_block_gemm, bit for bit, on the fused decode path and the staged
+    one; the static codes match the oracle's static quantizer."""
+    import torch
+    from block_scaled_precision_fp8_amd import lib as L
+    from oracle import convert as C
+    x = synth.llama_acts(M, K, seed=21)
+    w = synth.normal_bf16((N, K), 0.02, "llama", "w", seed=21)
+    xd, wd = to_dev_bf16(x), to_dev_bf16(w)
+    sdt = torch.float32 if fmt == 0 else torch.uint8
+    if fmt == 0:
+        sval = np.float32(0.05 if scale == "plain" else 2.0**-130)
+        stat = torch.tensor([sval], dtype=torch.float32, device=xd.device)
+    else:
+        sval = np.uint8(120 if scale == "plain" else 1)
+        stat = torch.tensor([int(sval)], dtype=torch.uint8, device=xd.device)
+    G = -(-K // 128)
+    xq = torch.empty((M, K), dtype=torch.uint8, device=xd.device)
+    xs = torch.empty((M, G), dtype=sdt, device=xd.device)
+    xs.view(-1)[0] = stat[0]
+    wq = torch.empty((N, K), dtype=torch.uint8, device=xd.device)
+    ws = torch.empty((-(-N // 128), G), dtype=sdt, device=xd.device)
+    L.fp8_quant_act(xd, xq, xs, act_scheme=L.ACT_STATIC, scale_fmt=fmt)
+    L.fp8_quant_weight(wd, wq, ws, scale_fmt=fmt)
+    y1 = torch.empty((M, N), dtype=torch.bfloat16, device=xd.device)
+    y2 = torch.empty_like(y1)
+    L.fp8_block_gemm(xq, xs, wq, ws, y1, scale_fmt=fmt)
+    L.fp8_linear(xd, wq, ws, y2, act_scheme=L.ACT_STATIC, scale_fmt=fmt, act_scale=stat)
+    torch.cuda.synchronize()
+    hq, _ = C.quant_act_static(x, sval, 128, fmt)
+    assert np.array_equal(xq.cpu().numpy(), hq), "static codes differ from the oracle"
+    assert np.array_equal(bf16_bits(y1), bf16_bits(y2)), "static fp8_linear differs"
+
+
+@pytest.mark.parametrize("M", [1, 32, 4096])
+def test_attention_projection_12288_sampled(M):
+    """The FP8 attention projection of the NVFP4-style model (12288 x 12288,
+    1x128 / 128x128, fp32 scales) in the launch configuration the bench
+    times; the oracle recomputes sampled outputs in three weight blocks."""
+    import torch
+    from block_scaled_precision_fp8_amd import lib as L
+    K = N = 12288
+    say(f"attention projection M={M}")
+    x = synth.normal_bf16((M, K), 1.0, "nvfp4", "x", index=M, seed=3)
+    xd = to_dev_bf16(x)
+    wd = synth.device_normal_bf16((N, K), 0.015, "nvfp4", "w", index=7, seed=3)
+    wq = torch.empty((N, K), dtype=torch.uint8, device=xd.device)
+    ws = torch.empty((N // 128, K // 128), dtype=torch.float32, device=xd.device)
+    L.fp8_quant_weight(wd, wq, ws)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=xd.device)
+    L.fp8_linear(xd, wq, ws, y)
+    torch.cuda.synchronize()
+    g = np.random.default_rng(M)
+    blocks = g.choice(N // 128, 3, replace=False)
+    wrows = np.concatenate([np.arange(b * 128, b * 128 + 128) for b in blocks])
+    wsub = bf16_bits(wd[torch.from_numpy(wrows).cuda()])       # the same bf16 draw
+    hw, hws = Q.quant_weight(wsub, 128, 128, 0)                  # whole blocks
+    rows = np.unique(g.integers(0, M, min(M, 64)))
+    hx, hxs = Q.quant_act(x[rows], 128, 0)
+    rr, cc = np.meshgrid(np.arange(len(rows)), np.arange(len(wrows)), indexing="ij")
+    ref = G.block_gemm_rows(hx, hxs, hw, hws, rr.ravel(), cc.ravel())
+    got = F.bf16_decode(bf16_bits(y)[rows][:, wrows]).ravel()
+    err = rel_fro(got, ref)
+    say(f"  sampled rel fro {err:.3e}")
+    assert err <= TOL
