@@ -26,7 +26,8 @@ EXPORTS = ("bsfp8_version", "bsfp8_status_string", "bsfp8_workspace_size", "bsfp
            "fp8_quant_act", "fp8_quant_weight", "fp8_block_gemm", "fp8_linear",
            "fp8_grouped_gemm", "fp4_quant", "fp4_group_gemm", "fp8_dequant_weight",
            "fp8_scale_to_ue8m0", "mxfp4_quant_weight", "fp8_fp4_gemm",
-           "fp8_grouped_gemm_silu_mul_quant")
+           "fp8_grouped_gemm_silu_mul_quant", "fp8_linear_noalloc")
+NOALLOC_SCRATCH_BYTES = 32 << 20     # BSFP8_NOALLOC_SCRATCH_BYTES
 
 
 class BsFp8Error(RuntimeError):
@@ -59,6 +60,8 @@ _SIGS = {
                               _P, _SZ, _P]),
     "fp8_linear": (_I32, [_P, _I64, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _I32,
                           _P, _P, _SZ, _P]),
+    "fp8_linear_noalloc": (_I32, [_P, _I64, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32,
+                                  _I32, _P, _P]),
     "fp8_grouped_gemm": (_I32, [_P, _P, _P, _P, _P, _I32, _P, _I64, _I64, _I64, _I32, _I32,
                                 _I32, _P, _SZ, _P]),
     "fp4_quant": (_I32, [_P, _I64, _I64, _I32, _P, _P, _P, _P, _SZ, _P]),

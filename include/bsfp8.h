@@ -207,6 +207,29 @@ BSFP8_API int32_t fp8_linear(const void* x, int64_t ldx, const void* wq,
                    const void* act_scale, void* workspace, size_t workspace_bytes,
                    void* stream);
 
+/* Bytes of the device array that fp8_linear_noalloc takes as its workspace
+   (one array per GPU the library runs on, held until the process ends). */
+#define BSFP8_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * fp8_linear_noalloc -- fp8_linear for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments and results as fp8_linear, without the
+ * workspace: the library uses a device array of BSFP8_NOALLOC_SCRATCH_BYTES
+ * of its own (looked up once per device), and calls no allocating routine.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's contents; calls that overlap on one GPU (different streams
+ *     without ordering) race and give undefined results.
+ *   - Errors: those of fp8_linear, and ENOSPC when
+ *     bsfp8_workspace_size(BSFP8_OP_LINEAR or BSFP8_OP_LINEAR_B32, M, N, K, 0)
+ *     exceeds BSFP8_NOALLOC_SCRATCH_BYTES (use fp8_linear then).
+ */
+BSFP8_API int32_t fp8_linear_noalloc(const void* x, int64_t ldx, const void* wq,
+                                     const void* w_scale_inv, const void* bias, void* y,
+                                     int64_t M, int64_t N, int64_t K, int32_t block_n,
+                                     int32_t block_k, int32_t act_scheme, int32_t scale_fmt,
+                                     const void* act_scale, void* stream);
+
 /*
  * fp8_grouped_gemm -- MoE expert GEMM over contiguous per-expert row
  * segments ([FG-FP8] §一 FP8Experts; §6.4 and §七 expert backends).  For

@@ -29,6 +29,28 @@ def test_header_declarations_match_binding():
     assert sorted(names) == sorted(L.EXPORTS)
 
 
+def test_noalloc_scratch_size_matches_header():
+    src = open(HEADER).read()
+    m = re.search(r"#define\s+BSFP8_NOALLOC_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == L.NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_argument_checks():
+    """fp8_linear_noalloc shares fp8_linear's checks; a problem whose
+    workspace exceeds the library's array is refused before any HIP call."""
+    f = L.load().fp8_linear_noalloc
+    assert f(FAKE, 256, FAKE, FAKE, None, FAKE, 16, 256, 256, 128, 128, 1, 0, None,
+             None) == L.EINVAL
+    assert f(FAKE, 256, FAKE, FAKE, None, FAKE, 16, 256, 256, 64, 64, 0, 0, None,
+             None) == L.ENOTSUP
+    assert f(FAKE, 256, FAKE, FAKE, None, FAKE, 0, 256, 256, 128, 128, 0, 0, None,
+             None) == L.OK
+    M, N, K = 8192, 4096, 14336
+    assert L.workspace_size(L.OP_LINEAR, M, N, K) > L.NOALLOC_SCRATCH_BYTES
+    assert f(FAKE, K, FAKE, FAKE, None, FAKE, M, N, K, 128, 128, 0, 0, None,
+             None) == L.ENOSPC
+
+
 def test_every_declared_symbol_exported():
     L.load()                      # the binding's load order (torch's HIP runtime first)
     lib = ctypes.CDLL(L.LIB_PATH)
