@@ -71,3 +71,23 @@ def fp8_fp4_gemm(xq, x_scale, wq4, w_scale, bias=None, fmt=0):
     if bias is not None:
         Y = Y + np.asarray(bias, dtype=np.float64)[None, :]
     return Y
+
+
+def grouped_fp8_fp4_gemm(xq, x_scale, wq4, w_scale, seg_offsets, fmt=0):
+    """MoE experts with FP4-packed (MXFP4) weights over contiguous row
+    segments ([FG-FP8] §一: V4-style FP4-packed expert weights): for every
+    expert e, rows [off[e], off[e+1]) of Y are fp8_fp4_gemm of those rows of
+    (xq, x_scale) with (wq4[e], w_scale[e]).
+
+    xq (T, K) E4M3, x_scale (T, K/128), wq4 (E, N, K/2), w_scale (E, N, K/32),
+    seg_offsets (E + 1,).  Returns Y (T, N) float64; rows of an empty
+    segment do not exist.
+    """
+    off = np.asarray(seg_offsets, dtype=np.int64)
+    E, N = wq4.shape[0], wq4.shape[1]
+    Y = np.zeros((xq.shape[0], N))
+    for e in range(E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi > lo:
+            Y[lo:hi] = fp8_fp4_gemm(xq[lo:hi], x_scale[lo:hi], wq4[e], w_scale[e], fmt=fmt)
+    return Y

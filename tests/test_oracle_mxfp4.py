@@ -85,3 +85,39 @@ def test_gemm_loops():
                     sw = 2.0 ** (int(ws[n, k // 32]) - 127)
                     acc += F.e4m3_decode(xq[m, k]) * sa * F.e2m1_decode(wc[n, k]) * sw
                 assert abs(acc - ref[m, n]) <= 1e-12 * max(1.0, abs(acc))
+
+
+def test_grouped_matches_per_row_loops():
+    """Grouped FP8 x MXFP4 experts: each row against an explicit loop over
+    its own expert's dequantized weights (empty experts included); swapping
+    two experts' weights changes exactly their rows."""
+    E, N, K = 4, 3, 64
+    counts = np.array([2, 0, 3, 1])
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    T = int(off[-1])
+    x = synth.normal_bf16((T, K), 1.0, "moe", "x", seed=7)
+    wq = np.empty((E, N, K // 2), np.uint8)
+    ws = np.empty((E, N, K // 32), np.uint8)
+    for e in range(E):
+        wq[e], ws[e] = X.quant_weight_mxfp4(synth.normal_bf16((N, K), 0.01, "moe", "w", e, seed=7))
+    for fmt in (0, 1):
+        xq, xs = Q.quant_act(x, 128, fmt)
+        Y = X.grouped_fp8_fp4_gemm(xq, xs, wq, ws, off, fmt=fmt)
+        for r in range(T):
+            e = int(np.searchsorted(off, r, side="right") - 1)
+            wc = F.e2m1_unpack(wq[e])
+            for n in range(N):
+                acc = 0.0
+                for k in range(K):
+                    sa = float(xs[r, k // 128]) if fmt == 0 else 2.0 ** (int(xs[r, k // 128]) - 127)
+                    sw = 2.0 ** (int(ws[e, n, k // 32]) - 127)
+                    acc += F.e4m3_decode(xq[r, k]) * sa * F.e2m1_decode(wc[n, k]) * sw
+                assert abs(acc - Y[r, n]) <= 1e-12 * max(1.0, abs(acc)), (fmt, r, n)
+        sw_ = wq.copy()
+        sw_[[0, 2]] = sw_[[2, 0]]
+        ss_ = ws.copy()
+        ss_[[0, 2]] = ss_[[2, 0]]
+        Y2 = X.grouped_fp8_fp4_gemm(xq, xs, sw_, ss_, off, fmt=fmt)
+        changed = np.flatnonzero(np.any(Y2 != Y, axis=1))
+        assert set(changed) <= set(range(off[0], off[1])) | set(range(off[2], off[3]))
+        assert len(changed) == counts[0] + counts[2]
