@@ -22,7 +22,8 @@ then fp8_block_gemm, the two launches fp8_linear makes for them.
 The other rows of the path are timed in the same run and reported in
 ``detail`` (not in ``value``): DeepSeek-V3-shaped linears with UE8M0 scales,
 the MoE expert MLP (256 experts, Zipf-routed top-8: gate/up grouped GEMM,
-the same with the fused SiLU-mul requant, the down GEMM on its output), the
+the same with the fused SiLU-mul requant, the down GEMM on its output, and
+the gate/up GEMM with MXFP4 expert weights), the
 NVFP4-style MLP (fp4_quant + fp4_group_gemm) with its FP8 attention
 projection, the FP8 activation x MXFP4 weight linear at DeepSeek-V3 expert
 shapes, FP8 linears with (32, 32) weight blocks, and weight quantization.
@@ -33,7 +34,10 @@ with their whole 2MNK; bsfp8_gemm_kernel says which): algorithmic flops over
 its launches / its summed duration from HIP events
 recorded on the launch stream inside the timed region.  ``traffic`` comes
 from the committed rocprofv3 PMC summary when that summary was taken on the
-current kernel source, else null.
+current kernel source, else null.  ``launch_us`` gives the median, p10 and
+p90 of the dominant kernel's timed launches, ``ms_per_step_stats`` those of
+the timed steps.  ``roofline_decode`` is the HBM roofline of the decode-sized
+runs (M <= 16, act quant included): their algorithmic bytes over their time.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--suites ...]
 """
@@ -120,10 +124,21 @@ class Timer:
         e.record(self.stream)
         self.ev.setdefault(key, []).append(e)
 
+    def all_ms(self, a, b):
+        """ms between marks a and b, one per occurrence"""
+        return [x.elapsed_time(y) for x, y in zip(self.ev[a], self.ev[b])]
+
     def ms(self, a, b):
         """mean ms between marks a and b (matched by occurrence)"""
-        ea, eb = self.ev[a], self.ev[b]
-        return sum(x.elapsed_time(y) for x, y in zip(ea, eb)) / len(ea)
+        v = self.all_ms(a, b)
+        return sum(v) / len(v)
+
+
+def pstats(v, scale=1.0, nd=2):
+    """median, p10 and p90 of a list of durations (times `scale`)"""
+    a = np.sort(np.asarray(v, dtype=np.float64)) * scale
+    return {"median": round(float(np.median(a)), nd), "p10": round(float(np.percentile(a, 10)), nd),
+            "p90": round(float(np.percentile(a, 90)), nd), "n": int(len(a))}
 
 
 def run_linears(torch, L, synth, shapes, ms, fmt, workload, steps, warmup, dev, sp):
@@ -194,14 +209,16 @@ def run_linears(torch, L, synth, shapes, ms, fmt, workload, steps, warmup, dev, 
     # timed region: events only around the dominant kernel's launches (the
     # roofline); the per-run breakdown comes from a second, untimed pass
     tb = Timer(torch, stream)
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
+    # one event per step boundary: the step time's median / p10 / p90 besides
+    # the whole-run mean
+    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    bounds[0].record(stream)
     for s in range(steps):
         step(s, tb, big_only=True)
-    t1.record(stream)
+        bounds[s + 1].record(stream)
     torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / steps
+    ms_step = bounds[0].elapsed_time(bounds[-1]) / steps
+    step_ms = [bounds[i].elapsed_time(bounds[i + 1]) for i in range(steps)]
     tm = Timer(torch, stream)
     for s in range(steps):
         step(s, tm)
@@ -209,6 +226,8 @@ def run_linears(torch, L, synth, shapes, ms, fmt, workload, steps, warmup, dev, 
     sb = 4 if fmt == 0 else 1
     detail, big_flops, big_ms, n_big, flops = [], 0.0, 0.0, 0, 0.0
     dec_bytes, dec_ms = 0.0, 0.0
+    big_launch_us = []          # every timed launch of the 256 x 256 tile
+    dec_runs = []               # (bytes, per-step ms list) of the M <= 16 runs
     for j, r in enumerate(runs):
         M, N, K = r["M"], r["N"], r["K"]
         qm, gm = tm.ms(("q", j), ("g", j)), tm.ms(("g", j), ("e", j))
@@ -224,6 +243,7 @@ def run_linears(torch, L, synth, shapes, ms, fmt, workload, steps, warmup, dev, 
                      frac_hbm=round(lb / (lm * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
             dec_bytes += lb
             dec_ms += lm
+            dec_runs.append((lb, tm.all_ms(("q", j), ("g", j))))
             log(f"[{workload}] M={M:5d} K={K:5d} N={N:5d} fused linear {lm*1e3:8.1f} us "
                 f"({d['linear_gbs']:7.1f} GB/s, {d['linear_tflops']:7.1f} TF/s)")
             detail.append(d)
@@ -239,25 +259,32 @@ def run_linears(torch, L, synth, shapes, ms, fmt, workload, steps, warmup, dev, 
         if M <= 16:
             dec_bytes += qb + gb
             dec_ms += qm + gm
+            dec_runs.append((qb + gb, tm.all_ms(("q", j), ("e", j))))
         detail.append(d)
         if r["big"]:
             big_flops += fl
             big_ms += tb.ms(("g", j), ("e", j))
             n_big += 1
+            big_launch_us += [v * 1e3 for v in tb.all_ms(("g", j), ("e", j))]
         log(f"[{workload}] M={M:5d} K={K:5d} N={N:5d} quant {qm*1e3:8.1f} us "
             f"({d['quant_gbs']:7.1f} GB/s)  gemm {gm*1e3:8.1f} us ({d['gemm_tflops']:7.1f} TF/s, "
             f"{d['gemm_gbs']:7.1f} GB/s)  linear {d['linear_tflops']:7.1f} TF/s")
     decode = None
     if dec_ms > 0:
+        # per step: all M <= 16 runs' bytes over their summed time (linear,
+        # act quant included), median / p10 / p90 over the steps
+        per_step = [sum(ms[i] for _, ms in dec_runs) for i in range(steps)]
         decode = dict(runs="M <= 16", bytes=dec_bytes, us=round(dec_ms * 1e3, 1),
+                      us_per_step=pstats(per_step, 1e3, 1),
                       gbs=round(dec_bytes / (dec_ms * 1e-3) / 1e9, 1),
                       frac_hbm=round(dec_bytes / (dec_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
     for r in runs:
         r.clear()
     weights.clear()
     torch.cuda.empty_cache()
-    return dict(detail=detail, ms_step=ms_step, flops=flops, big_flops=big_flops,
-                big_ms=big_ms, n_big=n_big, decode=decode)
+    return dict(detail=detail, ms_step=ms_step, step_ms=step_ms, flops=flops,
+                big_flops=big_flops, big_ms=big_ms, n_big=n_big, decode=decode,
+                big_launch_us=big_launch_us)
 
 
 def run_moe(torch, L, synth, steps, warmup, dev, sp):
@@ -282,6 +309,13 @@ def run_moe(torch, L, synth, steps, warmup, dev, sp):
             L.fp8_quant_weight(wb, wq[e], ws[e])
             del wb
         W[name] = (wq, ws)
+    # the gate/up experts again as MXFP4 (E2M1 in 1 x 32 groups, E8M0 scales)
+    wq4 = torch.empty((E, 2 * I, H // 2), dtype=torch.uint8, device=dev)
+    ws4 = torch.empty((E, 2 * I, H // 32), dtype=torch.uint8, device=dev)
+    for e in range(E):
+        wb = synth.device_normal_bf16((2 * I, H), 0.02, "moe", "w", e)
+        L.mxfp4_quant_weight(wb, wq4[e], ws4[e])
+        del wb
     xq = torch.empty((T, H), dtype=torch.uint8, device=dev)
     xs = torch.empty((T, H // 128), dtype=torch.float32, device=dev)
     y1 = torch.empty((T, 2 * I), dtype=torch.bfloat16, device=dev)
@@ -302,6 +336,8 @@ def run_moe(torch, L, synth, steps, warmup, dev, sp):
         mark("d")
         L.fp8_grouped_gemm(hq, hs, W["down"][0], W["down"][1], seg, y2, stream=sp)
         mark("e")
+        L.fp8_fp4_grouped_gemm(xq, xs, wq4, ws4, seg, y1, stream=sp)
+        mark("w4")
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -310,6 +346,7 @@ def run_moe(torch, L, synth, steps, warmup, dev, sp):
         step(tm)
     torch.cuda.synchronize()
     qm, gm, fm, dm = tm.ms("q", "g"), tm.ms("g", "f"), tm.ms("f", "d"), tm.ms("d", "e")
+    w4m = tm.ms("e", "w4")
 
     def row(ms, N, K, out_bytes):
         fl = 2.0 * T * N * K
@@ -322,10 +359,16 @@ def run_moe(torch, L, synth, steps, warmup, dev, sp):
            "gate_up": row(gm, 2 * I, H, 2 * T * 2 * I),
            "gate_up_silu_mul_quant": row(fm, 2 * I, H, T * I + 4 * T * (I // 128)),
            "down": row(dm, H, I, 2 * T * H),
+           "gate_up_mxfp4": dict(row(w4m, 2 * I, H, 2 * T * 2 * I),
+                                 gbs=round((nb * 2 * I * (H // 2 + H // 32) + T * (H + 4 * (H // 128))
+                                            + 2 * T * 2 * I) / (w4m * 1e-3) / 1e9, 1)),
            "ffn_us": round((qm + fm + dm) * 1e3, 1)}
+    g4 = res["gate_up_mxfp4"]
+    g4["frac_hbm"] = round(g4["gbs"] / PEAK_HBM_GBS, 4)
     log(f"[moe] T={T}: act quant {qm*1e3:.1f} us, gate/up {gm*1e3:.1f} us, fused gate/up + "
-        f"silu-mul quant {fm*1e3:.1f} us, down {dm*1e3:.1f} us, ffn {res['ffn_us']} us")
-    del W, xq, xs, y1, hq, hs, y2
+        f"silu-mul quant {fm*1e3:.1f} us, down {dm*1e3:.1f} us, ffn {res['ffn_us']} us, "
+        f"gate/up with MXFP4 experts {w4m*1e3:.1f} us ({g4['gbs']} GB/s)")
+    del W, xq, xs, y1, hq, hs, y2, wq4, ws4
     torch.cuda.empty_cache()
     res["rows_per_expert"] = dict(max=int(counts.max()), median=float(np.median(counts)),
                                   min=int(counts.min()))
@@ -641,7 +684,17 @@ def main():
                           "tiles), large-M block-scaled GEMM",
                 "launches_per_step": r["n_big"],
                 "avg_launch_us": round(r["big_ms"] / r["n_big"] * 1e3, 2),
+                "launch_us": pstats(r["big_launch_us"]),
                 "algorithmic_gflop_per_launch": round(r["big_flops"] / r["n_big"] / 1e9, 2)}
+    dec = r["decode"]
+    roofline_decode = None
+    if dec:
+        roofline_decode = {
+            "bound": "hbm", "achieved": dec["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": dec["frac_hbm"], "traffic": None,
+            "kernel": "gemm_decode_kernel (M <= 16; fp8_linear, act quant included)",
+            "runs": "the 8 Llama-3-8B linears with M in {1, 16}",
+            "algorithmic_bytes_per_step": dec["bytes"], "us_per_step": dec["us_per_step"]}
     detail = {"llama": r["detail"], "llama_decode_hbm": r["decode"]}
     suites = [] if args.suites == "none" else args.suites.split(",")
     if "deepseek" in suites:
@@ -680,7 +733,9 @@ def main():
                                "{1,16,128,2048,8192}; 1x128 act groups, 128x128 weight "
                                "blocks, fp32 scales, bf16 out",
                    "runs_per_step": 20, "flops_per_step": r["flops"]},
+        "ms_per_step_stats": pstats(r["step_ms"], 1.0, 4),
         "roofline": roofline,
+        "roofline_decode": roofline_decode,
         "cpu_baseline": cpu,
         "detail": detail,
     }

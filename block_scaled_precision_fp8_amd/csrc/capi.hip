@@ -350,6 +350,27 @@ int32_t fp8_grouped_gemm(const void* xq, const void* x_scale, const void* wq,
   return hip_status(launch_grouped_gemm(a, (hipStream_t)stream));
 }
 
+int32_t fp8_fp4_grouped_gemm(const void* xq, const void* x_scale, const void* wq4,
+                             const void* w_scale, const int32_t* seg_offsets, int32_t E, void* y,
+                             int64_t T, int64_t N, int64_t K, int32_t scale_fmt, void* stream) {
+  if (E < 1 || E > 1024) return BSFP8_EINVAL;
+  int32_t r = check_gemm(xq, x_scale, wq4, w_scale, nullptr, y, T, N, K, 128, 128, scale_fmt);
+  if (r != BSFP8_OK) return r;
+  if (K % 32 != 0) return BSFP8_EINVAL;
+  if (T == 0) return BSFP8_OK;
+  if (!seg_offsets || ((uintptr_t)seg_offsets & 3u)) return BSFP8_EINVAL;
+  const int64_t NT = (N + 255) / 256;
+  if (!fits_i32(((T + 127) / 128 + E) * NT)) return BSFP8_EINVAL;
+  if (!fits_i32(T * ((K + 127) / 128))) return BSFP8_EINVAL;
+  r = check_device(stream);
+  if (r != BSFP8_OK) return r;
+  GemmArgs a{};
+  a.xq = (const uint8_t*)xq; a.xs = x_scale; a.wq = (const uint8_t*)wq4; a.ws = w_scale;
+  a.bias = nullptr; a.y = (uint16_t*)y; a.M = T; a.N = N; a.K = K; a.fmt = scale_fmt;
+  a.seg = seg_offsets; a.E = E; a.w4 = true;
+  return hip_status(launch_grouped_gemm(a, (hipStream_t)stream));
+}
+
 int32_t fp8_grouped_gemm_silu_mul_quant(const void* xq, const void* x_scale, const void* wq,
                                         const void* w_scale_inv, const int32_t* seg_offsets,
                                         int32_t E, void* hq, void* h_scale, void* h_bf16,

@@ -385,7 +385,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
   constexpr int BM = WAVES_M * WM, BN = WAVES_N * WN;
   constexpr int MI = WM / 16, NI = WN / 16;
   static_assert(WN == 64 || WN == 128, "a wave's N range lies inside one weight block");
-  static_assert(!(W4 && GROUPED), "MXFP4 weights: dense launches");
   static_assert(!SWIGLU || (GROUPED && !W4 && WAVES_N % 2 == 0 && WAVES_N / 2 * WN == 128),
                 "SiLU-mul tiles: 128 gate rows then the 128 matching up rows");
   constexpr int kWRow = W4 ? 64 : kRowBytes;   // W bytes per row per K block
@@ -443,8 +442,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
   const int kb_begin = part ? tl.split * kbps : 0;
   const int kb_end = part ? min(KB, kb_begin + kbps) : KB;
   const int64_t NB = (N + 127) / 128;
-  const uint8_t* wbase = wq + (int64_t)tl.expert * N * K;
+  const int64_t KW = W4 ? K / 2 : K;         // W bytes per row
+  const int64_t G32 = K / 32;                // MXFP4 scales per row
+  // this tile's expert: weights (E, N, KW), FP8 block scales (E, NB, KB) or
+  // MXFP4 group scales (E, N, K/32)
+  const uint8_t* wbase = wq + (int64_t)tl.expert * N * KW;
   const uint8_t* wsb = (const uint8_t*)wsc + (int64_t)tl.expert * NB * KB * SB;
+  const uint8_t* wsb4 = (const uint8_t*)wsc + (int64_t)tl.expert * N * G32;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -454,7 +458,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
   const int64_t mrows = min((int64_t)BM, tl.mlim - tl.m0);
   const int64_t nrows = min((int64_t)BN, N - tl.n0);
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(xq + tl.m0 * K, mrows * K);
-  const int64_t KW = W4 ? K / 2 : K;         // W bytes per row
   // SWIGLU: N = 2 I weight rows, gate rows [0, I) then up rows [I, 2 I); an
   // N tile at n0 = 256 t covers h columns [128 t, 128 t + 128): its rows
   // [0, 128) are gate rows 128 t + r, rows [128, 256) the up rows I + 128 t + r
@@ -486,9 +489,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
     return (row < rows && kc < (uint32_t)KW) ? (uint32_t)(row * KW) + kc : kOOB;
   };
   // MXFP4 weight scales: lane row of each 16-row subtile, group 4 kb + g4
-  const int64_t G32 = K / 32;
-  const __amdgpu_buffer_rsrc_t rsw4 = make_rsrc((const uint8_t*)wsc + tl.n0 * G32,
-                                                W4 ? nrows * G32 : 0);
+  const __amdgpu_buffer_rsrc_t rsw4 = make_rsrc(wsb4 + tl.n0 * G32, W4 ? nrows * G32 : 0);
   // scale sources: this lane's token rows, and this wave's weight block
   uint32_t saoff[MI];
 #pragma unroll
@@ -1336,6 +1337,17 @@ BSFP8_INST2(1, 4, 2, 64, 128, false, true, false, false, true)
 BSFP8_INST2(1, 2, 4, 64, 64, false, true, false, false, true)
 BSFP8_INST2(1, 4, 2, 64, 128, false, true, false, true, true)
 BSFP8_INST2(1, 2, 4, 64, 64, false, true, false, true, true)
+// MoE experts with MXFP4 weights: the two grouped tile classes, with and
+// without staged weight scales (K a multiple of 128 or not)
+#define BSFP8_INST_W4G(FMT)                                       \
+  BSFP8_INST2(FMT, 4, 2, 64, 128, true, true, false, false, false) \
+  BSFP8_INST2(FMT, 1, 4, 64, 64, true, true, false, false, false)  \
+  BSFP8_INST2(FMT, 1, 4, 64, 64, true, true, false, false, true)
+BSFP8_INST_W4G(0)
+BSFP8_INST_W4G(1)
+BSFP8_INST2(1, 4, 2, 64, 128, true, true, false, false, true)
+BSFP8_INST2(1, 4, 2, 64, 128, true, true, false, true, true)
+#undef BSFP8_INST_W4G
 #undef BSFP8_INST_UE8M0_STAGED
 #undef BSFP8_INST2
 #undef BSFP8_INST_ALL
@@ -1452,6 +1464,27 @@ hipError_t launch_lds(const GemmArgs& a, hipStream_t st) {
     // than 128: two launches over disjoint experts, each with its own
     // device-built tile table
     const int kb = (int)((a.K + 127) / 128);
+    if (a.w4) {
+      // MXFP4 experts: the dense FP8 x MXFP4 tiles over the same two expert
+      // classes; weight scales staged through LDS when K is a multiple of
+      // 128 (for the big tile with UE8M0 scales only: with fp32 activation
+      // scales the staged big tile spills)
+      const bool sw4 = a.K % 128 == 0;
+      hipError_t e;
+      if constexpr (FMT == 1) {
+        if (sw4)
+          e = ue8m0_aligned(a, 1, kb)
+                  ? launch_cfg<FMT, 4, 2, 64, 128, true, true, false, true, true>(a, st, 1, kb, 1)
+                  : launch_cfg<FMT, 4, 2, 64, 128, true, true, false, false, true>(a, st, 1, kb, 1);
+        else
+          e = launch_cfg<FMT, 4, 2, 64, 128, true, true>(a, st, 1, kb, 1);
+      } else {
+        e = launch_cfg<FMT, 4, 2, 64, 128, true, true>(a, st, 1, kb, 1);
+      }
+      if (e != hipSuccess) return e;
+      return sw4 ? launch_cfg<FMT, 1, 4, 64, 64, true, true, false, false, true>(a, st, 1, kb, 2)
+                 : launch_cfg<FMT, 1, 4, 64, 64, true, true>(a, st, 1, kb, 2);
+    }
     const hipError_t e = ue8m0_aligned(a, 1, kb)
                              ? launch_cfg<FMT, 4, 2, 64, 128, true, false, false, U>(a, st, 1, kb, 1)
                              : launch_cfg<FMT, 4, 2, 64, 128, true>(a, st, 1, kb, 1);

@@ -26,7 +26,7 @@ EXPORTS = ("bsfp8_version", "bsfp8_status_string", "bsfp8_workspace_size", "bsfp
            "fp8_quant_act", "fp8_quant_weight", "fp8_block_gemm", "fp8_linear",
            "fp8_grouped_gemm", "fp4_quant", "fp4_group_gemm", "fp8_dequant_weight",
            "fp8_scale_to_ue8m0", "mxfp4_quant_weight", "fp8_fp4_gemm",
-           "fp8_grouped_gemm_silu_mul_quant", "fp8_linear_noalloc")
+           "fp8_grouped_gemm_silu_mul_quant", "fp8_linear_noalloc", "fp8_fp4_grouped_gemm")
 NOALLOC_SCRATCH_BYTES = 32 << 20     # BSFP8_NOALLOC_SCRATCH_BYTES
 
 
@@ -62,6 +62,7 @@ _SIGS = {
                           _P, _P, _SZ, _P]),
     "fp8_linear_noalloc": (_I32, [_P, _I64, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32,
                                   _I32, _P, _P]),
+    "fp8_fp4_grouped_gemm": (_I32, [_P, _P, _P, _P, _P, _I32, _P, _I64, _I64, _I64, _I32, _P]),
     "fp8_grouped_gemm": (_I32, [_P, _P, _P, _P, _P, _I32, _P, _I64, _I64, _I64, _I32, _I32,
                                 _I32, _P, _SZ, _P]),
     "fp4_quant": (_I32, [_P, _I64, _I64, _I32, _P, _P, _P, _P, _SZ, _P]),
@@ -232,6 +233,17 @@ def fp8_grouped_gemm(xq, x_scale, wq, w_scale_inv, seg_offsets, y, block_n=128, 
     _check("fp8_grouped_gemm", load().fp8_grouped_gemm(
         _ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale_inv), _ptr(seg_offsets), E, _ptr(y),
         T, N, K, block_n, block_k, scale_fmt, _ptr(ws), wsb, _stream(stream)))
+
+
+def fp8_fp4_grouped_gemm(xq, x_scale, wq4, w_scale, seg_offsets, y, scale_fmt=SCALE_FLOAT,
+                         stream=None):
+    """xq (T, K) E4M3; x_scale (T, K/128); wq4 uint8 (E, N, K/2); w_scale
+    uint8 (E, N, K/32); seg_offsets int32 (E+1,) on the device; y bf16 (T, N)."""
+    T, K = xq.shape
+    E, N = wq4.shape[0], wq4.shape[1]
+    _check("fp8_fp4_grouped_gemm", load().fp8_fp4_grouped_gemm(
+        _ptr(xq), _ptr(x_scale), _ptr(wq4), _ptr(w_scale), _ptr(seg_offsets), E, _ptr(y), T, N, K,
+        scale_fmt, _stream(stream)))
 
 
 def fp4_quant(x, q4, gscale, tscale, dynamic_tscale=1, workspace=None, stream=None):

@@ -363,6 +363,30 @@ BSFP8_API int32_t fp8_fp4_gemm(const void* xq, const void* x_scale, const void* 
                                size_t workspace_bytes, void* stream);
 
 /*
+ * fp8_fp4_grouped_gemm -- MoE expert GEMM with FP4-packed expert weights
+ * ([FG-FP8] §一: FP8Experts can take V4-style FP4-packed expert weights;
+ * §6.1 and §6.4: the FP8 x FP4 linear and the grouped expert GEMMs of the
+ * fast backend).  For every expert e, rows [off[e], off[e+1]) of Y are the
+ * fp8_fp4_gemm of the same rows of (xq, x_scale) with expert e's MXFP4
+ * weights (wq4[e], w_scale[e]):
+ *
+ *   Y[t][n] = bf16( sum_k E4M3(xq[t][k]) S_a[t][k/128]
+ *                         * E2M1(wq4[e][n][k]) 2^(w_scale[e][n][k/32]-127) )
+ *
+ *   xq, x_scale  as written by fp8_quant_act (T rows; FLOAT or UE8M0).
+ *   wq4          uint8 [E][N][K/2] (mxfp4_quant_weight per expert);
+ *   w_scale      E8M0 bytes [E][N][K/32].
+ *   seg_offsets  DEVICE int32 [E+1], the precondition of fp8_grouped_gemm.
+ *   E            1 <= E <= 1024;  y out, bf16 [T][N].
+ *   K % 32 == 0, N % 8 == 0, K <= 2^22.  No workspace.
+ * Errors as fp8_grouped_gemm (block sizes are fixed here).
+ */
+BSFP8_API int32_t fp8_fp4_grouped_gemm(const void* xq, const void* x_scale, const void* wq4,
+                                       const void* w_scale, const int32_t* seg_offsets,
+                                       int32_t E, void* y, int64_t T, int64_t N, int64_t K,
+                                       int32_t scale_fmt, void* stream);
+
+/*
  * fp8_dequant_weight -- fold the block scales back into the weights, the
  * dequantize-on-load step for pre-quantized checkpoints ([FG-FP8] §五,
  * Fp8Dequantize):  W[n][k] = bf16_rne(fl32(E4M3(wq[n][k]) * S_w[n/B][k/B]))

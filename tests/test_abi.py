@@ -194,6 +194,18 @@ def test_grouped_argument_checks():
     assert f(*bad) == L.OK
 
 
+def test_fp8_fp4_grouped_argument_checks():
+    f = L.load().fp8_fp4_grouped_gemm
+    #       xq    xs    wq4   ws    seg   E  y     T   N    K    fmt stream
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, 64, 256, 256, 0, None]
+    for i, v, code in [(5, 0, L.EINVAL), (5, 1025, L.EINVAL), (4, None, L.EINVAL),
+                       (4, 0x100002, L.EINVAL), (9, 48, L.EINVAL), (9, 100, L.EINVAL),
+                       (8, 12, L.EINVAL), (10, 2, L.EINVAL), (6, None, L.EINVAL),
+                       (2, MIS, L.EINVAL), (9, 2**22 + 32, L.ENOTSUP), (7, 0, L.OK)]:
+        a = list(args); a[i] = v
+        assert f(*a) == code, (i, v)
+
+
 def test_fp4_argument_checks():
     lib = L.load()
     assert lib.fp4_quant(FAKE, 4, 48, 1, FAKE, FAKE, FAKE, None, 0, None) == L.EINVAL

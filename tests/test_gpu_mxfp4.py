@@ -121,3 +121,93 @@ def test_fp8_fp4_gemm_full_size_sampled(M, K, N, fmt):
     assert err <= TOL
     # the device-quantized weights of the sampled rows equal the oracle's
     assert np.array_equal(u8(wq)[uc], hw) and np.array_equal(u8(ws)[uc], hws)
+
+
+def _grouped_w4_case(counts, N, K, fmt, seed):
+    import torch
+    from block_scaled_precision_fp8_amd import lib as L
+    E = len(counts)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    T = int(off[-1])
+    x = synth.deepseek_acts(T, K, seed=seed) if fmt else synth.llama_acts(T, K, seed=seed)
+    xq, xs = Q.quant_act(x, 128, fmt)
+    wq = np.empty((E, N, K // 2), np.uint8)
+    ws = np.empty((E, N, K // 32), np.uint8)
+    for e in range(E):
+        wq[e], ws[e] = X.quant_weight_mxfp4(synth.normal_bf16((N, K), 0.01, "moe", "w", e,
+                                                              seed=seed))
+    yf = torch.full((T * N + 64,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    y = yf[:T * N].view(T, N)
+    L.fp8_fp4_grouped_gemm(to_dev(xq), to_dev(xs), to_dev(wq), to_dev(ws), to_dev(off), y,
+                           scale_fmt=fmt)
+    torch.cuda.synchronize()
+    assert torch.isnan(yf[T * N:].float()).all(), "wrote past the output"
+    got = F.bf16_decode(bf16_bits(y))
+    assert np.isfinite(got).all(), "unwritten rows"
+    return rel_fro(got, X.grouped_fp8_fp4_gemm(xq, xs, wq, ws, off, fmt=fmt))
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("counts,N,K", [
+    ([3, 0, 1, 6, 2], 256, 256),
+    ([0, 0, 130, 0, 1, 257, 64, 0], 512, 640),     # both tile classes, K % 128 == 0
+    ([300], 264, 1056),                            # ragged N, K % 128 != 0 (per-block scales)
+    ([0, 300, 5, 140], 384, 1024),                 # large experts, dword-aligned UE8M0 rows
+    ([0, 129, 0, 0], 256, 288),                    # one large expert, ragged K
+    (list(np.random.default_rng(5).integers(0, 40, 33)), 384, 512),
+])
+def test_fp8_fp4_grouped_gemm_parity(counts, N, K, fmt):
+    """MoE experts with MXFP4 weights against the oracle's per-expert
+    FP8 x FP4 product; both expert classes (more / at most 128 rows), empty
+    experts, ragged N and K."""
+    say(f"fp8 x fp4 grouped E={len(counts)} T={sum(counts)} N={N} K={K} fmt={fmt}")
+    err = _grouped_w4_case(counts, N, K, fmt, seed=len(counts) + K)
+    say(f"  rel fro {err:.3e}")
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_fp8_fp4_grouped_moe_shape_sampled(fmt):
+    """The MoE gate/up shape (256 experts, 7168 -> 4096, 4096 tokens x top-8
+    Zipf routing) with MXFP4 expert weights; the oracle recomputes sampled
+    rows of the largest, the smallest and two other experts."""
+    import torch
+    from block_scaled_precision_fp8_amd import lib as L
+    E, N, K, TOK, TOPK = 256, 4096, 7168, 4096, 8
+    tok, off = synth.moe_routing(TOK, E, TOPK)
+    T = len(tok)
+    say(f"fp8 x fp4 moe shape T={T} fmt={fmt}")
+    x = synth.deepseek_acts(TOK, K, seed=9) if fmt else synth.normal_bf16((TOK, K), 1.0, "moe", "x")
+    xd = to_dev_bf16(x)[torch.from_numpy(tok).cuda()]
+    sdt = torch.float32 if fmt == 0 else torch.uint8
+    xq = torch.empty((T, K), dtype=torch.uint8, device="cuda")
+    xs = torch.empty((T, K // 128), dtype=sdt, device="cuda")
+    L.fp8_quant_act(xd, xq, xs, scale_fmt=fmt)
+    wq = torch.empty((E, N, K // 2), dtype=torch.uint8, device="cuda")
+    ws = torch.empty((E, N, K // 32), dtype=torch.uint8, device="cuda")
+    for e in range(E):
+        wb = synth.device_normal_bf16((N, K), 0.01, "moe", "w", e)
+        L.mxfp4_quant_weight(wb, wq[e], ws[e])
+    y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+    L.fp8_fp4_grouped_gemm(xq, xs, wq, ws, to_dev(off), y, scale_fmt=fmt)
+    torch.cuda.synchronize()
+    counts = np.diff(off)
+    experts = [int(np.argmax(counts)), int(np.argmin(counts)), 17, 200]
+    g = np.random.default_rng(fmt)
+    from oracle import gemm as G
+    got_all, ref_all = [], []
+    for e in experts:
+        lo, hi = int(off[e]), int(off[e + 1])
+        rows = g.integers(lo, hi, 8)
+        cols = g.integers(0, N, 64)
+        hx, hxs = Q.quant_act(x[tok[rows]], 128, fmt)            # the oracle's own codes
+        wb = synth.device_normal_bf16((N, K), 0.01, "moe", "w", e)
+        hw, hws = X.quant_weight_mxfp4(bf16_bits(wb)[cols])
+        assert np.array_equal(u8(wq[e])[cols], hw) and np.array_equal(u8(ws[e])[cols], hws)
+        ref = G.dequant_act(hx, hxs, 128, fmt) @ X.dequant_mxfp4(hw, hws).T
+        got = F.bf16_decode(bf16_bits(y[torch.from_numpy(rows).cuda()]))[:, cols]
+        got_all.append(got.ravel())
+        ref_all.append(ref.ravel())
+    err = rel_fro(np.concatenate(got_all), np.concatenate(ref_all))
+    say(f"  sampled rel fro {err:.3e}")
+    assert err <= TOL
