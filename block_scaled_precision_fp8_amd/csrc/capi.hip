@@ -127,6 +127,14 @@ int32_t linear_launch(const void* x, int64_t ldx, const void* wq, const void* w_
     a.xstat = stat ? act_scale : nullptr;
     return hip_status(launch_block_gemm(a, st));
   }
+  if (blk == 128 && linear_xq(M, N, K)) {
+    // the large-M GEMM quantizes the activations in its K loop (xs: the
+    // static scale or null); the workspace holds only the K splits' partials
+    a.x_bf16 = (const uint16_t*)x; a.ldx = ldx;
+    a.xs = stat ? act_scale : nullptr;
+    a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    return hip_status(launch_block_gemm(a, st));
+  }
   // workspace: [xq M*K][x_scale M*G*4][gemm workspace], 256-byte aligned parts
   const int64_t G = (K + blk - 1) / blk;
   auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };

@@ -228,6 +228,12 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// s_waitcnt lgkmcnt(0): this wave's LDS stores are done (s_barrier alone
+// does not wait for them on gfx950)
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
+}
+
 // One fragment read from LDS.  The restrict-qualified pointer gives the
 // loads alias-scope information; without it the compiler assumes they may
 // read what the in-flight LDS-DMA of the next stage writes and waits for
@@ -370,12 +376,13 @@ __device__ __forceinline__ void swiglu_epilogue(v4f (&acc)[WN / 16][WM / 16], ui
 // with the X chunks g4 and g4 + 4 of the FP8 operand (the lane layout of
 // the FP4 x FP8 form, checked on the GPU), and passes its own group's scale.
 template <int FMT, int WAVES_M, int WAVES_N, int WM, int WN, bool GROUPED, bool W4 = false,
-          bool SWIGLU = false, bool SA = false, bool SW4 = false>
+          bool SWIGLU = false, bool SA = false, bool SW4 = false, bool XQ = false>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
     const uint8_t* __restrict__ xq, const void* __restrict__ xs, const uint8_t* __restrict__ wq,
     const void* __restrict__ wsc, const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
     int64_t M, int64_t N, int64_t K, const int32_t* __restrict__ seg, int E, int gsel,
-    float* __restrict__ part, int kbps, uint8_t* __restrict__ hq, void* __restrict__ hs) {
+    float* __restrict__ part, int kbps, uint8_t* __restrict__ hq, void* __restrict__ hs,
+    const uint16_t* __restrict__ xb, int64_t ldx) {
   // The body exists only in the device pass; the host pass needs nothing
   // but the launch stub of each instantiation.
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -404,7 +411,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
   // per-block loads otherwise.  (A runtime choice between the two would
   // make the compiler wait for every load of the step before using the
   // per-block scales, the next stage's DMA included.)
-  constexpr bool SCL = BM >= 128 && (FMT == 0 || (SA && !SWIGLU));
+  // XQ: X arrives as bf16 and is quantized here, one K block at a time
+  // (fp8_linear's fused large-M form): each stage's 1 x 128 act groups are
+  // loaded into registers with the weight DMA, encoded with the activation
+  // codec once they land, and written to the stage's X tile and to a
+  // per-stage scale row in LDS.  xs is then null (dynamic groups) or the
+  // static scheme's calibrated scale.
+  static_assert(!XQ || (!GROUPED && !W4 && !SWIGLU && !SA && BM == 128 && THREADS == 512),
+                "fused act quant: dense 128 x 256 tiles");
+  constexpr int XQJ = XQ ? BM * 16 / THREADS : 1;   // 16-byte bf16 loads per lane per stage
+  constexpr bool SCL = !XQ && BM >= 128 && (FMT == 0 || (SA && !SWIGLU));
   constexpr int SCH = FMT == 0 ? 8 : 16;
   constexpr int SROW = SCH * SB;            // bytes per row per chunk
   constexpr int SDW = SROW / 4;             // dword loads per row per chunk
@@ -421,9 +437,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
   constexpr int WSJ = SW4 ? BN * 8 / (64 * WAVES) : 0;
   static_assert(!SW4 || WSJ * 64 * WAVES == BN * 8, "weight-scale chunk / thread mismatch");
   __shared__ __attribute__((aligned(1024)))
-  uint8_t lds[STAGES * STAGE + (SCL ? 2 * SBUF : 0) + (SW4 ? 2 * WBUF : 0)];
+  uint8_t lds[STAGES * STAGE + (SCL ? 2 * SBUF : 0) + (SW4 ? 2 * WBUF : 0) + (XQ ? 2 * BM * 4 : 0)];
   uint8_t* const sbuf = lds + STAGES * STAGE;
   uint8_t* const wbuf = sbuf + (SCL ? 2 * SBUF : 0);
+  float* const sxq = (float*)(wbuf + (SW4 ? 2 * WBUF : 0));   // XQ: [2][BM] scales
   static_assert(!GROUPED || STAGES * STAGE >= 1025 * 4, "tile table fits the stage buffers");
   static_assert(!SWIGLU || WAVES_M * (WAVES_N / 2) * MI * NI * 1024 +
                                (WAVES_N > 2 ? WAVES_M * (WAVES_N / 2) * MI * 64 : 0) <=
@@ -504,6 +521,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
   float sa_reg[STAGES][MI];
   float sw_reg[STAGES];
   int sw4_reg[STAGES][W4 && !SW4 ? NI : 1];
+  // XQ: the next stage's bf16 X, 16 bytes per load; lane t takes row q / 16,
+  // 8-value chunk q % 16 of the K block (q = j THREADS + t), so the 16 lanes
+  // of a row are one quarter-wave
+  u32x4 xr[XQJ];
+  const uint16_t* const xrow = XQ ? xb + tl.m0 * ldx : nullptr;   // this tile's first row
 
   // issue one stage: X and W tiles into LDS buffer `buf`, scales into
   // registers; exactly LOADS vector-memory ops per lane, in this order.
@@ -511,11 +533,22 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
     uint8_t* sx = lds + buf * STAGE;
     uint8_t* sw = sx + XBYTES;
     const uint32_t kbyte = (uint32_t)kb * 128;
+    if constexpr (XQ) {
 #pragma unroll
-    for (int j = 0; j < XJ; ++j) {
-      const int q = (j * WAVES + wave) * 64 + lane;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, BSFP8_LDS(sx + (j * WAVES + wave) * 1024),
-                                               16, dma_src(q, mrows, kbyte), 0, 0, 0);
+      for (int j = 0; j < XQJ; ++j) {
+        const int q = j * THREADS + (int)threadIdx.x;
+        const int row = q >> 4;
+        const int64_t k = (int64_t)kbyte + (q & 15) * 8;
+        xr[j] = u32x4{0u, 0u, 0u, 0u};
+        if (row < mrows && k < K) xr[j] = *(const u32x4*)(xrow + row * ldx + k);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < XJ; ++j) {
+        const int q = (j * WAVES + wave) * 64 + lane;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, BSFP8_LDS(sx + (j * WAVES + wave) * 1024),
+                                                 16, dma_src(q, mrows, kbyte), 0, 0, 0);
+      }
     }
 #pragma unroll
     for (int j = 0; j < WJ; ++j) {
@@ -543,7 +576,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
                                                    off, 0, 0, 0);
         }
       }
-    } else {
+    } else if constexpr (!XQ) {
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
         const uint32_t off = saoff[i] == kOOB ? kOOB : saoff[i] + kb * SB;
@@ -625,7 +658,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
 #pragma unroll
       for (int ii = 0; ii < NI; ++ii) sw4[ii] = sw4_reg[buf][ii] & 0xff;
     }
-    if constexpr (SCL) {
+    if constexpr (XQ) {
+      // the scales this workgroup derived for the stage's rows
+#pragma unroll
+      for (int j = 0; j < MI; ++j) {
+        sa[j] = read_scale(sxq + buf * BM, wm * WM + j * 16 + l16);
+        if (FMT == 1) sa[j] = __int_as_float(__float_as_int(sa[j]) & 0xff);
+      }
+    } else if constexpr (SCL) {
       // this block's scales of the lane's token rows, from the chunk buffer
       const int rel = kb_cur - kb_begin;
       const uint8_t* sc = sbuf + ((rel / SCH) & 1) * SBUF + (rel % SCH) * SB;
@@ -647,8 +687,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
     for (int j = 0; j < MI; ++j) bx[j] = read_frag(sx + j * 16 * kRowBytes, ch0, ch1);
     // W fragments in groups of NG 16-row subtiles, read one group ahead:
     // group g + 1 is in flight while the MFMAs of group g run.  Scheduling
-    // fences keep that order (and bound the live fragments).
-    constexpr int NG = 2;
+    // fences keep that order (and bound the live fragments).  The dense
+    // 256 x 256 UE8M0 tile (no promotion FMAs) takes one subtile per group
+    // and interleaves each MFMA with one fragment read (3.4% faster over the
+    // DeepSeek-sized shapes, 8% at 4096 x 18432 x 7168; with fp32 scales the
+    // two-subtile groups measured best).
+    constexpr bool ONE = FMT == 1 && BM == 256 && !GROUPED && !W4 && !SWIGLU && !XQ;
+    constexpr int NG = ONE ? 1 : 2;
     constexpr int NGR = NI / NG;
     v8i aw[2][NG];
 #pragma unroll
@@ -671,8 +716,63 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
           else
             acc[g * NG + ii][j] = mfma_step<FMT>(acc[g * NG + ii][j], aw[g & 1][ii], bx[j], sa[j], sw);
         }
+      if constexpr (ONE) {
+#pragma unroll
+        for (int i = 0; i < NG * MI; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
     });
+  };
+
+  // XQ: encode the landed bf16 stage with the activation codec (the codes
+  // and scales fp8_quant_act writes for these rows and K block) into the X
+  // tile of buffer `buf` (row-swizzled 16-byte chunks, as the DMA lays them
+  // out) and its scale row
+  auto xquant = [&](int buf) {
+    uint8_t* sxl = lds + buf * STAGE;
+    float* sq = sxq + buf * BM;
+#pragma unroll
+    for (int j = 0; j < XQJ; ++j) {
+      const int q = j * THREADS + (int)threadIdx.x;
+      const int row = q >> 4, c16 = q & 15;
+      const u32x4 v = xr[j];
+      float f[8];
+      f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x); f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+      f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z); f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
+      uint2 codes;
+      float sv;
+      if constexpr (FMT == 0) {
+        // static scheme (xs carries the calibrated scale): x / s is not
+        // bounded by 448 and may overflow, so it divides directly too
+        const float sc = xs ? *(const float*)xs : act_scale_f32(amax);
+        if (xs || !(sc >= kMinNormal)) {
+          // subnormal scale: direct division (see div_by_rcp)
+          codes.x = act_encode4<0>(f[0], f[1], f[2], f[3], sc, 0);
+          codes.y = act_encode4<0>(f[4], f[5], f[6], f[7], sc, 0);
+        } else {
+          const float r = 1.0f / sc;
+          codes.x = act_encode4_rcp<0>(f[0], f[1], f[2], f[3], sc, r, 0);
+          codes.y = act_encode4_rcp<0>(f[4], f[5], f[6], f[7], sc, r, 0);
+        }
+        sv = sc;
+      } else {
+        const int e = xs ? (int)*(const uint8_t*)xs - 127 : ue8m0_exp(amax);
+        codes.x = act_encode4<1>(f[0], f[1], f[2], f[3], 0.0f, e);
+        codes.y = act_encode4<1>(f[4], f[5], f[6], f[7], 0.0f, e);
+        sv = __int_as_float(e + 127);
+      }
+      const int pc = (c16 >> 1) ^ ((row >> 1) & 7);
+      *(uint2*)(sxl + row * kRowBytes + pc * 16 + (c16 & 1) * 8) = codes;
+      if (c16 == 0) sq[row] = sv;
+    }
   };
 
   // prologue: the first stage
@@ -691,6 +791,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
       // stage kb landed (own loads), then everyone's loads landed and
       // everyone is done reading the buffer about to be refilled
       wait_vmcnt<0>();
+      if constexpr (XQ) {
+        xquant(s);
+        asm volatile("" ::: "memory");
+        wait_lgkmcnt0();
+      }
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       step(std::integral_constant<int, s>{}, kb + 1);
@@ -889,6 +994,9 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
     float swb[DEPTH];
     uint4 xa[XD], xb[XD];
     float sx[XD];
+    // FUSED: this lane's 32 bf16 activations of each block, loaded with the
+    // weights so that no block waits on a second round trip
+    uint4 xv[FUSED ? DEPTH : 1][4];
     // B32: the four groups' scales (fp32), or this lane's group's bytes
     float sx4[B32 ? DEPTH : 1][4], sw32[B32 ? DEPTH : 1][4];
 #pragma unroll
@@ -942,6 +1050,15 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
           if (k + 16 < K) wb[u] = ld_stream16(wrow + k + 16);
         }
       }
+      if constexpr (FUSED) {
+        const int64_t k0 = (int64_t)kb * 128 + kx0, k1 = (int64_t)kb * 128 + kx1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t k = (i < 2 ? k0 : k1) + 8 * (i & 1);
+          xv[u][i] = make_uint4(0, 0, 0, 0);
+          if (kb < KB && mvalid && k < K) xv[u][i] = *(const uint4*)(x + (int64_t)l16 * ldx + k);
+        }
+      }
       if constexpr (!FUSED) {
         // the quantized X fragment and its scale (L2-resident), issued with
         // the weight loads so their latencies overlap
@@ -965,17 +1082,10 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
     for (int u = 0; u < DEPTH; ++u) {
       const int kb = kb0 + u * kDecodeWaves;
       if (kb >= KB) break;
-      const int64_t k0 = (int64_t)kb * 128 + kx0, k1 = (int64_t)kb * 128 + kx1;
       v8i bx;
       float sa;
       if constexpr (FUSED) {
-        uint4 v[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t k = (i < 2 ? k0 : k1) + 8 * (i & 1);
-          v[i] = make_uint4(0, 0, 0, 0);
-          if (mvalid && k < K) v[i] = *(const uint4*)(x + (int64_t)l16 * ldx + k);
-        }
+        const uint4* v = xv[u];
         float f[32];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -1305,11 +1415,13 @@ template __global__ void gemm_b32_kernel<1, true>(const uint8_t* __restrict__, c
 #define BSFP8_INST(FMT, WMN, WNN, WM, WN, G, W4, SW, SA)                                      \
   BSFP8_INST2(FMT, WMN, WNN, WM, WN, G, W4, SW, SA, false)
 #define BSFP8_INST2(FMT, WMN, WNN, WM, WN, G, W4, SW, SA, SW4)                                \
-  template __global__ void gemm_lds_kernel<FMT, WMN, WNN, WM, WN, G, W4, SW, SA, SW4>(       \
+  BSFP8_INST3(FMT, WMN, WNN, WM, WN, G, W4, SW, SA, SW4, false)
+#define BSFP8_INST3(FMT, WMN, WNN, WM, WN, G, W4, SW, SA, SW4, XQ)                            \
+  template __global__ void gemm_lds_kernel<FMT, WMN, WNN, WM, WN, G, W4, SW, SA, SW4, XQ>(   \
       const uint8_t* __restrict__, const void* __restrict__, const uint8_t* __restrict__,     \
       const void* __restrict__, const uint16_t* __restrict__, uint16_t* __restrict__, int64_t, \
       int64_t, int64_t, const int32_t* __restrict__, int, int, float* __restrict__, int,      \
-      uint8_t* __restrict__, void* __restrict__);
+      uint8_t* __restrict__, void* __restrict__, const uint16_t* __restrict__, int64_t);
 #define BSFP8_INST_ALL(FMT)                                 \
   BSFP8_INST(FMT, 4, 2, 64, 128, false, false, false, false) \
   BSFP8_INST(FMT, 2, 4, 64, 64, false, false, false, false)  \
@@ -1348,6 +1460,10 @@ BSFP8_INST_W4G(1)
 BSFP8_INST2(1, 4, 2, 64, 128, true, true, false, false, true)
 BSFP8_INST2(1, 4, 2, 64, 128, true, true, false, true, true)
 #undef BSFP8_INST_W4G
+// fp8_linear's fused large-M form: bf16 X quantized inside the 128 x 256 tile
+BSFP8_INST3(0, 2, 4, 64, 64, false, false, false, false, false, true)
+BSFP8_INST3(1, 2, 4, 64, 64, false, false, false, false, false, true)
+#undef BSFP8_INST3
 #undef BSFP8_INST_UE8M0_STAGED
 #undef BSFP8_INST2
 #undef BSFP8_INST_ALL
@@ -1359,6 +1475,12 @@ BSFP8_INST2(1, 4, 2, 64, 128, true, true, false, true, true)
 constexpr int64_t kDecodeMaxM = 16;
 constexpr int64_t kDecodeFusedMaxNK = int64_t(1) << 24;
 constexpr int64_t kDecodeFusedMaxK = 6144;
+// fused act quant in the large-M GEMM: every 256-wide N tile re-encodes
+// its M x K activations, about seven VALU operations per value, against the
+// separate launch it saves.  Measured (fp32 and UE8M0 scales): 1.1-1.2x
+// faster while M K ceil(N / 256) <= 2^21 (e.g. M = 32 at 4096 -> 4096 or
+// 7168 -> 1536), break-even near 2^22, 0.55-0.9x beyond
+constexpr int64_t kLinearXqMaxWork = int64_t(1) << 21;
 
 // Large-M tile configurations (WAVES_M x WAVES_N waves, wave tile WM x WN,
 // two LDS stages): BM = WM WAVES_M, BN = WN WAVES_N.
@@ -1372,7 +1494,7 @@ constexpr int64_t kDecodeFusedMaxK = 6144;
 // Two stages wait for vmcnt(0) before each K block, which does not depend
 // on the completion order of the LDS-DMA loads and the scale loads.
 template <int FMT, int WMN, int WNN, int WM, int WN, bool GROUPED, bool W4 = false,
-          bool SW = false, bool SA = false, bool SW4 = false>
+          bool SW = false, bool SA = false, bool SW4 = false, bool XQ = false>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t st, int splits, int kbps, int gsel = 0) {
   constexpr int BM = WMN * WM, BN = WNN * WN;
   const int64_t NT = (a.N + BN - 1) / BN;
@@ -1389,10 +1511,10 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t st, int splits, int kbps, i
     tiles = (tiles + 7) / 8 * 8;                 // whole rounds over the 8 XCDs
   }
   float* part = splits > 1 ? (float*)a.workspace : nullptr;
-  hipLaunchKernelGGL((gemm_lds_kernel<FMT, WMN, WNN, WM, WN, GROUPED, W4, SW, SA, SW4>),
+  hipLaunchKernelGGL((gemm_lds_kernel<FMT, WMN, WNN, WM, WN, GROUPED, W4, SW, SA, SW4, XQ>),
                      dim3((unsigned)tiles), dim3(64 * WMN * WNN), 0, st, a.xq, a.xs, a.wq, a.ws,
                      GROUPED ? nullptr : a.bias, a.y, a.M, a.N, a.K, a.seg, a.E, gsel, part,
-                     kbps, a.hq, a.hs);
+                     kbps, a.hq, a.hs, XQ ? a.x_bf16 : nullptr, XQ ? a.ldx : (int64_t)0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || part == nullptr) return e;
   const int64_t MN = a.M * a.N;
@@ -1492,6 +1614,12 @@ hipError_t launch_lds(const GemmArgs& a, hipStream_t st) {
     return launch_cfg<FMT, 1, 4, 64, 64, true>(a, st, 1, kb, 2);
   } else {
     const Plan p = plan_dense(a.M, a.N, a.K);
+    if (a.x_bf16) {
+      // fp8_linear's fused form (linear_xq chose it: the plan's small tile),
+      // the same tile and K splits as fp8_block_gemm, so the same sums
+      return launch_cfg<FMT, 2, 4, 64, 64, false, false, false, false, false, true>(a, st, p.splits,
+                                                                                  p.kbps);
+    }
     const bool sa = ue8m0_aligned(a, p.splits, p.kbps);
     if (a.w4) {
       if (a.K % 128 == 0 && (FMT == 1 || !p.big)) {   // staged MXFP4 weight scales
@@ -1539,11 +1667,20 @@ bool linear_fused(int64_t M, int64_t N, int64_t K) {
   return M > 0 && M <= kDecodeMaxM && K <= kDecodeFusedMaxK && N * K <= kDecodeFusedMaxNK;
 }
 
+// fp8_linear quantizes the activations inside the large-M GEMM (128 x 256
+// tiles, the plan's choice) instead of staging them with a separate launch
+bool linear_xq(int64_t M, int64_t N, int64_t K) {
+  if (M <= kDecodeMaxM || N <= 0 || K <= 0) return false;
+  if (M * K * ((N + 255) / 256) > kLinearXqMaxWork) return false;
+  return !plan_dense(M, N, K).big;
+}
+
 size_t linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int blk) {
   if (M <= 0) return 0;
   auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
   if (blk == 32) return up((size_t)M * K) + up((size_t)M * ((K + 31) / 32) * 4);
   if (linear_fused(M, N, K)) return 0;   // quantization inside the decode kernel
+  if (linear_xq(M, N, K)) return gemm_workspace_bytes(M, N, K);   // inside the large-M GEMM
   const int64_t G = (K + 127) / 128;
   return up((size_t)M * K) + up((size_t)M * G * 4) + gemm_workspace_bytes(M, N, K);
 }

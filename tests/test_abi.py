@@ -143,7 +143,8 @@ def test_block_gemm_workspace_too_small():
 def test_decode_needs_no_workspace():
     """M <= 16 runs in one launch with no workspace; fp8_linear fuses the
     activation quantization there up to N K = 2^24 with K <= 6144 and stages
-    it beyond (every workgroup would re-quantize all of X)."""
+    it beyond (every workgroup would re-quantize all of X).  For M > 16 it
+    fuses it into the large-M GEMM on 128 x 256 tiles."""
     for M in (1, 16):
         assert L.workspace_size(L.OP_BLOCK_GEMM, M, 28672, 4096) == 0
         assert L.workspace_size(L.OP_LINEAR, M, 4096, 4096) == 0
@@ -151,7 +152,16 @@ def test_decode_needs_no_workspace():
         assert L.workspace_size(L.OP_LINEAR, M, 4104, 4096) > 0
         assert L.workspace_size(L.OP_LINEAR, M, 1536, 7168) > 0
         assert L.workspace_size(L.OP_LINEAR, M, 8192, 4096) > 0
-    assert L.workspace_size(L.OP_LINEAR, 17, 256, 256) > 0
+    # M > 16 on the 128 x 256 tile with M K ceil(N / 256) <= 2^21: the GEMM
+    # quantizes in its K loop, so the workspace is the K splits' partial
+    # sums only (none here); otherwise the codes and scales are staged
+    assert L.workspace_size(L.OP_LINEAR, 17, 256, 256) == 0
+    for (M, N, K) in ((40, 1024, 1536), (32, 4096, 4096), (32, 1536, 7168)):
+        assert L.gemm_kernel(M, N, K)[0] == L.GEMM_TILE_128x256
+        assert L.workspace_size(L.OP_LINEAR, M, N, K) == L.workspace_size(L.OP_BLOCK_GEMM, M, N, K)
+    for (M, N, K) in ((64, 4096, 4096), (128, 4096, 4096), (2048, 4096, 4096), (2048, 6144, 4096)):
+        assert L.workspace_size(L.OP_LINEAR, M, N, K) >= M * K + L.workspace_size(
+            L.OP_BLOCK_GEMM, M, N, K)
 
 
 def test_linear_argument_checks():
@@ -171,12 +181,12 @@ def test_linear_argument_checks():
              1 << 20, None) == L.OK
     assert f(FAKE, 128, FAKE, FAKE, None, FAKE, 16, 256, 256, 128, 128, 0, 0, None, FAKE,
              1 << 20, None) == L.EINVAL
-    need = L.workspace_size(L.OP_LINEAR, 64, 256, 256)
+    need = L.workspace_size(L.OP_LINEAR, 2048, 6144, 4096)
     assert need > 0
-    assert f(FAKE, 256, FAKE, FAKE, None, FAKE, 64, 256, 256, 128, 128, 0, 0, None, FAKE,
+    assert f(FAKE, 4096, FAKE, FAKE, None, FAKE, 2048, 6144, 4096, 128, 128, 0, 0, None, FAKE,
              need - 1, None) == L.ENOSPC
-    assert f(FAKE, 256, FAKE, FAKE, None, FAKE, 64, 256, 256, 128, 128, 1, 1, FAKE + 1, FAKE,
-             need - 1, None) == L.ENOSPC
+    assert f(FAKE, 4096, FAKE, FAKE, None, FAKE, 2048, 6144, 4096, 128, 128, 1, 1, FAKE + 1,
+             FAKE, need - 1, None) == L.ENOSPC
 
 
 def test_grouped_argument_checks():

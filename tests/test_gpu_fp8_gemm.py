@@ -446,3 +446,91 @@ def test_attention_projection_12288_sampled(M):
     err = rel_fro(got, ref)
     say(f"  sampled rel fro {err:.3e}")
     assert err <= TOL
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("M,N,K,ldx", [
+    (17, 256, 256, 256),          # one K block, one tile, ragged M
+    (40, 1024, 1536, 1536),       # K split in 4
+    (200, 520, 1040, 1040),       # ragged M, N and K (partial last K block), 3 splits
+    (32, 4096, 4096, 4096),       # 16 K splits: the largest problem the rule fuses
+    (150, 1000, 2048, 2560),      # a strided X view (row stride > K)
+    (520, 512, 512, 512),         # five M tiles
+])
+def test_linear_fused_large_m(M, N, K, ldx, fmt):
+    """fp8_linear with M > 16 on 128 x 256 tiles quantizes the activations in
+    the GEMM's K loop: bit-identical to fp8_quant_act + fp8_block_gemm (same
+    tile and K splits), within the bound of the oracle's product."""
+    import torch
+    from block_scaled_precision_fp8_amd import lib as L
+    assert L.gemm_kernel(M, N, K)[0] == L.GEMM_TILE_128x256
+    assert M * K * -(-N // 256) <= 2**21                         # the rule that fuses
+    assert L.workspace_size(L.OP_LINEAR, M, N, K) == L.workspace_size(L.OP_BLOCK_GEMM, M, N, K)
+    say(f"fused large-M linear M={M} N={N} K={K} ldx={ldx} fmt={fmt}")
+    xfull = synth.deepseek_acts(M, ldx, seed=M + K) if fmt else synth.llama_acts(M, ldx, seed=M + K)
+    x = np.ascontiguousarray(xfull[:, :K])
+    w = synth.normal_bf16((N, K), 0.02, "llama", "w", seed=N + K)
+    b = synth.normal_bf16((N,), 0.5, "llama", "bias", seed=N)
+    xd = to_dev_bf16(xfull)[:, :K]
+    wd, bd = to_dev_bf16(w), to_dev_bf16(b)
+    sdt = torch.float32 if fmt == 0 else torch.uint8
+    G_ = -(-K // 128)
+    xq = torch.empty((M, K), dtype=torch.uint8, device=wd.device)
+    xs = torch.empty((M, G_), dtype=sdt, device=wd.device)
+    wq = torch.empty((N, K), dtype=torch.uint8, device=wd.device)
+    ws = torch.empty((-(-N // 128), G_), dtype=sdt, device=wd.device)
+    L.fp8_quant_act(xd, xq, xs, scale_fmt=fmt)
+    L.fp8_quant_weight(wd, wq, ws, scale_fmt=fmt)
+    y1 = torch.empty((M, N), dtype=torch.bfloat16, device=wd.device)
+    y2 = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=wd.device)
+    L.fp8_block_gemm(xq, xs, wq, ws, y1, bias=bd, scale_fmt=fmt)
+    L.fp8_linear(xd, wq, ws, y2, bias=bd, scale_fmt=fmt)
+    torch.cuda.synchronize()
+    b1, b2 = bf16_bits(y1), bf16_bits(y2)
+    assert np.array_equal(b1, b2), f"{np.count_nonzero(b1 != b2)} outputs differ from quant + gemm"
+    hq, hs = Q.quant_act(x, 128, fmt)
+    assert np.array_equal(xq.cpu().numpy(), hq)
+    ref = G.block_gemm(hq, hs, *Q.quant_weight(w, 128, 128, fmt), bias=F.bf16_decode(b), fmt=fmt)
+    err = rel_fro(F.bf16_decode(b2), ref)
+    say(f"  rel fro {err:.3e}")
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_linear_fused_large_m_tiny_scales(fmt):
+    """The large-M in-loop quantization on rows whose groups have subnormal
+    scales (1 / s overflowing at 2^-128), zero and mixed groups, and the
+    static scheme with a subnormal scale: bit-identical to the two calls."""
+    import torch
+    from block_scaled_precision_fp8_amd import lib as L
+    M, K, N = 48, 4096, 512
+    assert L.gemm_kernel(M, N, K)[0] == L.GEMM_TILE_128x256
+    x = np.concatenate([_tiny_amax_acts(16, K)] * 3)
+    w = synth.normal_bf16((N, K), 2.0**100, "llama", "w", seed=13)
+    xd, wd = to_dev_bf16(x), to_dev_bf16(w)
+    sdt = torch.float32 if fmt == 0 else torch.uint8
+    xq = torch.empty((M, K), dtype=torch.uint8, device=xd.device)
+    xs = torch.empty((M, K // 128), dtype=sdt, device=xd.device)
+    wq = torch.empty((N, K), dtype=torch.uint8, device=xd.device)
+    ws = torch.empty((N // 128, K // 128), dtype=sdt, device=xd.device)
+    L.fp8_quant_weight(wd, wq, ws, scale_fmt=fmt)
+    ws_ = L.workspace_size(L.OP_LINEAR, M, N, K)
+    work = torch.empty(max(ws_, 16), dtype=torch.uint8, device=xd.device)
+    for stat in (None, "tiny"):
+        if stat is None:
+            L.fp8_quant_act(xd, xq, xs, scale_fmt=fmt)
+            sc = None
+        else:
+            sc = (torch.tensor([2.0**-130], dtype=torch.float32, device=xd.device) if fmt == 0
+                  else torch.tensor([3], dtype=torch.uint8, device=xd.device))
+            xs.view(-1)[0] = sc[0]
+            L.fp8_quant_act(xd, xq, xs, act_scheme=L.ACT_STATIC, scale_fmt=fmt)
+        y1 = torch.empty((M, N), dtype=torch.bfloat16, device=xd.device)
+        y2 = torch.empty_like(y1)
+        L.fp8_block_gemm(xq, xs, wq, ws, y1, scale_fmt=fmt, workspace=work)
+        L.fp8_linear(xd, wq, ws, y2, scale_fmt=fmt, workspace=work,
+                     act_scheme=L.ACT_DYNAMIC if stat is None else L.ACT_STATIC, act_scale=sc)
+        torch.cuda.synchronize()
+        b1, b2 = bf16_bits(y1), bf16_bits(y2)
+        bad = np.argwhere(b1 != b2)
+        assert bad.size == 0, f"{stat}: rows {np.unique(bad[:, 0])} differ"
