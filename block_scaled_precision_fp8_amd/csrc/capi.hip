@@ -341,20 +341,21 @@ int32_t fp8_grouped_gemm(const void* xq, const void* x_scale, const void* wq,
   int32_t r = check_gemm(xq, x_scale, wq, w_scale_inv, nullptr, y, T, N, K, block_n, block_k,
                          scale_fmt);
   if (r != BSFP8_OK) return r;
-  if (block_n != 128) return BSFP8_ENOTSUP;       // experts: 128 x 128 blocks
   if (T == 0) return BSFP8_OK;
   if (!seg_offsets || ((uintptr_t)seg_offsets & 3u)) return BSFP8_EINVAL;
   const size_t need = grouped_workspace_bytes(T, N, K, E);
   if (workspace_bytes < need) return BSFP8_ENOSPC;
   if (need && (!workspace || !al16(workspace))) return BSFP8_EINVAL;
-  const int64_t NT = (N + 255) / 256;
+  const int64_t NT = block_n == 32 ? (N + 127) / 128 : (N + 255) / 256;
   if (!fits_i32(((T + 127) / 128 + E) * NT)) return BSFP8_EINVAL;
+  if (!fits_i32(T * ((K + block_k - 1) / block_k))) return BSFP8_EINVAL;
   r = check_device(stream);
   if (r != BSFP8_OK) return r;
   GemmArgs a{};
   a.xq = (const uint8_t*)xq; a.xs = x_scale; a.wq = (const uint8_t*)wq; a.ws = w_scale_inv;
   a.bias = nullptr; a.y = (uint16_t*)y; a.M = T; a.N = N; a.K = K; a.fmt = scale_fmt;
   a.seg = seg_offsets; a.E = E; a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+  a.blk = block_n;
   return hip_status(launch_grouped_gemm(a, (hipStream_t)stream));
 }
 

@@ -1169,11 +1169,15 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
 // takes for group g is half (u & 1) of logical chunk u >> 1, u = 4 g + g4,
 // and the chunk swizzle keeps those reads free of bank conflicts.
 // ------------------------------------------------------------------------
-template <int FMT, bool SA>
+//
+// GROUPED: the MoE expert GEMM over contiguous row segments with (32, 32)
+// expert weight blocks, on the same tile table as the large-M kernel (one
+// expert class, 128-row M tiles).
+template <int FMT, bool SA, bool GROUPED = false>
 __global__ __launch_bounds__(256, 2) void gemm_b32_kernel(
     const uint8_t* __restrict__ xq, const void* __restrict__ xs, const uint8_t* __restrict__ wq,
     const void* __restrict__ wsc, const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
-    int64_t M, int64_t N, int64_t K) {
+    int64_t M, int64_t N, int64_t K, const int32_t* __restrict__ seg, int E) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int BM = 128, BN = 128, WAVES = 4;
   constexpr int MI = 4, NI = 4;                      // 64 x 64 per wave
@@ -1192,22 +1196,30 @@ __global__ __launch_bounds__(256, 2) void gemm_b32_kernel(
   constexpr int SJ = BM * 8 / (64 * WAVES);          // chunk DMA loads per lane
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE + (SCL ? 2 * SBUF : 0)];
   uint8_t* const sbuf = lds + 2 * STAGE;
-  const Tile tl = dense_tile<BM, BN>(M, N, 1);
+  static_assert(!GROUPED || 2 * STAGE >= 1025 * 4, "tile table fits the stage buffers");
+  Tile tl;
+  // the grouped tile table lives in the stage buffers until the tile is known
+  if (GROUPED) tl = grouped_tile<BM, BN, 64 * WAVES>(seg, E, N, (int*)lds, 0);
+  else tl = dense_tile<BM, BN>(M, N, 1);
   if (!tl.valid) return;
+  if (GROUPED) __syncthreads();            // every lookup done before the first DMA
   const int KB = (int)((K + 127) / 128);
   const int GS = (int)((K + 31) / 32);               // scale groups per row
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave & 1, wn = wave >> 1;
   const int l16 = lane & 15, g4 = lane >> 4;
-  const int64_t mrows = min((int64_t)BM, M - tl.m0);
+  const int64_t mrows = min((int64_t)BM, (GROUPED ? tl.mlim : M) - tl.m0);
   const int64_t nrows = min((int64_t)BN, N - tl.n0);
+  const int64_t NBS = (N + 31) / 32;
+  // this tile's expert: weights (E, N, K), scales (E, NBS, GS)
+  const uint8_t* wbase = wq + (int64_t)tl.expert * N * K;
+  const uint8_t* wsb = (const uint8_t*)wsc + (int64_t)tl.expert * NBS * GS * SB;
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(xq + tl.m0 * K, mrows * K);
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(wq + tl.n0 * K, nrows * K);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(wbase + tl.n0 * K, nrows * K);
   const __amdgpu_buffer_rsrc_t rsa =
       make_rsrc((const uint8_t*)xs + tl.m0 * GS * SB, mrows * GS * SB);
-  const int64_t NBS = (N + 31) / 32;
-  const __amdgpu_buffer_rsrc_t rsw = make_rsrc(wsc, NBS * GS * SB);
+  const __amdgpu_buffer_rsrc_t rsw = make_rsrc(wsb, NBS * GS * SB);
   auto dma_src = [&](int q, int64_t rows, uint32_t kbyte) -> uint32_t {
     const int row = q >> 3, c = (q & 7) ^ ((row >> 1) & 7);
     const uint32_t kc = kbyte + c * 16;
@@ -1390,24 +1402,24 @@ __global__ __launch_bounds__(256, 2) void gemm_b32_kernel(
     const int L = p * 64 * WAVES + (int)threadIdx.x;
     const int row = L / CPR, c = L % CPR;
     const int64_t m = tl.m0 + row, n = tl.n0 + c * 8;
-    if (m < M && n < N)
+    if (row < mrows && n < N)
       *(uint4*)(y + m * N + n) = *(const uint4*)(lds + row * (BN * 2) + ((c ^ (row & (CPR - 1))) << 4));
   }
 #endif
 }
 
-template __global__ void gemm_b32_kernel<0, false>(const uint8_t* __restrict__, const void* __restrict__,
-                                            const uint8_t* __restrict__, const void* __restrict__,
-                                            const uint16_t* __restrict__, uint16_t* __restrict__,
-                                            int64_t, int64_t, int64_t);
-template __global__ void gemm_b32_kernel<1, false>(const uint8_t* __restrict__, const void* __restrict__,
-                                            const uint8_t* __restrict__, const void* __restrict__,
-                                            const uint16_t* __restrict__, uint16_t* __restrict__,
-                                            int64_t, int64_t, int64_t);
-template __global__ void gemm_b32_kernel<1, true>(const uint8_t* __restrict__, const void* __restrict__,
-                                           const uint8_t* __restrict__, const void* __restrict__,
-                                           const uint16_t* __restrict__, uint16_t* __restrict__,
-                                           int64_t, int64_t, int64_t);
+#define BSFP8_B32(FMT, SA, G)                                                                  \
+  template __global__ void gemm_b32_kernel<FMT, SA, G>(                                        \
+      const uint8_t* __restrict__, const void* __restrict__, const uint8_t* __restrict__,      \
+      const void* __restrict__, const uint16_t* __restrict__, uint16_t* __restrict__, int64_t, \
+      int64_t, int64_t, const int32_t* __restrict__, int);
+BSFP8_B32(0, false, false)
+BSFP8_B32(1, false, false)
+BSFP8_B32(1, true, false)
+BSFP8_B32(0, false, true)
+BSFP8_B32(1, false, true)
+BSFP8_B32(1, true, true)
+#undef BSFP8_B32
 
 // Explicit instantiations of every tile configuration the dispatcher below
 // can launch (the host pass does not always emit launch stubs for kernel
@@ -1455,6 +1467,7 @@ BSFP8_INST2(1, 2, 4, 64, 64, false, true, false, true, true)
   BSFP8_INST2(FMT, 4, 2, 64, 128, true, true, false, false, false) \
   BSFP8_INST2(FMT, 1, 4, 64, 64, true, true, false, false, false)  \
   BSFP8_INST2(FMT, 1, 4, 64, 64, true, true, false, false, true)
+BSFP8_INST2(0, 2, 4, 64, 64, true, true, false, false, true)
 BSFP8_INST_W4G(0)
 BSFP8_INST_W4G(1)
 BSFP8_INST2(1, 4, 2, 64, 128, true, true, false, false, true)
@@ -1601,7 +1614,11 @@ hipError_t launch_lds(const GemmArgs& a, hipStream_t st) {
         else
           e = launch_cfg<FMT, 4, 2, 64, 128, true, true>(a, st, 1, kb, 1);
       } else {
-        e = launch_cfg<FMT, 4, 2, 64, 128, true, true>(a, st, 1, kb, 1);
+        // fp32 activation scales: the large experts on 128 x 256 tiles, whose
+        // staged weight scales fit (the 256 x 256 tile loads a scale byte per
+        // lane, subtile and K block: 2x slower on the MoE gate/up shape)
+        e = sw4 ? launch_cfg<FMT, 2, 4, 64, 64, true, true, false, false, true>(a, st, 1, kb, 1)
+                : launch_cfg<FMT, 4, 2, 64, 128, true, true>(a, st, 1, kb, 1);
       }
       if (e != hipSuccess) return e;
       return sw4 ? launch_cfg<FMT, 1, 4, 64, 64, true, true, false, false, true>(a, st, 1, kb, 2)
@@ -1745,28 +1762,31 @@ hipError_t launch_decode(const GemmArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <bool G>
 hipError_t launch_b32(const GemmArgs& a, hipStream_t st) {
-  int64_t tiles = (a.M + 127) / 128 * ((a.N + 127) / 128);
-  tiles = (tiles + 7) / 8 * 8;                   // whole rounds over the 8 XCDs
-  if (a.fmt == 0)
-    hipLaunchKernelGGL((gemm_b32_kernel<0, false>), dim3((unsigned)tiles), dim3(256), 0, st, a.xq,
-                       a.xs, a.wq, a.ws, a.bias, a.y, a.M, a.N, a.K);
-  else if (a.K % 128 == 0)   // UE8M0 rows of K/32 bytes are dword-aligned: staged scales
-    hipLaunchKernelGGL((gemm_b32_kernel<1, true>), dim3((unsigned)tiles), dim3(256), 0, st, a.xq,
-                       a.xs, a.wq, a.ws, a.bias, a.y, a.M, a.N, a.K);
-  else
-    hipLaunchKernelGGL((gemm_b32_kernel<1, false>), dim3((unsigned)tiles), dim3(256), 0, st, a.xq,
-                       a.xs, a.wq, a.ws, a.bias, a.y, a.M, a.N, a.K);
+  const int64_t NT = (a.N + 127) / 128;
+  // grouped: every expert adds at most one partial M tile
+  int64_t tiles = G ? ((a.M + 127) / 128 + a.E) * NT : (a.M + 127) / 128 * NT;
+  if (!G) tiles = (tiles + 7) / 8 * 8;           // whole rounds over the 8 XCDs
+  const uint16_t* bias = G ? nullptr : a.bias;
+#define BSFP8_B32L(FMT, SA)                                                                       \
+  hipLaunchKernelGGL((gemm_b32_kernel<FMT, SA, G>), dim3((unsigned)tiles), dim3(256), 0, st, a.xq, \
+                     a.xs, a.wq, a.ws, bias, a.y, a.M, a.N, a.K, a.seg, a.E)
+  if (a.fmt == 0) BSFP8_B32L(0, false);
+  else if (a.K % 128 == 0) BSFP8_B32L(1, true);   // UE8M0 rows of K/32 bytes dword-aligned: staged
+  else BSFP8_B32L(1, false);
+#undef BSFP8_B32L
   return hipGetLastError();
 }
 
 hipError_t launch_block_gemm(const GemmArgs& a, hipStream_t st) {
-  if (a.blk == 32 && a.M > kDecodeMaxM) return launch_b32(a, st);
+  if (a.blk == 32 && a.M > kDecodeMaxM) return launch_b32<false>(a, st);
   if (a.M <= kDecodeMaxM) return a.fmt == 0 ? launch_decode<0>(a, st) : launch_decode<1>(a, st);
   return a.fmt == 0 ? launch_lds<0, false>(a, st) : launch_lds<1, false>(a, st);
 }
 
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t st) {
+  if (a.blk == 32) return launch_b32<true>(a, st);
   return a.fmt == 0 ? launch_lds<0, true>(a, st) : launch_lds<1, true>(a, st);
 }
 

@@ -174,7 +174,8 @@ BSFP8_API int32_t fp8_quant_weight(const void* w, int64_t N, int64_t K, int64_t 
  * enum, misalignment); ENOTSUP (other block sizes, K > 2^22); ENOSPC.
  * fp8_linear shares these limits (with (32, 32) blocks its workspace is
  * bsfp8_workspace_size(BSFP8_OP_LINEAR_B32, ...)); fp8_grouped_gemm takes
- * 128 x 128 blocks only.
+ * (128, 128) and (32, 32) blocks, fp8_grouped_gemm_silu_mul_quant
+ * (128, 128) only.
  */
 BSFP8_API int32_t fp8_block_gemm(const void* xq, const void* x_scale, const void* wq,
                        const void* w_scale_inv, const void* bias, void* y,
@@ -236,8 +237,10 @@ BSFP8_API int32_t fp8_linear_noalloc(const void* x, int64_t ldx, const void* wq,
  * every expert e, rows [off[e], off[e+1]) of Y are the fp8_block_gemm of the
  * same rows of (xq, x_scale) with expert e's (wq[e], w_scale_inv[e]).
  *
- *   xq           E4M3 [T][K];  x_scale [T][ceil(K/128)] (fp32 | UE8M0).
- *   wq           E4M3 [E][N][K];  w_scale_inv [E][ceil(N/128)][ceil(K/128)].
+ *   xq           E4M3 [T][K];  x_scale [T][ceil(K/B)] (fp32 | UE8M0).
+ *   wq           E4M3 [E][N][K];  w_scale_inv [E][ceil(N/B)][ceil(K/B)].
+ *   block_n, block_k  (B, B) = (128, 128), or (32, 32) with 1 x 32 act
+ *                groups ([FG-FP8] §九); other sizes ENOTSUP.
  *   seg_offsets  DEVICE int32 [E+1]: off[0] = 0, nondecreasing, off[E] = T.
  *                This is a precondition and is not checked (checking would
  *                need a device synchronisation).

@@ -326,5 +326,9 @@ def test_block32_argument_checks():
     assert _gemm(bn=32, bk=32, M=0) == L.OK and _gemm(bn=32, bk=64) == L.ENOTSUP
     g = lib.fp8_grouped_gemm
     args = [FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, 64, 256, 256, 32, 32, 0, None, 0, None]
-    assert g(*args) == L.ENOTSUP                   # experts: 128 x 128 blocks only
+    assert g(*args) == L.EHIP                      # (32, 32) experts: past the checks
+    bad = list(args); bad[10] = 64; bad[11] = 64
+    assert g(*bad) == L.ENOTSUP                    # other sizes
+    bad = list(args); bad[10] = 32; bad[11] = 128
+    assert g(*bad) == L.ENOTSUP                    # mixed sizes
     assert L.workspace_size(L.OP_LINEAR_B32, 64, 256, 256) >= 64 * 256 + 64 * 8 * 4

@@ -151,3 +151,40 @@ def test_block32_gemm_full_size_sampled():
     err = rel_fro(got, ref)
     say(f"  sampled rel fro {err:.3e}")
     assert err <= TOL
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("counts,N,K", [
+    ([3, 0, 1, 6, 2], 128, 256),
+    ([0, 0, 130, 0, 1, 257, 64, 0], 200, 1040),   # ragged N and K, partial M tiles
+    ([300], 264, 512),
+    (list(np.random.default_rng(6).integers(0, 40, 33)), 384, 640),
+])
+def test_grouped_gemm_block32(counts, N, K, fmt):
+    """MoE experts with (32, 32) weight blocks and 1 x 32 activation groups
+    against the oracle's per-expert block-by-block product; empty experts,
+    ragged N and K."""
+    import torch
+    from block_scaled_precision_fp8_amd import lib as L
+    E = len(counts)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    T = int(off[-1])
+    say(f"grouped (32, 32) E={E} T={T} N={N} K={K} fmt={fmt}")
+    x = synth.deepseek_acts(T, K, seed=K) if fmt else synth.llama_acts(T, K, seed=K)
+    xq, xs = Q.quant_act(x, 32, fmt)
+    wq = np.empty((E, N, K), np.uint8)
+    ws = np.empty((E, -(-N // 32), -(-K // 32)), np.float32 if fmt == 0 else np.uint8)
+    for e in range(E):
+        wq[e], ws[e] = Q.quant_weight(synth.normal_bf16((N, K), 0.02, "moe", "w", e, seed=K),
+                                      32, 32, fmt)
+    yf = torch.full((T * N + 64,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    y = yf[:T * N].view(T, N)
+    L.fp8_grouped_gemm(to_dev(xq), to_dev(xs), to_dev(wq), to_dev(ws), to_dev(off), y,
+                       block_n=32, block_k=32, scale_fmt=fmt)
+    torch.cuda.synchronize()
+    assert torch.isnan(yf[T * N:].float()).all(), "wrote past the output"
+    got = F.bf16_decode(bf16_bits(y))
+    assert np.isfinite(got).all(), "unwritten rows"
+    err = rel_fro(got, G.grouped_gemm(xq, xs, wq, ws, off, 32, 32, fmt))
+    say(f"  rel fro {err:.3e}")
+    assert err <= TOL
