@@ -680,7 +680,7 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
                 "traffic": traffic,
-                "kernel": "gemm_lds_kernel<0,4,2,64,128,false,false,false,false,false> (fp32 scales, 256x256 "
+                "kernel": "gemm_lds_kernel<0,4,2,64,128,false,false,false,false,false,false> (fp32 scales, 256x256 "
                           "tiles), large-M block-scaled GEMM",
                 "launches_per_step": r["n_big"],
                 "avg_launch_us": round(r["big_ms"] / r["n_big"] * 1e3, 2),

@@ -21,6 +21,9 @@ runs (a third, TCC_HIT_sum TCC_MISS_sum, adds the L2 hit rate): texture-data sta
 stalls, and the L1-to-L2 request count and average latency, with the
 concurrency they imply (Little's law).
 `summary`: the text form of one bench.py JSON line.
+`trace`: from a --kernel-trace run of the default bench command and that
+run's JSON line, the dominant kernel's average over the timed steps, the
+roofline fraction it implies, and the gaps between kernels in that window.
 """
 
 import argparse
@@ -233,6 +236,48 @@ def stats(a):
     print("\n".join(lines))
 
 
+def trace(a):
+    """kernel-trace run of bench.py: the dominant kernel's average duration
+    over the timed steps of the Llama step (its launches in order: warm-up
+    steps, timed steps, the untimed detail pass), the roofline fraction it
+    implies, the bench line of the same run, and the gaps between kernels
+    inside the timed window"""
+    rows = list(csv.DictReader(open(a.trace)))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    with open(a.json) as f:
+        d = json.loads(f.read().strip().splitlines()[-1])
+    rl = d["roofline"]
+    per = int(rl["launches_per_step"])
+    idx = [i for i, r in enumerate(rows) if a.kernel in r["Kernel_Name"]]
+    lo, hi = a.warmup * per, (a.warmup + a.steps) * per
+    timed = idx[lo:hi]
+    dur = [(int(rows[i]["End_Timestamp"]) - int(rows[i]["Start_Timestamp"])) / 1e3 for i in timed]
+    avg = sum(dur) / len(dur)
+    gflop = float(rl["algorithmic_gflop_per_launch"])
+    t0, t1 = int(rows[timed[0]]["Start_Timestamp"]), int(rows[timed[-1]]["End_Timestamp"])
+    win = [r for r in rows if int(r["Start_Timestamp"]) >= t0 and int(r["End_Timestamp"]) <= t1]
+    busy = sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in win) / 1e3
+    span = (t1 - t0) / 1e3
+    lines = [
+        f"# dominant kernel over the timed steps, from one kernel-trace run of bench.py; command: {a.cmd}",
+        f"kernel: {a.kernel}",
+        f"dispatches in the run: {len(idx)}; timed-step dispatches: {len(dur)} "
+        f"(occurrences {lo}..{hi - 1}: {a.warmup} warm-up steps x {per} come first)",
+        f"average duration over the timed steps (us): {avg:.2f}",
+        f"algorithmic GFLOP per launch: {gflop}",
+        f"achieved TFLOP/s: {gflop / avg * 1e3:.1f}; fraction of the 5000 TFLOP/s dense FP8 peak: "
+        f"{gflop / avg * 1e3 / 5000.0:.4f}",
+        f"the same run's bench line: value {d['value']} TFLOP/s, ms_per_step {d['ms_per_step']}, "
+        f"roofline achieved {rl['achieved']} frac {rl['frac']} (HIP events: avg_launch_us "
+        f"{rl['avg_launch_us']})",
+        f"timed window: {span:.1f} us, {len(win)} kernels, {busy:.1f} us busy, "
+        f"{span - busy:.1f} us between kernels ({(span - busy) / len(win):.2f} us per kernel)",
+    ]
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def summary(a):
     """one bench.py JSON line -> the text summary kept under profiles/"""
     with open(a.json) as f:
@@ -285,13 +330,21 @@ def main():
     l.add_argument("--pmc3", default=None, help="optional TCC_HIT_sum TCC_MISS_sum run")
     l.add_argument("--cmd", required=True)
     l.add_argument("--out", required=True)
+    tr = sub.add_parser("trace")
+    tr.add_argument("--trace", required=True)
+    tr.add_argument("--json", required=True)
+    tr.add_argument("--cmd", required=True)
+    tr.add_argument("--out", required=True)
+    tr.add_argument("--kernel", default=GEMM_KERNEL)
+    tr.add_argument("--warmup", type=int, default=5)
+    tr.add_argument("--steps", type=int, default=20)
     b = sub.add_parser("summary")
     b.add_argument("--json", required=True)
     b.add_argument("--cmd", required=True)
     b.add_argument("--out", required=True)
     a = ap.parse_args()
     {"traffic": traffic, "stats": stats, "summary": summary, "mfma": mfma,
-     "decode": decode, "l1": l1}[a.what](a)
+     "decode": decode, "l1": l1, "trace": trace}[a.what](a)
 
 
 if __name__ == "__main__":
