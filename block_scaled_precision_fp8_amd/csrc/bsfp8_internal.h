@@ -83,26 +83,42 @@ __device__ __forceinline__ uint32_t act_encode4(float a, float b, float c, float
 
 constexpr float kMinNormal = 0x1p-126f;   // smallest normal fp32
 
-// fl32(x / s) from r = fl32(1 / s) in three operations (Markstein's
-// correction step: q = RN(x r), the residual x - q s is exact with an FMA,
-// and RN(q + residual r) is the correctly rounded quotient when r is the
-// correctly rounded reciprocal and no intermediate underflows).  Valid for a
-// NORMAL scale s only: a subnormal s (group amax below 448 * 2^-126) can
-// make 1 / s overflow (s < 2^-128) and the residual round, so callers divide
-// directly there.  With s normal, quotients small enough to underflow are
-// far below the smallest E4M3 subnormal and encode to a signed zero either
-// way, so the codes equal those of x / s.
-__device__ __forceinline__ float div_by_rcp(float x, float s, float r) {
-  const float q = x * r;
-  const float res = fmaf(-q, s, x);
-  return fmaf(res, r, q);
+// fl32(x / s) for a NORMAL scale s from its reciprocal, in four operations
+// per value instead of an IEEE division: q = RN(x' r), the residual
+// x' - q s' (exact with an FMA) and q' = RN(q + residual r), Markstein's
+// correction, which gives the correctly rounded quotient when r = RN(1 / s')
+// and nothing underflows.  Two details make that hold for every x the
+// activation codec meets:
+//   * s < 2^-60: x and s are both multiplied by 2^64 first (exact; the
+//     quotient is unchanged), so a subnormal x cannot leave a residual below
+//     the smallest subnormal -- without this, x subnormal against a small
+//     normal s rounded a tie the wrong way (an E4M3 code off by one);
+//   * the result takes the sign of x: for x = -0 the correction step returns
+//     +0 (-0 + +0), where the quotient is -0 (code 0x80).
+// Against IEEE division (CPU emulation with exact rounding, every finite bf16
+// x against 6000 scales from 448 * 2^-126 up): identical E4M3 codes; the fp32
+// quotients differ only where they lie far below the smallest E4M3 subnormal
+// (code +-0 either way).  Subnormal scales and the static scheme (x / s not
+// bounded by 448) still divide directly.
+struct RcpDiv {
+  float s, r, m;   // rescaled scale, its correctly rounded reciprocal, the rescale
+};
+__device__ __forceinline__ RcpDiv rcp_div(float s) {
+  const float m = s < 0x1p-60f ? 0x1p64f : 1.0f;
+  const float sm = s * m;
+  return RcpDiv{sm, 1.0f / sm, m};
+}
+__device__ __forceinline__ float div_by_rcp(float x, const RcpDiv& d) {
+  const float xm = x * d.m;
+  const float q = xm * d.r;
+  const float res = fmaf(-q, d.s, xm);
+  return copysignf(fmaf(res, d.r, q), x);
 }
 template <int FMT>
 __device__ __forceinline__ uint32_t act_encode4_rcp(float a, float b, float c, float d,
-                                                    float s, float r, int e) {
+                                                    const RcpDiv& dv, int e) {
   if (FMT == 0)
-    return e4m3x4(div_by_rcp(a, s, r), div_by_rcp(b, s, r), div_by_rcp(c, s, r),
-                  div_by_rcp(d, s, r));
+    return e4m3x4(div_by_rcp(a, dv), div_by_rcp(b, dv), div_by_rcp(c, dv), div_by_rcp(d, dv));
   return e4m3x4(ldexpf(a, -e), ldexpf(b, -e), ldexpf(c, -e), ldexpf(d, -e));
 }
 

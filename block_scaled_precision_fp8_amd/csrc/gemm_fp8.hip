@@ -758,9 +758,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
           codes.x = act_encode4<0>(f[0], f[1], f[2], f[3], sc, 0);
           codes.y = act_encode4<0>(f[4], f[5], f[6], f[7], sc, 0);
         } else {
-          const float r = 1.0f / sc;
-          codes.x = act_encode4_rcp<0>(f[0], f[1], f[2], f[3], sc, r, 0);
-          codes.y = act_encode4_rcp<0>(f[4], f[5], f[6], f[7], sc, r, 0);
+          const RcpDiv dv = rcp_div(sc);
+          codes.x = act_encode4_rcp<0>(f[0], f[1], f[2], f[3], dv, 0);
+          codes.y = act_encode4_rcp<0>(f[4], f[5], f[6], f[7], dv, 0);
         }
         sv = sc;
       } else {
@@ -1117,11 +1117,11 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
           for (int i = 0; i < 8; ++i)
             bx[i] = (int)act_encode4<FMT>(f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3], s, e);
         } else {
-          const float r = FMT == 0 ? 1.0f / s : 0.0f;
+          const RcpDiv dv = rcp_div(FMT == 0 ? s : 1.0f);
 #pragma unroll
           for (int i = 0; i < 8; ++i)
             bx[i] = (int)act_encode4_rcp<FMT>(f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3],
-                                              s, r, e);
+                                              dv, e);
         }
         sa = FMT == 0 ? s : __int_as_float(e + 127);
       } else {

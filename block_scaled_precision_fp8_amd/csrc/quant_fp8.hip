@@ -12,7 +12,8 @@
 //
 // Scale formats (section 七 of the guide; readings for the open points):
 //   FLOAT: s = fl32(amax / 448) (1.0 for amax == 0), code = E4M3(fl32(x / s))
-//          with IEEE (correctly rounded) fp32 division.
+//          with the correctly rounded fp32 quotient (reciprocal plus one
+//          exact correction for a normal s, IEEE division otherwise).
 //   UE8M0: s = 2^e, e = ceil(log2(amax / 448)) clamped to [-127, 127] (fp32
 //          scales round *up* to UE8M0), code = E4M3(x * 2^-e) (exact scaling).
 #include "bsfp8_internal.h"
@@ -43,6 +44,10 @@ __device__ __forceinline__ float amax8(const Unpacked& u) {
 
 // Encode eight values of one group with the group's scale.  Returns the
 // codes packed little-endian; writes the stored scale representation.
+// fp32 scales divide by the correctly rounded reciprocal with one exact
+// correction (div_by_rcp: the same E4M3 codes as IEEE x / s for a normal s,
+// at four operations per value instead of an IEEE division each); a
+// subnormal scale divides directly.
 template <int FMT>
 __device__ __forceinline__ uint2 encode8(const Unpacked& u, float amax, float* s_f32, int* s_exp) {
   const float s = FMT == 0 ? act_scale_f32(amax) : 0.0f;
@@ -50,8 +55,14 @@ __device__ __forceinline__ uint2 encode8(const Unpacked& u, float amax, float* s
   *s_f32 = s;
   *s_exp = e;
   uint2 r;
-  r.x = act_encode4<FMT>(u.f[0], u.f[1], u.f[2], u.f[3], s, e);
-  r.y = act_encode4<FMT>(u.f[4], u.f[5], u.f[6], u.f[7], s, e);
+  if (FMT == 0 && s >= kMinNormal) {
+    const RcpDiv dv = rcp_div(s);
+    r.x = act_encode4_rcp<FMT>(u.f[0], u.f[1], u.f[2], u.f[3], dv, e);
+    r.y = act_encode4_rcp<FMT>(u.f[4], u.f[5], u.f[6], u.f[7], dv, e);
+  } else {
+    r.x = act_encode4<FMT>(u.f[0], u.f[1], u.f[2], u.f[3], s, e);
+    r.y = act_encode4<FMT>(u.f[4], u.f[5], u.f[6], u.f[7], s, e);
+  }
   return r;
 }
 

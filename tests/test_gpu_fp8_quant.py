@@ -170,3 +170,55 @@ def test_weight_quant_parity(N, K, sigma, work, fmt):
         assert np.array_equal(ws.view(np.uint32), rs.view(np.uint32))
     else:
         assert np.array_equal(ws, rs)
+
+
+def _subnormal_groups(M, K, seed):
+    """Groups whose amax (one element) lies between 448 * 2^-126 and 2^-100,
+    so the fp32 scale is a small normal number, and whose other elements are
+    random bf16 subnormals and negative zeros: the region where dividing by
+    the reciprocal needs its rescaling and sign care to match x / s."""
+    g = np.random.default_rng(seed)
+    x = g.integers(0, 0x80, size=(M, K), dtype=np.uint16) | (g.integers(0, 2, size=(M, K)) << 15).astype(np.uint16)
+    x[g.random((M, K)) < 0.02] = 0x8000                       # -0
+    for r in range(M):
+        for gi in range(K // 128):
+            e = g.uniform(-117.2, -100.0)
+            a = synth.f32_to_bf16_bits(np.float32([2.0 ** e]))[0]
+            x[r, gi * 128 + g.integers(0, 128)] = a | (0x8000 if g.random() < 0.5 else 0)
+    return x
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_act_quant_subnormal_values_small_scales(fmt):
+    x = _subnormal_groups(256, 4096, seed=31)
+    _check_act(x, fmt)
+
+
+def test_fused_paths_subnormal_values_small_scales():
+    """The same groups through fp8_linear's fused decode (M <= 16) and
+    in-loop large-M (M = 32) quantization: bit-identical to the two calls
+    (large weights keep the products of the tiny codes visible)."""
+    import torch
+    from block_scaled_precision_fp8_amd import lib as L
+    K, N = 4096, 512
+    w = synth.normal_bf16((N, K), 2.0**100, "llama", "w", seed=33)
+    wd = to_dev_bf16(w)
+    wq = torch.empty((N, K), dtype=torch.uint8, device=wd.device)
+    ws = torch.empty((N // 128, K // 128), dtype=torch.float32, device=wd.device)
+    L.fp8_quant_weight(wd, wq, ws)
+    for M in (16, 32):
+        x = _subnormal_groups(M, K, seed=32 + M)
+        xd = to_dev_bf16(x)
+        assert L.workspace_size(L.OP_LINEAR, M, N, K) == L.workspace_size(L.OP_BLOCK_GEMM, M, N, K)
+        xq = torch.empty((M, K), dtype=torch.uint8, device=wd.device)
+        xs = torch.empty((M, K // 128), dtype=torch.float32, device=wd.device)
+        L.fp8_quant_act(xd, xq, xs)
+        y1 = torch.empty((M, N), dtype=torch.bfloat16, device=wd.device)
+        y2 = torch.empty_like(y1)
+        L.fp8_block_gemm(xq, xs, wq, ws, y1)
+        L.fp8_linear(xd, wq, ws, y2)
+        torch.cuda.synchronize()
+        rq, _ = Q.quant_act(x, 128, 0)
+        assert np.array_equal(u8(xq), rq)
+        from gpu_util import bf16_bits
+        assert np.array_equal(bf16_bits(y1), bf16_bits(y2)), f"M={M}: fused differs"
