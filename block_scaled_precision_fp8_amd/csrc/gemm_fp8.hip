@@ -1156,6 +1156,168 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
 }
 
 // ------------------------------------------------------------------------
+// Persistent decode kernel (4 <= M <= 16, FP8 weights in 128 x 128 blocks,
+// X quantized beforehand).  Same 16-row tiles, lane layout and per-block
+// arithmetic as gemm_decode_kernel, but the grid is the workgroups that fit
+// on the device at once and each walks the tiles t = blockIdx.x,
+// + gridDim.x, ...: the whole M x K of X codes (and the activation scales)
+// is copied to LDS once per workgroup and serves all its tiles.  In
+// gemm_decode_kernel each lane loads its X fragment per block from L2, a
+// second stream as large as the weights' at M = 16 that held that kernel to
+// about 3.3 TB/s on weight-bound shapes (4.5 TB/s at M = 1).  X rows are
+// padded by 16 bytes so that the 16 token rows of a fragment read fall in
+// distinct LDS banks.
+// The K blocks of a tile are dealt to the 16 waves (wave w takes w + 16 j),
+// DEPTH per chunk; every chunk's loads are issued before the previous chunk
+// is multiplied, across tile boundaries, so a chunk stays in flight through
+// the MFMAs, the LDS reduction of the waves' partial tiles and the store.
+// Chunk slots past a tile's blocks load nothing (out-of-range buffer offsets
+// read zeros) and are multiplied like the others: every chunk issues the
+// same loads and consumes all of them.
+// ------------------------------------------------------------------------
+constexpr int kPersXsBytes = 4096;   // activation scales (M x KB)
+constexpr int kPersXlBytes = 163840 - 2 * kDecodeWaves * 64 * 16 - kPersXsBytes;   // X codes
+
+template <int FMT, int DEPTH>
+__global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_pers_kernel(
+    const uint8_t* __restrict__ xq, const void* __restrict__ xs, const uint8_t* __restrict__ wq,
+    const void* __restrict__ wsc, const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
+    int M, int64_t N, int64_t K, int ntiles) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __shared__ v4f red[2][kDecodeWaves][64];
+  __shared__ __attribute__((aligned(16))) uint8_t sxs[kPersXsBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sxl[kPersXlBytes];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const bool mvalid = l16 < M;
+  const int KB = (int)((K + 127) / 128);
+  const int64_t NB = (N + 127) / 128;
+  constexpr int SB = FMT == 0 ? 4 : 1;
+  const int64_t KP = K + 16;                                // X row pitch in LDS
+  const int nbw = (KB + kDecodeWaves - 1) / kDecodeWaves;   // blocks per wave and tile
+  const int C = (nbw + DEPTH - 1) / DEPTH;                  // chunks per tile
+
+  // two chunks' registers (index S = 0, 1, always a constant): the lane's
+  // 32 W bytes of a block (K [32 g4, 32 g4 + 32), the K assignment of
+  // gemm_decode_kernel, so both kernels form the same sums) and the wave's
+  // weight-block scale per slot
+  uint4 wa[2][DEPTH], wb[2][DEPTH];
+  float sw[2][DEPTH];
+  auto issue = [&](auto sc, int t, int c) __attribute__((always_inline)) {
+    constexpr int S = decltype(sc)::value;
+    const bool tin = t < ntiles;
+    const int64_t n0 = (int64_t)t * 16;
+    const int64_t rows = tin ? min((int64_t)16, N - n0) : 0;
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(wq + (tin ? n0 * K : 0), rows * K);
+    const int64_t nblk = n0 >> 7;
+#pragma unroll
+    for (int u = 0; u < DEPTH; ++u) {
+      const int kb = wave + kDecodeWaves * (c * DEPTH + u);
+      const int64_t k = (int64_t)kb * 128 + g4 * 32;
+      const bool kin = kb < KB;
+      const uint32_t ow = (uint32_t)(l16 * K + k);
+      u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rw, kin && k < K ? ow : kOOB, 0, 2);   // nt
+      wa[S][u] = make_uint4(v.x, v.y, v.z, v.w);
+      v = __builtin_amdgcn_raw_buffer_load_b128(rw, kin && k + 16 < K ? ow + 16 : kOOB, 0, 2);
+      wb[S][u] = make_uint4(v.x, v.y, v.z, v.w);
+      // the wave's weight-block scale: one uniform address, a scalar load
+      // (clamped in range; slots past the blocks multiply zeros)
+      sw[S][u] = load_scale<FMT>(wsc, min(nblk * KB + kb, NB * KB - 1));
+    }
+  };
+
+  int t0 = blockIdx.x, c0 = 0;       // the launcher sizes the grid <= ntiles
+  issue(std::integral_constant<int, 0>{}, t0, c0);   // in flight during the copy below
+
+  // activation scales (M x KB) and codes (M x K), once per workgroup
+  {
+    const int nbytes = M * KB * SB;  // launcher: <= kPersXsBytes
+    for (int i = threadIdx.x * 4; i < nbytes; i += 64 * kDecodeWaves * 4) {
+      if (i + 4 <= nbytes) {
+        *(uint32_t*)(sxs + i) = *(const uint32_t*)((const uint8_t*)xs + i);
+      } else {
+        for (int b = i; b < nbytes; ++b) sxs[b] = ((const uint8_t*)xs)[b];
+      }
+    }
+    const int k16 = (int)(K / 16);
+    const int nch = M * k16;         // launcher: M * KP <= kPersXlBytes
+    for (int i = threadIdx.x; i < nch; i += 64 * kDecodeWaves) {
+      const int m = i / k16, c = i - m * k16;
+      *(uint4*)(sxl + m * KP + c * 16) = *(const uint4*)(xq + (int64_t)m * K + c * 16);
+    }
+  }
+  __syncthreads();
+
+  auto compute = [&](auto sc, int c, v4f& acc) __attribute__((always_inline)) {
+    constexpr int S = decltype(sc)::value;
+#pragma unroll
+    for (int u = 0; u < DEPTH; ++u) {
+      const int kb = wave + kDecodeWaves * (c * DEPTH + u);
+      const int64_t k = (int64_t)kb * 128 + g4 * 32;
+      uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
+      const uint8_t* p = sxl + l16 * KP + k;
+      if (mvalid && k < K) a = *(const uint4*)p;
+      if (mvalid && k + 16 < K) b = *(const uint4*)(p + 16);
+      float sa = FMT == 0 ? 0.0f : __int_as_float(127);
+      if (mvalid && kb < KB)
+        sa = FMT == 0 ? ((const float*)sxs)[l16 * KB + kb] : __int_as_float((int)sxs[l16 * KB + kb]);
+      acc = mfma_step<FMT>(acc, join(wa[S][u], wb[S][u]), join(a, b), sa, sw[S][u]);
+    }
+  };
+  // the waves' partial tiles summed through LDS (two buffers: a wave may
+  // write the next tile's partial while wave 0 still reads this one)
+  int par = 0;
+  auto finish = [&](int t, v4f& acc) __attribute__((always_inline)) {
+    red[par][wave][lane] = acc;
+    acc = v4f{0.f, 0.f, 0.f, 0.f};
+    wait_lgkmcnt0();                 // this wave's LDS write is done
+    __builtin_amdgcn_s_barrier();    // no wait for the chunk in flight
+    asm volatile("" ::: "memory");
+    if (wave == 0) {
+      v4f sum = red[par][0][lane];
+#pragma unroll
+      for (int w = 1; w < kDecodeWaves; ++w) sum += red[par][w][lane];
+      const int64_t n = (int64_t)t * 16 + 4 * g4;
+      if (mvalid && n < N) store_out4(y, N, l16, n, sum, bias);
+    }
+    par ^= 1;
+  };
+
+  // Chunk q of this workgroup: tile blockIdx.x + (q / C) gridDim.x, chunk
+  // q % C of it.  The loop runs an even number of chunks (one all-zero chunk
+  // past the end when needed) and tests only at its bottom, so the set
+  // issued last in an iteration is always multiplied in the next: no path
+  // back to the loop head carries unconsumed loads, which would make the
+  // compiler wait for them before reusing their registers.
+  const int nT = (ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int Q = nT * C;
+  const int QP = (Q + 1) & ~1;
+  auto advance = [&](int& t, int& c) __attribute__((always_inline)) {
+    if (++c == C) { c = 0; t += gridDim.x; }
+  };
+  int t1 = t0, c1 = c0;              // chunk q + 1
+  advance(t1, c1);
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  for (int q = 0; q < QP; q += 2) {
+    issue(std::integral_constant<int, 1>{}, t1, c1);   // past the last tile: no loads
+    compute(std::integral_constant<int, 0>{}, c0, acc);
+    if (q < Q && c0 == C - 1) finish(t0, acc);
+    int t2 = t1, c2 = c1;
+    advance(t2, c2);
+    issue(std::integral_constant<int, 0>{}, t2, c2);
+    compute(std::integral_constant<int, 1>{}, c1, acc);
+    if (q + 1 < Q && c1 == C - 1) finish(t1, acc);
+    t0 = t2;
+    c0 = c2;
+    t1 = t2;
+    c1 = c2;
+    advance(t1, c1);
+  }
+#endif
+}
+
+// ------------------------------------------------------------------------
 // (32, 32) weight blocks with 1 x 32 activation groups (the fine-grained FP8
 // guide, section 九, names weight_block_size=(32, 32) among the non-default
 // blocks its tests cover).  A 128-wide K block then holds four
@@ -1713,6 +1875,55 @@ int gemm_kind(int64_t M, int64_t N, int64_t K, int* splits) {
   return p.big ? BSFP8_GEMM_TILE_256x256 : BSFP8_GEMM_TILE_128x256;
 }
 
+// compute units of the current device, queried once per device
+int cu_count() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cache[dev] = cus;
+  }
+  return cache[dev];
+}
+
+template <int FMT, int DEPTH>
+hipError_t launch_pers(const GemmArgs& a, hipStream_t st, int ntiles, int res) {
+  const int grid = ntiles < res ? ntiles : res;
+  hipLaunchKernelGGL((gemm_decode_pers_kernel<FMT, DEPTH>), dim3((unsigned)grid),
+                     dim3(64 * kDecodeWaves), 0, st, a.xq, a.xs, a.wq, a.ws, a.bias, a.y, (int)a.M,
+                     a.N, a.K, ntiles);
+  return hipGetLastError();
+}
+
+// The persistent decode kernel where it measured faster than
+// gemm_decode_kernel: at least 4 token rows whose codes and scales fit its
+// LDS, and several tiles per resident workgroup or long rows (1.1-1.4x at
+// M = 4..16 on 4096 x 28672, 7168 x 18432, 1536 x 24576, 14336 x 4096; at
+// M <= 2, or one tile of short rows per workgroup, the copy of X costs more
+// than its loads).  Chunk depth from the blocks each wave takes per tile:
+// the depth (2 or 3: 128 VGPRs at 16 waves) that pads the fewest slots.
+// Returns false when the shape is not one of those.
+template <int FMT>
+bool launch_decode_pers(const GemmArgs& a, hipStream_t st, hipError_t* err) {
+  const int64_t KB = (a.K + 127) / 128;
+  if (a.M < 4 || a.M * (a.K + 16) > kPersXlBytes || a.M * KB * (FMT == 0 ? 4 : 1) > kPersXsBytes)
+    return false;
+  const int res = cu_count();        // its LDS holds one workgroup per CU
+  const int ntiles = (int)((a.N + 15) / 16);
+  if (res <= 0 || !(2 * (int64_t)ntiles >= 3 * (int64_t)res || KB >= 48)) return false;
+  const int nbw = (int)((KB + kDecodeWaves - 1) / kDecodeWaves);
+  int d = nbw <= 3 ? nbw : ((nbw + 2) / 3 * 3 - nbw <= (nbw + 1) / 2 * 2 - nbw ? 3 : 2);
+  switch (d) {
+    case 1: *err = launch_pers<FMT, 1>(a, st, ntiles, res); break;
+    case 2: *err = launch_pers<FMT, 2>(a, st, ntiles, res); break;
+    default: *err = launch_pers<FMT, 3>(a, st, ntiles, res); break;
+  }
+  return true;
+}
+
 template <int FMT>
 hipError_t launch_decode(const GemmArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)((a.N + 15) / 16));
@@ -1751,6 +1962,8 @@ hipError_t launch_decode(const GemmArgs& a, hipStream_t st) {
     else BSFP8_DEC4(false, false);
 #undef BSFP8_DEC4
   } else {
+    hipError_t e = hipSuccess;
+    if (launch_decode_pers<FMT>(a, st, &e)) return e;
     if (sxl)
       hipLaunchKernelGGL((gemm_decode_kernel<FMT, false, false, false, true>), grid, block, 0, st,
                          a.xq, a.xs, nullptr, (int64_t)0, a.wq, a.ws, a.bias, a.y, (int)a.M, a.N,

@@ -94,6 +94,32 @@ def test_block_gemm_scale_staging(M, N, K, fmt):
     assert err <= TOL
 
 
+@pytest.mark.parametrize("M,N,K,fmt,bias", [
+    (4, 6144, 1792, 0, True),     # 384 tiles over the resident workgroups; one block per wave
+    (16, 6400, 4096, 1, False),   # 400 tiles: some workgroups one tile (an all-zero chunk)
+    (8, 6160, 6160, 0, False),    # ragged K and N; two chunks of two blocks per tile
+    (4, 2056, 14352, 0, True),    # long ragged rows: 113 blocks, four chunks of two
+    (6, 1032, 18432, 1, False),   # 144 blocks: three chunks of three, ragged last tile
+])
+def test_decode_persistent_parity(M, N, K, fmt, bias):
+    """Decode shapes (4 <= M <= 16) on the persistent kernel: the M x K codes
+    staged in LDS, chunks prefetched across tiles, chunk slots past a tile's
+    blocks, a final all-zero chunk, ragged K and N, against the oracle."""
+    from block_scaled_precision_fp8_amd import lib as L
+    say(f"persistent decode M={M} N={N} K={K} fmt={fmt} bias={bias}")
+    assert L.gemm_kernel(M, N, K)[0] == L.GEMM_DECODE
+    x = synth.deepseek_acts(M, K, seed=K) if fmt else synth.llama_acts(M, K, seed=K)
+    w = synth.normal_bf16((N, K), 0.02, "llama", "w", seed=N)
+    b = synth.normal_bf16((N,), 0.5, "llama", "bias", seed=N) if bias else None
+    h, d = _quant_dev(x, w, fmt)
+    y = _gemm_dev(d, M, N, b, fmt)
+    ref = G.block_gemm(*h, bias=None if b is None else F.bf16_decode(b), fmt=fmt)
+    assert np.isfinite(y).all(), "unwritten outputs"
+    err = rel_fro(y, ref)
+    say(f"  rel fro {err:.3e}")
+    assert err <= TOL
+
+
 @pytest.mark.parametrize("M,K,N,fmt,gen", [
     (2048, 4096, 28672, 0, "llama"), (16, 14336, 4096, 0, "llama"),
     (128, 4096, 6144, 0, "llama"), (4096, 7168, 18432, 1, "deepseek"),
@@ -174,7 +200,9 @@ def test_linear_fused_quant_every_bf16_pattern(fmt):
                                    (1, 8200, 256), (5, 264, 4112),
                                    # either side of the fused-quantization bound
                                    # (N K <= 2^24, K <= 6144)
-                                   (1, 2728, 6144), (16, 4104, 4096), (4, 1536, 7168)])
+                                   (1, 2728, 6144), (16, 4104, 4096), (4, 1536, 7168),
+                                   # fused kernel against the persistent decode kernel
+                                   (8, 2048, 6144)])
 def test_linear_matches_two_calls(M, N, K, fmt):
     import torch
     from block_scaled_precision_fp8_amd import lib as L
