@@ -1178,11 +1178,12 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
 constexpr int kPersXsBytes = 4096;   // activation scales (M x KB)
 constexpr int kPersXlBytes = 163840 - 2 * kDecodeWaves * 64 * 16 - kPersXsBytes;   // X codes
 
-template <int FMT, int DEPTH>
+template <int FMT, int DEPTH, bool FUSED = false>
 __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_pers_kernel(
     const uint8_t* __restrict__ xq, const void* __restrict__ xs, const uint8_t* __restrict__ wq,
     const void* __restrict__ wsc, const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
-    int M, int64_t N, int64_t K, int ntiles) {
+    int M, int64_t N, int64_t K, int ntiles, const uint16_t* __restrict__ x, int64_t ldx,
+    const void* __restrict__ xstat) {
 #if defined(__HIP_DEVICE_COMPILE__)
   __shared__ v4f red[2][kDecodeWaves][64];
   __shared__ __attribute__((aligned(16))) uint8_t sxs[kPersXsBytes];
@@ -1231,7 +1232,53 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_pers_kernel(
   issue(std::integral_constant<int, 0>{}, t0, c0);   // in flight during the copy below
 
   // activation scales (M x KB) and codes (M x K), once per workgroup
-  {
+  if constexpr (FUSED) {
+    // FUSED: quantized here from the bf16 rows x (row stride ldx) with the
+    // activation codec, to the codes and scales fp8_quant_act writes: one
+    // 1 x 128 group per quarter-wave, 8 values per lane, the group amax
+    // gathered over the quarter-wave's 16 lanes; xstat: the static scheme's
+    // calibrated scale.  (Every workgroup repeats this M x K quantization, so
+    // the launcher keeps it to small M.)
+    const int ql = threadIdx.x & 15;
+    const int ngroups = M * KB;
+    for (int gi = threadIdx.x >> 4; gi < ngroups; gi += 4 * kDecodeWaves) {
+      const int m = gi / KB, g = gi - m * KB;
+      const int64_t k0 = (int64_t)g * 128 + ql * 8;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (k0 < K) v = *(const uint4*)(x + (int64_t)m * ldx + k0);
+      const float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                          bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+      float sc = 0.0f;
+      int e = 0;
+      if (xstat) {
+        if (FMT == 0) sc = *(const float*)xstat;
+        else e = (int)*(const uint8_t*)xstat - 127;
+      } else {
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+        if (FMT == 0) sc = act_scale_f32(amax);
+        else e = ue8m0_exp(amax);
+      }
+      uint2 codes;
+      if (FMT == 0 && (xstat || !(sc >= kMinNormal))) {
+        // a subnormal or static scale: divide directly (as the other fused paths)
+        codes.x = act_encode4<FMT>(f[0], f[1], f[2], f[3], sc, e);
+        codes.y = act_encode4<FMT>(f[4], f[5], f[6], f[7], sc, e);
+      } else {
+        const RcpDiv dv = rcp_div(FMT == 0 ? sc : 1.0f);
+        codes.x = act_encode4_rcp<FMT>(f[0], f[1], f[2], f[3], dv, e);
+        codes.y = act_encode4_rcp<FMT>(f[4], f[5], f[6], f[7], dv, e);
+      }
+      if (k0 < K) *(uint2*)(sxl + m * KP + k0) = codes;
+      if (ql == 0) {
+        if (FMT == 0) ((float*)sxs)[gi] = sc;
+        else sxs[gi] = (uint8_t)(e + 127);
+      }
+    }
+  } else {
     const int nbytes = M * KB * SB;  // launcher: <= kPersXsBytes
     for (int i = threadIdx.x * 4; i < nbytes; i += 64 * kDecodeWaves * 4) {
       if (i + 4 <= nbytes) {
@@ -1842,7 +1889,33 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return p.splits > 1 ? (size_t)p.splits * M * N * sizeof(float) : 0;
 }
 
+// The persistent decode kernel where it measured faster than
+// gemm_decode_kernel: X codes and scales that fit its LDS, and several tiles
+// per resident workgroup (counted for 256 CUs) or long rows; below 4 token
+// rows (no X reuse worth its copy) only with at least two blocks per wave
+// and tile.  1.1-1.4x at M = 4..16 on 4096 x 28672, 7168 x 18432,
+// 1536 x 24576, 14336 x 4096; 1.03-1.1x at M = 1..3 on the long-row and
+// many-tile shapes; slower on one tile of short rows per workgroup.
+// (The fp32 activation scales, M KB 4 bytes, fit whenever the codes do.)
+bool decode_pers(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || M > kDecodeMaxM || N <= 0 || K <= 0) return false;
+  const int64_t KB = (K + 127) / 128;
+  if (M * (K + 16) > kPersXlBytes || M * KB * 4 > kPersXsBytes) return false;
+  const int64_t ntiles = (N + 15) / 16;
+  const int64_t nbw = (KB + kDecodeWaves - 1) / kDecodeWaves;
+  if (!(2 * ntiles >= 3 * 256 || KB >= 48)) return false;
+  return M >= 4 || nbw >= 2;
+}
+
+// fp8_linear's one-launch decode forms: gemm_decode_kernel quantizing per
+// block (every workgroup re-encodes X, so only while N K is small), or the
+// persistent kernel quantizing X once per workgroup while M K is small
+// enough that this prologue costs less than a quantization launch
+// (measured: faster up to 4 x 7168 and 2 x 18432, slower at 4 x 14336 and
+// 16 x 4096)
+constexpr int64_t kPersFusedMaxMK = 40960;
 bool linear_fused(int64_t M, int64_t N, int64_t K) {
+  if (M > 0 && M * K <= kPersFusedMaxMK && decode_pers(M, N, K)) return true;
   return M > 0 && M <= kDecodeMaxM && K <= kDecodeFusedMaxK && N * K <= kDecodeFusedMaxNK;
 }
 
@@ -1889,39 +1962,31 @@ int cu_count() {
   return cache[dev];
 }
 
-template <int FMT, int DEPTH>
+template <int FMT, int DEPTH, bool FUSED>
 hipError_t launch_pers(const GemmArgs& a, hipStream_t st, int ntiles, int res) {
   const int grid = ntiles < res ? ntiles : res;
-  hipLaunchKernelGGL((gemm_decode_pers_kernel<FMT, DEPTH>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((gemm_decode_pers_kernel<FMT, DEPTH, FUSED>), dim3((unsigned)grid),
                      dim3(64 * kDecodeWaves), 0, st, a.xq, a.xs, a.wq, a.ws, a.bias, a.y, (int)a.M,
-                     a.N, a.K, ntiles);
+                     a.N, a.K, ntiles, FUSED ? a.x_bf16 : nullptr, FUSED ? a.ldx : (int64_t)0,
+                     FUSED ? a.xstat : nullptr);
   return hipGetLastError();
 }
 
-// The persistent decode kernel where it measured faster than
-// gemm_decode_kernel: at least 4 token rows whose codes and scales fit its
-// LDS, and several tiles per resident workgroup or long rows (1.1-1.4x at
-// M = 4..16 on 4096 x 28672, 7168 x 18432, 1536 x 24576, 14336 x 4096; at
-// M <= 2, or one tile of short rows per workgroup, the copy of X costs more
-// than its loads).  Chunk depth from the blocks each wave takes per tile:
-// the depth (2 or 3: 128 VGPRs at 16 waves) that pads the fewest slots.
-// Returns false when the shape is not one of those.
-template <int FMT>
-bool launch_decode_pers(const GemmArgs& a, hipStream_t st, hipError_t* err) {
+// chunk depth from the blocks each wave takes per tile: the depth (2 or 3:
+// 128 VGPRs at 16 waves) that pads the fewest slots
+template <int FMT, bool FUSED>
+hipError_t launch_pers_depth(const GemmArgs& a, hipStream_t st) {
   const int64_t KB = (a.K + 127) / 128;
-  if (a.M < 4 || a.M * (a.K + 16) > kPersXlBytes || a.M * KB * (FMT == 0 ? 4 : 1) > kPersXsBytes)
-    return false;
-  const int res = cu_count();        // its LDS holds one workgroup per CU
   const int ntiles = (int)((a.N + 15) / 16);
-  if (res <= 0 || !(2 * (int64_t)ntiles >= 3 * (int64_t)res || KB >= 48)) return false;
+  const int res = cu_count();        // its LDS holds one workgroup per CU
+  if (res <= 0) return hipErrorInvalidDevice;
   const int nbw = (int)((KB + kDecodeWaves - 1) / kDecodeWaves);
-  int d = nbw <= 3 ? nbw : ((nbw + 2) / 3 * 3 - nbw <= (nbw + 1) / 2 * 2 - nbw ? 3 : 2);
+  const int d = nbw <= 3 ? nbw : ((nbw + 2) / 3 * 3 - nbw <= (nbw + 1) / 2 * 2 - nbw ? 3 : 2);
   switch (d) {
-    case 1: *err = launch_pers<FMT, 1>(a, st, ntiles, res); break;
-    case 2: *err = launch_pers<FMT, 2>(a, st, ntiles, res); break;
-    default: *err = launch_pers<FMT, 3>(a, st, ntiles, res); break;
+    case 1: return launch_pers<FMT, 1, FUSED>(a, st, ntiles, res);
+    case 2: return launch_pers<FMT, 2, FUSED>(a, st, ntiles, res);
+    default: return launch_pers<FMT, 3, FUSED>(a, st, ntiles, res);
   }
-  return true;
 }
 
 template <int FMT>
@@ -1932,7 +1997,10 @@ hipError_t launch_decode(const GemmArgs& a, hipStream_t st) {
   // several token rows share the staging (at M = 1 its prologue costs more
   // than the one scale row's loads it saves)
   const bool sxl = a.M >= 4 && a.M * ((a.K + 127) / 128) * (a.fmt == 0 ? 4 : 1) <= kDecodeXsBytes;
-  if (a.x_bf16) {
+  const bool pers = decode_pers(a.M, a.N, a.K);
+  if (a.x_bf16 && pers && a.M * a.K <= kPersFusedMaxMK) {
+    return launch_pers_depth<FMT, true>(a, st);
+  } else if (a.x_bf16) {
     hipLaunchKernelGGL((gemm_decode_kernel<FMT, true>), grid, block, 0, st, nullptr, nullptr,
                        a.x_bf16, a.ldx, a.wq, a.ws, a.bias, a.y, (int)a.M, a.N, a.K, a.xstat);
   } else if (a.blk == 32) {
@@ -1961,9 +2029,9 @@ hipError_t launch_decode(const GemmArgs& a, hipStream_t st) {
     else if (swl) BSFP8_DEC4(false, true);
     else BSFP8_DEC4(false, false);
 #undef BSFP8_DEC4
+  } else if (pers) {
+    return launch_pers_depth<FMT, false>(a, st);
   } else {
-    hipError_t e = hipSuccess;
-    if (launch_decode_pers<FMT>(a, st, &e)) return e;
     if (sxl)
       hipLaunchKernelGGL((gemm_decode_kernel<FMT, false, false, false, true>), grid, block, 0, st,
                          a.xq, a.xs, nullptr, (int64_t)0, a.wq, a.ws, a.bias, a.y, (int)a.M, a.N,

@@ -142,16 +142,22 @@ def test_block_gemm_workspace_too_small():
 
 def test_decode_needs_no_workspace():
     """M <= 16 runs in one launch with no workspace; fp8_linear fuses the
-    activation quantization there up to N K = 2^24 with K <= 6144 and stages
-    it beyond (every workgroup would re-quantize all of X).  For M > 16 it
-    fuses it into the large-M GEMM on 128 x 256 tiles."""
-    for M in (1, 16):
+    activation quantization there up to N K = 2^24 with K <= 6144, and with
+    M K <= 40960 also on the persistent decode kernel's shapes (at least 384
+    16-row tiles or 48 K blocks; below 4 rows two blocks per wave): X
+    quantized once per workgroup.  Elsewhere it stages it (every workgroup
+    of the per-block form would re-quantize all of X).  For M > 16 it fuses
+    it into the large-M GEMM on 128 x 256 tiles."""
+    for M in (1, 2, 3, 16):
         assert L.workspace_size(L.OP_BLOCK_GEMM, M, 28672, 4096) == 0
         assert L.workspace_size(L.OP_LINEAR, M, 4096, 4096) == 0
         assert L.workspace_size(L.OP_LINEAR, M, 2728, 6144) == 0
-        assert L.workspace_size(L.OP_LINEAR, M, 4104, 4096) > 0
-        assert L.workspace_size(L.OP_LINEAR, M, 1536, 7168) > 0
-        assert L.workspace_size(L.OP_LINEAR, M, 8192, 4096) > 0
+        assert L.workspace_size(L.OP_LINEAR, M, 4104, 4096) > 0   # 257 tiles of 32 blocks
+        for (N, K) in ((1536, 7168), (8192, 4096), (4096, 14336), (7168, 18432)):
+            fused = M * K <= 40960
+            assert (L.workspace_size(L.OP_LINEAR, M, N, K) == 0) == fused, (M, N, K)
+        # one block per wave and tile (K <= 2048): staged below 4 rows
+        assert (L.workspace_size(L.OP_LINEAR, M, 24576, 1536) == 0) == (M >= 4)
     # M > 16 on the 128 x 256 tile with M K ceil(N / 256) <= 2^21: the GEMM
     # quantizes in its K loop, so the workspace is the K splits' partial
     # sums only (none here); otherwise the codes and scales are staged

@@ -202,7 +202,10 @@ def test_linear_fused_quant_every_bf16_pattern(fmt):
                                    # (N K <= 2^24, K <= 6144)
                                    (1, 2728, 6144), (16, 4104, 4096), (4, 1536, 7168),
                                    # fused kernel against the persistent decode kernel
-                                   (8, 2048, 6144)])
+                                   (8, 2048, 6144),
+                                   # the persistent kernel quantizing X itself
+                                   (1, 1536, 7168), (2, 8192, 4096), (1, 1032, 14352),
+                                   (16, 6144, 1536), (4, 1032, 7168)])
 def test_linear_matches_two_calls(M, N, K, fmt):
     import torch
     from block_scaled_precision_fp8_amd import lib as L
@@ -355,8 +358,10 @@ def _tiny_amax_acts(M, K, seed=11):
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
-@pytest.mark.parametrize("M", [16, 5, 1])
-def test_linear_fused_quant_tiny_scales(fmt, M):
+@pytest.mark.parametrize("M,N", [(16, 512), (5, 512), (1, 512),
+                                 # the persistent decode kernel's in-launch form
+                                 (1, 8192), (2, 8192), (5, 8192)])
+def test_linear_fused_quant_tiny_scales(fmt, M, N):
     """fp8_linear's in-launch quantization on groups whose scale is subnormal
     (amax below, at and above 448 * 2^-128, where 1 / s overflows, and
     around 448 * 2^-126), all-zero and mixed groups: bit-identical to
@@ -365,10 +370,10 @@ def test_linear_fused_quant_tiny_scales(fmt, M):
     oracle's product."""
     import torch
     from block_scaled_precision_fp8_amd import lib as L
-    K, N = 4096, 512
+    K = 4096
     assert L.workspace_size(L.OP_LINEAR, M, N, K) == 0          # the fused path
     # 16 tokens: every class; 5: the subnormal-scale classes; 1: s = 2^-128
-    rows = {16: list(range(16)), 5: [1, 3, 5, 6, 8], 1: [5]}[M]
+    rows = {16: list(range(16)), 5: [1, 3, 5, 6, 8], 2: [3, 5], 1: [5]}[M]
     x = np.ascontiguousarray(_tiny_amax_acts(16, K)[rows])
     # large weights keep the products of the tiny activations normal
     w = synth.normal_bf16((N, K), 2.0**100, "llama", "w", seed=12)
@@ -405,6 +410,7 @@ def test_linear_fused_quant_tiny_scales(fmt, M):
 
 @pytest.mark.parametrize("fmt", [0, 1])
 @pytest.mark.parametrize("M,N,K", [(1, 512, 4096), (16, 1024, 4096), (16, 4104, 4096),
+                                   (1, 8192, 4096), (2, 1032, 14352),
                                    (64, 1024, 1536), (300, 520, 640)])
 @pytest.mark.parametrize("scale", ["plain", "tiny"])
 def test_linear_static_matches_two_calls(M, N, K, fmt, scale):
