@@ -37,7 +37,10 @@ from the committed rocprofv3 PMC summary when that summary was taken on the
 current kernel source, else null.  ``launch_us`` gives the median, p10 and
 p90 of the dominant kernel's timed launches, ``ms_per_step_stats`` those of
 the timed steps.  ``roofline_decode`` is the HBM roofline of the decode-sized
-runs (M <= 16, act quant included): their algorithmic bytes over their time.
+runs (M <= 16, act quant included): their algorithmic bytes over the time of
+one pass over them, launched back to back with events only at the pass
+boundaries (a decode step's launch pattern; events between launches would
+add their own gaps); median, p10, p90 over ``steps`` passes.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--suites ...]
 """
@@ -178,10 +181,13 @@ def run_linears(torch, L, synth, shapes, ms, fmt, workload, steps, warmup, dev, 
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
-    def step(s, tm=None, big_only=False):
-        """one pass over every run; tm marks around every launch, or with
-        big_only around the 256 x 256-tile GEMM launches only"""
+    def step(s, tm=None, big_only=False, only=None):
+        """one pass over every run (or the runs whose indices `only` lists);
+        tm marks around every launch, or with big_only around the
+        256 x 256-tile GEMM launches only"""
         for j, r in enumerate(runs):
+            if only is not None and j not in only:
+                continue
             # consecutive runs of one shape read different copies, so no run
             # finds its weights in the 256 MB last-level cache
             wq, wsc = weights[(r["K"], r["N"])][(s + j) % WEIGHT_COPIES]
@@ -223,11 +229,21 @@ def run_linears(torch, L, synth, shapes, ms, fmt, workload, steps, warmup, dev, 
     for s in range(steps):
         step(s, tm)
     torch.cuda.synchronize()
+    # the decode-sized runs (M <= 16) back to back, events at pass boundaries
+    dec_idx = {j for j, r in enumerate(runs) if r["M"] <= 16}
+    dec_pass_ms = []
+    if dec_idx:
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record(stream)
+        for s in range(steps):
+            step(s, only=dec_idx)
+            ev[s + 1].record(stream)
+        torch.cuda.synchronize()
+        dec_pass_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
     sb = 4 if fmt == 0 else 1
     detail, big_flops, big_ms, n_big, flops = [], 0.0, 0.0, 0, 0.0
     dec_bytes, dec_ms = 0.0, 0.0
     big_launch_us = []          # every timed launch of the 256 x 256 tile
-    dec_runs = []               # (bytes, per-step ms list) of the M <= 16 runs
     for j, r in enumerate(runs):
         M, N, K = r["M"], r["N"], r["K"]
         qm, gm = tm.ms(("q", j), ("g", j)), tm.ms(("g", j), ("e", j))
@@ -243,7 +259,6 @@ def run_linears(torch, L, synth, shapes, ms, fmt, workload, steps, warmup, dev, 
                      frac_hbm=round(lb / (lm * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
             dec_bytes += lb
             dec_ms += lm
-            dec_runs.append((lb, tm.all_ms(("q", j), ("g", j))))
             log(f"[{workload}] M={M:5d} K={K:5d} N={N:5d} fused linear {lm*1e3:8.1f} us "
                 f"({d['linear_gbs']:7.1f} GB/s, {d['linear_tflops']:7.1f} TF/s)")
             detail.append(d)
@@ -259,7 +274,6 @@ def run_linears(torch, L, synth, shapes, ms, fmt, workload, steps, warmup, dev, 
         if M <= 16:
             dec_bytes += qb + gb
             dec_ms += qm + gm
-            dec_runs.append((qb + gb, tm.all_ms(("q", j), ("e", j))))
         detail.append(d)
         if r["big"]:
             big_flops += fl
@@ -270,14 +284,16 @@ def run_linears(torch, L, synth, shapes, ms, fmt, workload, steps, warmup, dev, 
             f"({d['quant_gbs']:7.1f} GB/s)  gemm {gm*1e3:8.1f} us ({d['gemm_tflops']:7.1f} TF/s, "
             f"{d['gemm_gbs']:7.1f} GB/s)  linear {d['linear_tflops']:7.1f} TF/s")
     decode = None
-    if dec_ms > 0:
-        # per step: all M <= 16 runs' bytes over their summed time (linear,
-        # act quant included), median / p10 / p90 over the steps
-        per_step = [sum(ms[i] for _, ms in dec_runs) for i in range(steps)]
-        decode = dict(runs="M <= 16", bytes=dec_bytes, us=round(dec_ms * 1e3, 1),
-                      us_per_step=pstats(per_step, 1e3, 1),
-                      gbs=round(dec_bytes / (dec_ms * 1e-3) / 1e9, 1),
-                      frac_hbm=round(dec_bytes / (dec_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
+    if dec_pass_ms:
+        # all M <= 16 runs' bytes (act quant included) over one back-to-back
+        # pass over them (median over the passes; p10 / p90 besides); the sum
+        # of the per-launch event times is kept for comparison
+        med = float(np.median(dec_pass_ms))
+        decode = dict(runs="M <= 16", bytes=dec_bytes, us=round(med * 1e3, 1),
+                      us_per_step=pstats(dec_pass_ms, 1e3, 1),
+                      us_launch_events=round(dec_ms * 1e3, 1),
+                      gbs=round(dec_bytes / (med * 1e-3) / 1e9, 1),
+                      frac_hbm=round(dec_bytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
     for r in runs:
         r.clear()
     weights.clear()
@@ -692,7 +708,8 @@ def main():
         roofline_decode = {
             "bound": "hbm", "achieved": dec["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": dec["frac_hbm"], "traffic": None,
-            "kernel": "gemm_decode_kernel (M <= 16; fp8_linear, act quant included)",
+            "kernel": "gemm_decode_kernel / gemm_decode_pers_kernel (M <= 16; act quant "
+                      "included, fused where fp8_linear fuses it)",
             "runs": "the 8 Llama-3-8B linears with M in {1, 16}",
             "algorithmic_bytes_per_step": dec["bytes"], "us_per_step": dec["us_per_step"]}
     detail = {"llama": r["detail"], "llama_decode_hbm": r["decode"]}
