@@ -63,14 +63,28 @@ __device__ __forceinline__ float block_max(float v, float* red) {
   return r;
 }
 
-// Partial max |x| over a grid-stride slice of the tensor (16 bytes per lane
-// per step).  Rows are dense (K elements each, K % 32 == 0).
+// Partial max |x| over a grid-stride slice of the tensor, four independent
+// 16-byte loads per lane per step (64 KB in flight per CU at four
+// workgroups; one load per step left the pass latency-bound).  Plain
+// (cached) loads: the quantization pass reads x again right after, and finds
+// much of it in the last-level cache (8-10% faster than streaming loads at
+// 4096 x 12288 and 4096 x 28672).  Rows are dense (K elements each,
+// K % 32 == 0).
+constexpr int kAmaxUnroll = 4;
 __global__ __launch_bounds__(256) void fp4_amax_kernel(const uint16_t* __restrict__ x,
                                                        int64_t n8, float* __restrict__ part) {
   __shared__ float red[4];
   float a = 0.0f;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256)
-    a = fmaxf(a, amax_bf16x8(ld_stream16(x + i * 8)));
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  for (; i + (kAmaxUnroll - 1) * stride < n8; i += kAmaxUnroll * stride) {
+    uint4 v[kAmaxUnroll];
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; ++u) v[u] = *(const uint4*)(x + (i + u * stride) * 8);
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; ++u) a = fmaxf(a, amax_bf16x8(v[u]));
+  }
+  for (; i < n8; i += stride) a = fmaxf(a, amax_bf16x8(*(const uint4*)(x + i * 8)));
   a = block_max(a, red);
   if (threadIdx.x == 0) part[blockIdx.x] = a;
 }
@@ -111,16 +125,31 @@ __global__ __launch_bounds__(256) void fp4_quant_kernel(
     uint2 codes = make_uint2(0, 0);
     if (eff > 0.0f) {
       // E2M1 encode of fl32(x / eff): the hardware convert with a unit scale
-      // rounds to nearest even and saturates at 6; element 2i -> low nibble
+      // rounds to nearest even and saturates at 6; element 2i -> low nibble.
+      // Dynamic tensor scale: |x / eff| stays below 16 (eff follows the
+      // group amax), where the reciprocal form with its correction gives
+      // the same codes as IEEE division (checked on the CPU with exact fp32
+      // rounding: every finite bf16 x with |x| <= 16 eff against 3000 scales
+      // over the whole positive range, none differ); a static tensor scale
+      // does not bound the quotient, so that case divides.
+      float q[16];
+      if (part != nullptr) {
+        const RcpDiv dv = rcp_div(eff);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) q[i] = div_by_rcp(f[i], dv);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) q[i] = f[i] / eff;
+      }
       uint32_t lo = 0, hi = 0;
-      lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, f[0] / eff, f[1] / eff, 1.0f, 0);
-      lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, f[2] / eff, f[3] / eff, 1.0f, 1);
-      lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, f[4] / eff, f[5] / eff, 1.0f, 2);
-      lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, f[6] / eff, f[7] / eff, 1.0f, 3);
-      hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, f[8] / eff, f[9] / eff, 1.0f, 0);
-      hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, f[10] / eff, f[11] / eff, 1.0f, 1);
-      hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, f[12] / eff, f[13] / eff, 1.0f, 2);
-      hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, f[14] / eff, f[15] / eff, 1.0f, 3);
+      lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, q[0], q[1], 1.0f, 0);
+      lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, q[2], q[3], 1.0f, 1);
+      lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, q[4], q[5], 1.0f, 2);
+      lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, q[6], q[7], 1.0f, 3);
+      hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, q[8], q[9], 1.0f, 0);
+      hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, q[10], q[11], 1.0f, 1);
+      hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, q[12], q[13], 1.0f, 2);
+      hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, q[14], q[15], 1.0f, 3);
       codes = make_uint2(lo, hi);
     }
     *(uint2*)(q4 + gi * 8) = codes;
