@@ -21,6 +21,14 @@ runs (a third, TCC_HIT_sum TCC_MISS_sum, adds the L2 hit rate): texture-data sta
 stalls, and the L1-to-L2 request count and average latency, with the
 concurrency they imply (Little's law).
 `summary`: the text form of one bench.py JSON line.
+`bound`: for the kernels named by --kernels (label=substring pairs), per
+launch shape (grid), the share of each hardware limit the launches reach,
+from five counter runs of one command: HBM traffic (FETCH_SIZE, WRITE_SIZE,
+scaled by the copy kernel's readings) against 8 TB/s, MFMA busy cycles
+(SQ_VALU_MFMA_BUSY_CYCLES) and VALU issue (SQ_INSTS_VALU, 4 cycles per wave
+instruction) against the SIMD cycles, texture address and data unit busy
+cycles (TA_TA_BUSY_sum, TD_TD_BUSY_sum) against the CU cycles, and the L2
+hit rate; the largest share names the bounding counter.
 `trace`: from a --kernel-trace run of the default bench command and that
 run's JSON line, the dominant kernel's average over the timed steps, the
 roofline fraction it implies, and the gaps between kernels in that window.
@@ -297,6 +305,60 @@ def summary(a):
         f.write("\n".join(lines) + "\n")
 
 
+def bound(a):
+    """which hardware limit each selected kernel's launches come closest to"""
+    simds, cus, xcds = 1024, 256, 8
+    runs = {k: dispatches(getattr(a, k)) for k in ("fetch", "write", "sq", "l2", "tx")}
+    scale = {}
+    for k, ctr in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
+        copy = [d[ctr] for d in runs[k].values() if "copy" in d["name"]]
+        if not copy:
+            sys.exit(f"no copy kernel in the {ctr} run")
+        scale[k] = a.copy_mib * 1024.0 / max(copy)
+    sel = [kv.split("=", 1) for kv in a.kernels.split(";")]
+    mops = a.mops.split(",")
+
+    def groups(rs):
+        g = {}
+        for d in rs.values():
+            for label, needle in sel:
+                if needle in d["name"]:
+                    g.setdefault((label, d["grid"]), []).append(d)
+        return g
+
+    G = {k: groups(v) for k, v in runs.items()}
+    lines = [f"# What bounds {a.title}", f"# commands: {a.cmd}",
+             f"FETCH_SIZE / WRITE_SIZE scale (true / counter, {a.copy_mib} MiB copy): "
+             f"{scale['fetch']:.4f} / {scale['write']:.4f}",
+             "# kernel | grid | launches | us | HBM read MB | HBM write MB | HBM share of 8 TB/s | "
+             "MFMA busy | MFMA TF/s | VALU issue share | TA busy | TD busy | L2 hit | nearest limit"]
+    for key in sorted(G["fetch"], key=lambda t: (t[0], t[1])):
+        def mean(run, f):
+            rs = G[run].get(key, [])
+            return sum(f(d) for d in rs) / len(rs) if rs else float("nan")
+        us = mean("fetch", lambda d: d["ns"]) / 1e3
+        rd = mean("fetch", lambda d: d["FETCH_SIZE"] * scale["fetch"] * 1024 / 1e6)
+        wr = mean("write", lambda d: d["WRITE_SIZE"] * scale["write"] * 1024 / 1e6)
+        hbm = (rd + wr) * 1e6 / (us * 1e-6) / 8e12
+        cyc = lambda d: d["GRBM_GUI_ACTIVE"] / xcds
+        mf = mean("sq", lambda d: d["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc(d) * simds))
+        tf = mean("sq", lambda d: sum(d.get(c, 0.0) for c in mops) * 512 / d["ns"] / 1e3)
+        va = mean("sq", lambda d: d["SQ_INSTS_VALU"] * 4 / (cyc(d) * simds))
+        ta = mean("tx", lambda d: d["TA_TA_BUSY_sum"] / (cyc(d) * cus))
+        td = mean("tx", lambda d: d["TD_TD_BUSY_sum"] / (cyc(d) * cus))
+        hit = mean("l2", lambda d: d["TCC_HIT_sum"] / max(d["TCC_HIT_sum"] + d["TCC_MISS_sum"], 1.0))
+        lim = max((("HBM (FETCH_SIZE + WRITE_SIZE)", hbm), ("MFMA (SQ_VALU_MFMA_BUSY_CYCLES)", mf),
+                   ("VALU (SQ_INSTS_VALU)", va), ("TA (TA_TA_BUSY_sum)", ta),
+                   ("TD (TD_TD_BUSY_sum)", td)), key=lambda t: t[1])
+        n = len(G["fetch"][key])
+        lines.append(f"{key[0]} | {key[1]} | {n} | {us:.1f} | {rd:.1f} | {wr:.1f} | {hbm:.3f} | "
+                     f"{mf:.3f} | {tf:.0f} | {va:.3f} | {ta:.3f} | {td:.3f} | {100 * hit:.1f}% | "
+                     f"{lim[0]} {lim[1]:.3f}")
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -338,13 +400,22 @@ def main():
     tr.add_argument("--kernel", default=GEMM_KERNEL)
     tr.add_argument("--warmup", type=int, default=5)
     tr.add_argument("--steps", type=int, default=20)
+    bd = sub.add_parser("bound")
+    for k in ("fetch", "write", "sq", "l2", "tx"):
+        bd.add_argument("--" + k, required=True)
+    bd.add_argument("--copy-mib", type=int, required=True)
+    bd.add_argument("--kernels", required=True, help="label=substring;label=substring...")
+    bd.add_argument("--mops", default="SQ_INSTS_VALU_MFMA_MOPS_F8")
+    bd.add_argument("--title", required=True)
+    bd.add_argument("--cmd", required=True)
+    bd.add_argument("--out", required=True)
     b = sub.add_parser("summary")
     b.add_argument("--json", required=True)
     b.add_argument("--cmd", required=True)
     b.add_argument("--out", required=True)
     a = ap.parse_args()
     {"traffic": traffic, "stats": stats, "summary": summary, "mfma": mfma,
-     "decode": decode, "l1": l1, "trace": trace}[a.what](a)
+     "decode": decode, "l1": l1, "trace": trace, "bound": bound}[a.what](a)
 
 
 if __name__ == "__main__":

@@ -162,6 +162,13 @@ __device__ __forceinline__ Tile dense_tile(int64_t M, int64_t N, int splits) {
 // (M fastest, so the M tiles of one expert's weight tile run together).
 // gsel picks the experts a launch covers: 0 all, 1 those with more than
 // kSmallSegment rows, 2 the others (each class runs on its own tile shape).
+// XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so
+// workgroup b takes logical tile (b % 8) ceil(total / 8) + b / 8 -- each XCD
+// a contiguous eighth of the (device-known) tile count -- and the M tiles
+// of one weight tile, and the N tiles of one expert, meet in one L2 (dealt
+// in launch order they landed on different XCDs and re-read the weights
+// from HBM: 12.1 GB read for 7.5 GB of gate/up experts).  The grid is the
+// host's upper bound on the count, a multiple of 8.
 constexpr int kSmallSegment = 128;
 
 template <int BM, int BN, int THREADS>
@@ -188,9 +195,11 @@ __device__ __forceinline__ Tile grouped_tile(const int32_t* __restrict__ seg, in
   }
   Tile tl;
   tl.split = 0;
-  const int t = blockIdx.x;
   const int total = s_pref[E] * NT;
-  tl.valid = t < total;
+  const int per_xcd = (total + 7) / 8;
+  const int bid = blockIdx.x;
+  const int t = (bid & 7) * per_xcd + (bid >> 3);
+  tl.valid = (bid >> 3) < per_xcd && t < total;
   tl.expert = 0;
   tl.m0 = 0; tl.mlim = 0; tl.n0 = 0;
   if (!tl.valid) return tl;
@@ -1730,8 +1739,8 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t st, int splits, int kbps, i
     tiles = (gsel == 2 ? (int64_t)a.E * ((kSmallSegment + BM - 1) / BM) : full + parts) * NT;
   } else {
     tiles = (a.M + BM - 1) / BM * NT * splits;
-    tiles = (tiles + 7) / 8 * 8;                 // whole rounds over the 8 XCDs
   }
+  tiles = (tiles + 7) / 8 * 8;                   // whole rounds over the 8 XCDs
   float* part = splits > 1 ? (float*)a.workspace : nullptr;
   hipLaunchKernelGGL((gemm_lds_kernel<FMT, WMN, WNN, WM, WN, GROUPED, W4, SW, SA, SW4, XQ>),
                      dim3((unsigned)tiles), dim3(64 * WMN * WNN), 0, st, a.xq, a.xs, a.wq, a.ws,
@@ -2048,7 +2057,7 @@ hipError_t launch_b32(const GemmArgs& a, hipStream_t st) {
   const int64_t NT = (a.N + 127) / 128;
   // grouped: every expert adds at most one partial M tile
   int64_t tiles = G ? ((a.M + 127) / 128 + a.E) * NT : (a.M + 127) / 128 * NT;
-  if (!G) tiles = (tiles + 7) / 8 * 8;           // whole rounds over the 8 XCDs
+  tiles = (tiles + 7) / 8 * 8;                   // whole rounds over the 8 XCDs
   const uint16_t* bias = G ? nullptr : a.bias;
 #define BSFP8_B32L(FMT, SA)                                                                       \
   hipLaunchKernelGGL((gemm_b32_kernel<FMT, SA, G>), dim3((unsigned)tiles), dim3(256), 0, st, a.xq, \
