@@ -21,6 +21,9 @@ runs (a third, TCC_HIT_sum TCC_MISS_sum, adds the L2 hit rate): texture-data sta
 stalls, and the L1-to-L2 request count and average latency, with the
 concurrency they imply (Little's law).
 `summary`: the text form of one bench.py JSON line.
+`keep`: copy a counter CSV keeping only the rows of kernels whose names
+contain one of the ';'-separated --kernels substrings (a whole-bench counter
+run writes tens of MB).
 `bound`: for the kernels named by --kernels (label=substring pairs), per
 launch shape (grid), the share of each hardware limit the launches reach,
 from five counter runs of one command: HBM traffic (FETCH_SIZE, WRITE_SIZE,
@@ -305,6 +308,18 @@ def summary(a):
         f.write("\n".join(lines) + "\n")
 
 
+def keep(a):
+    """the rows of the selected kernels of one counter CSV"""
+    needles = a.kernels.split(";")
+    with open(a.src) as f, open(a.dst, "w", newline="") as g:
+        r = csv.DictReader(f)
+        w = csv.DictWriter(g, fieldnames=r.fieldnames)
+        w.writeheader()
+        for row in r:
+            if any(n in row["Kernel_Name"] for n in needles):
+                w.writerow(row)
+
+
 def bound(a):
     """which hardware limit each selected kernel's launches come closest to"""
     simds, cus, xcds = 1024, 256, 8
@@ -400,6 +415,10 @@ def main():
     tr.add_argument("--kernel", default=GEMM_KERNEL)
     tr.add_argument("--warmup", type=int, default=5)
     tr.add_argument("--steps", type=int, default=20)
+    kp = sub.add_parser("keep")
+    kp.add_argument("--src", required=True)
+    kp.add_argument("--dst", required=True)
+    kp.add_argument("--kernels", required=True)
     bd = sub.add_parser("bound")
     for k in ("fetch", "write", "sq", "l2", "tx"):
         bd.add_argument("--" + k, required=True)
@@ -415,7 +434,7 @@ def main():
     b.add_argument("--out", required=True)
     a = ap.parse_args()
     {"traffic": traffic, "stats": stats, "summary": summary, "mfma": mfma,
-     "decode": decode, "l1": l1, "trace": trace, "bound": bound}[a.what](a)
+     "decode": decode, "l1": l1, "trace": trace, "bound": bound, "keep": keep}[a.what](a)
 
 
 if __name__ == "__main__":

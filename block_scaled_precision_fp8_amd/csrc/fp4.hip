@@ -159,6 +159,25 @@ __global__ __launch_bounds__(256) void fp4_quant_kernel(
 
 // ---------------------------------------------------------------- GEMM
 
+// LDS reads through restrict-qualified pointers: the alias scope tells the
+// compiler they do not touch the buffers the in-flight LDS-DMA writes, so it
+// does not wait for that DMA before them
+__device__ __forceinline__ uint4 read_u128(const uint8_t* __restrict__ p, int off) {
+  return *(const uint4*)(p + off);
+}
+__device__ __forceinline__ uint32_t read_u16(const uint8_t* __restrict__ p, int off) {
+  return *(const uint16_t*)(p + off);
+}
+// compile-time loop: f(std::integral_constant<int, 0>) .. f(<N - 1>)
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
+
 // Eight E2M1 codes (one 32-bit word, element 0 in the low nibble) times one
 // group scale -> eight fp16 values, exact.
 __device__ __forceinline__ half8 dequant8(uint32_t w, _Float16 s) {
@@ -521,6 +540,193 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void fp4_gemm_lds_kernel
   }
 }
 
+// ------------------------------------------------------------------------
+// Large-M NVFP4 GEMM on staged codes (K % 128 == 0).  fp4_gemm_lds_kernel
+// keeps both operands in LDS as fp16, four times the bytes of the codes: per
+// 128-wide K block its dequantized stores and fragment reads move about
+// 256 KB through LDS against about 1000 cycles of fp16 MFMA work, and the
+// kernel runs at about a third of the fp16 peak.  Here LDS holds the raw
+// operands -- E2M1 codes, 64 bytes per row and K block, and E4M3 group
+// scales, 8 bytes -- in a four-stage pipeline filled by LDS-DMA, and each
+// wave dequantizes its fragments in registers after reading them (hardware
+// fp4 -> fp16 convert, one packed multiply by the group scale; exact, as in
+// fp4_gemm_lds_kernel): about 55 KB of LDS traffic per K block.
+//   tile 128 x 128, four waves of 64 x 64 (2 x 2), two workgroups per CU;
+//   lane (l16, g4) reads 16 contiguous code bytes of a row -- K
+//   [32 g4, 32 g4 + 32) of the block -- and feeds 8 of them to each of the
+//   four 16x16x32 MFMA steps (step s: K [32 g4 + 8 s, + 8)), the same K
+//   assignment for both operands; its two group scales are bytes 2 g4 and
+//   2 g4 + 1 of the row's eight;
+//   LDS rows of 64 bytes: lane chunk c of row r sits at chunk c ^ ((r >> 1)
+//   & 3), so the 16 rows of a fragment read hit distinct banks (the DMA
+//   stays contiguous: the swizzle is applied to its source offsets).
+// ------------------------------------------------------------------------
+constexpr int kDmaStages = 4;
+constexpr int kDmaCodes = 128 * 64;                          // one operand's codes per stage
+constexpr int kDmaScales = 128 * 8;                          // one operand's group scales
+constexpr int kDmaStage = 2 * (kDmaCodes + kDmaScales);      // 18 KB
+constexpr int kDmaLoads = 6;                                 // DMA ops per lane per stage
+
+__global__ __launch_bounds__(256, 2) void fp4_gemm_dma_kernel(
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
+    const float* __restrict__ xt, const uint8_t* __restrict__ wq,
+    const uint8_t* __restrict__ ws, const float* __restrict__ wt, uint16_t* __restrict__ y,
+    int64_t M, int64_t N, int64_t K) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int BM = 128, BN = 128, WM = 64, WN = 64, MI = WM / 16, NI = WN / 16;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kDmaStages * kDmaStage];
+  const int64_t MT = (M + BM - 1) / BM;
+  const int64_t NT = (N + BN - 1) / BN;
+  // XCD-aware order, M tiles fastest within groups of 8 (as fp4_gemm_lds_kernel)
+  const int bid = blockIdx.x;
+  const int per_xcd = (int)(gridDim.x / 8);
+  const int t = (bid & 7) * per_xcd + (bid >> 3);
+  if (t >= MT * NT) return;
+  constexpr int GM = 8;
+  const int group = t / (GM * (int)NT);
+  const int first_m = group * GM;
+  const int gsz = min((int)MT - first_m, GM);
+  const int in = t - group * GM * (int)NT;
+  const int64_t m0 = (int64_t)(first_m + in % gsz) * BM;
+  const int64_t n0 = (int64_t)(in / gsz) * BN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int KB = (int)(K / 128);
+  const int64_t KH = K / 2, KG = K / 16;            // code and scale bytes per row
+  const int64_t mrows = min((int64_t)BM, M - m0), nrows = min((int64_t)BN, N - n0);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(xq + m0 * KH, mrows * KH);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(wq + n0 * KH, nrows * KH);
+  const __amdgpu_buffer_rsrc_t rxs = make_rsrc(xs + m0 * KG, mrows * KG);
+  const __amdgpu_buffer_rsrc_t rws = make_rsrc(ws + n0 * KG, nrows * KG);
+  const float gg = (*xt) * (*wt);
+
+  // stage kb into buffer b: codes (lane chunk q: row q >> 2, LDS chunk q & 3
+  // holding code chunk (q & 3) ^ ((row >> 1) & 3)), then scales (row q >> 1,
+  // dword q & 1); rows past the tile and blocks past K read zeros
+  auto issue = [&](int kb, int b) __attribute__((always_inline)) {
+    uint8_t* st = lds + b * kDmaStage;
+    const uint32_t kc = (uint32_t)kb * 64, ks = (uint32_t)kb * 8;
+    const bool kin = kb < KB;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int q = (j * 4 + wave) * 64 + lane;
+      const int row = q >> 2, c = (q & 3) ^ ((row >> 1) & 3);
+      const uint32_t off = kin ? (uint32_t)(row * KH) + kc + c * 16 : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, BSFP8_LDS(st + (j * 4 + wave) * 1024), 16, off,
+                                               0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rw, BSFP8_LDS(st + kDmaCodes + (j * 4 + wave) * 1024), 16, off, 0, 0, 0);
+    }
+    const int q = wave * 64 + lane;
+    const uint32_t so = kin ? (uint32_t)((q >> 1) * KG) + ks + (q & 1) * 4 : kOOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rxs, BSFP8_LDS(st + 2 * kDmaCodes + wave * 256), 4,
+                                             so, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rws, BSFP8_LDS(st + 2 * kDmaCodes + kDmaScales + wave * 256), 4, so, 0, 0, 0);
+  };
+
+  v4f acc[NI][MI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < MI; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // one K block from buffer b: 16 code bytes and two scale bytes per row
+  auto compute = [&](int b) __attribute__((always_inline)) {
+    const uint8_t* st = lds + b * kDmaStage;
+    uint4 xc[MI], wc[NI];
+    uint32_t xsc[MI], wsc[NI];
+#pragma unroll
+    for (int j = 0; j < MI; ++j) {
+      const int r = wm * WM + j * 16 + l16;
+      xc[j] = read_u128(st, r * 64 + ((g4 ^ ((r >> 1) & 3)) << 4));
+      xsc[j] = read_u16(st + 2 * kDmaCodes, r * 8 + 2 * g4);
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int r = wn * WN + i * 16 + l16;
+      wc[i] = read_u128(st + kDmaCodes, r * 64 + ((g4 ^ ((r >> 1) & 3)) << 4));
+      wsc[i] = read_u16(st + 2 * kDmaCodes + kDmaScales, r * 8 + 2 * g4);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      half8 bx[MI], aw[NI];
+#pragma unroll
+      for (int j = 0; j < MI; ++j) {
+        const uint32_t w = s == 0 ? xc[j].x : s == 1 ? xc[j].y : s == 2 ? xc[j].z : xc[j].w;
+        bx[j] = dequant8(w, e4m3_to_f16((xsc[j] >> (8 * (s >> 1))) & 0xffu));
+      }
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const uint32_t w = s == 0 ? wc[i].x : s == 1 ? wc[i].y : s == 2 ? wc[i].z : wc[i].w;
+        aw[i] = dequant8(w, e4m3_to_f16((wsc[i] >> (8 * (s >> 1))) & 0xffu));
+      }
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int j = 0; j < MI; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw[i], bx[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // prologue: stages 0..2; then per block: its stage has landed (the two
+  // newer ones may still fly: loads retire in issue order), everyone's has
+  // and everyone is done reading the buffer refilled next, refill, multiply
+  issue(0, 0);
+  issue(1, 1);
+  issue(2, 2);
+  for (int kb0 = 0; kb0 < KB; kb0 += kDmaStages) {
+    static_for<kDmaStages>([&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+      const int kb = kb0 + s;
+      if (kb >= KB) return;
+      wait_vmcnt<2 * kDmaLoads>();
+      wait_lgkmcnt0();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      issue(kb + 3, (s + 3) % kDmaStages);
+      compute(s);
+    });
+  }
+  // drain: no DMA may land in LDS once it holds the output tile
+  wait_vmcnt<0>();
+  wait_lgkmcnt0();
+  __syncthreads();
+
+  // bf16 epilogue through LDS (as fp4_gemm_lds_kernel)
+  constexpr int CPR = BN / 8;                  // 16-byte chunks per output row
+  uint8_t* ot = lds;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int col = wn * WN + i * 16 + 4 * g4;
+#pragma unroll
+    for (int j = 0; j < MI; ++j) {
+      const int row = wm * WM + j * 16 + l16;
+      const v4f v = acc[i][j] * gg;
+      uint2 o;
+      o.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+      o.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+      const int c = col >> 3;
+      *(uint2*)(ot + row * (BN * 2) + ((c ^ (row & (CPR - 1))) << 4) + ((col >> 2) & 1) * 8) = o;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < BM * CPR / 256; ++p) {
+    const int L = p * 256 + tid;
+    const int row = L / CPR, c = L % CPR;
+    const int64_t m = m0 + row, n = n0 + c * 8;
+    if (m < M && n < N)
+      *(uint4*)(y + m * N + n) = *(const uint4*)(ot + row * (BN * 2) + ((c ^ (row & (CPR - 1))) << 4));
+  }
+#endif
+}
+
 constexpr int kFp4WavesN = 4;   // 2 x 4 waves of 64 x 32 (two per SIMD)
 
 constexpr int64_t kStreamMaxM = 64;
@@ -584,8 +790,12 @@ hipError_t launch_fp4_gemm(const uint8_t* xq, const uint8_t* xs, const float* xt
   if (M > kStreamMaxM) {
     int64_t tiles = ((M + kLdsBM - 1) / kLdsBM) * ((N + kLdsBN - 1) / kLdsBN);
     tiles = (tiles + 7) / 8 * 8;
-    hipLaunchKernelGGL((fp4_gemm_lds_kernel<2, kFp4WavesN>), dim3((unsigned)tiles),
-                       dim3(64 * 2 * kFp4WavesN), 0, s, xq, xs, xt, wq, wsc, wt, y, M, N, K);
+    if (K % 128 == 0)   // staged codes, dequantized per fragment
+      hipLaunchKernelGGL(fp4_gemm_dma_kernel, dim3((unsigned)tiles), dim3(256), 0, s, xq, xs, xt,
+                         wq, wsc, wt, y, M, N, K);
+    else
+      hipLaunchKernelGGL((fp4_gemm_lds_kernel<2, kFp4WavesN>), dim3((unsigned)tiles),
+                         dim3(64 * 2 * kFp4WavesN), 0, s, xq, xs, xt, wq, wsc, wt, y, M, N, K);
     return hipGetLastError();
   }
   int kbps, real;

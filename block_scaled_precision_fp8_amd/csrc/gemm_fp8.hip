@@ -220,29 +220,6 @@ __device__ __forceinline__ Tile grouped_tile(const int32_t* __restrict__ seg, in
   return tl;
 }
 
-// Buffer resource over [base, base + bytes): loads past the end return 0,
-// which handles ragged M, N and K edges without branches.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int n = bytes > 0x7fffffffLL ? 0x7fffffff : (int)bytes;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
-}
-constexpr uint32_t kOOB = 0x80000000u;   // an offset past any buffer's end
-
-#define BSFP8_LDS(p) ((__attribute__((address_space(3))) void*)(p))
-
-// s_waitcnt vmcnt(n), other counters untouched (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-// s_waitcnt lgkmcnt(0): this wave's LDS stores are done (s_barrier alone
-// does not wait for them on gfx950)
-__device__ __forceinline__ void wait_lgkmcnt0() {
-  __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
-}
-
 // One fragment read from LDS.  The restrict-qualified pointer gives the
 // loads alias-scope information; without it the compiler assumes they may
 // read what the in-flight LDS-DMA of the next stage writes and waits for

@@ -81,6 +81,8 @@ def _gemm_dev(h, M, N):
     (1, 256, 256), (5, 264, 288), (16, 1000, 1024), (33, 512, 640), (64, 256, 2048),
     (65, 256, 256), (130, 520, 640), (300, 1000, 1056), (256, 256, 128),
     (200, 264, 2144), (129, 136, 96),     # K blocks ending after 96 of 128 values
+    # K % 128 == 0, M > 64: codes staged through the four-stage LDS pipeline
+    (384, 1024, 4096), (300, 1000, 1152), (129, 136, 128), (4100, 264, 640),
 ])
 def test_fp4_gemm_parity(M, N, K):
     say(f"fp4 gemm M={M} N={N} K={K}")
