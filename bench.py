@@ -68,7 +68,9 @@ PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 MFMA
 PEAK_F16_TFLOPS = 2500.0  # MI355X dense fp16 / bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_lds_kernel_llama_traffic.txt")
-GEMM_SOURCE = os.path.join(ROOT, "block_scaled_precision_fp8_amd", "csrc", "gemm_fp8.hip")
+# the large-M GEMM's code: its kernel source and the device helpers it includes
+GEMM_SOURCES = [os.path.join(ROOT, "block_scaled_precision_fp8_amd", "csrc", f)
+                for f in ("gemm_fp8.hip", "bsfp8_internal.h")]
 
 
 def log(*a):
@@ -76,8 +78,11 @@ def log(*a):
 
 
 def source_hash():
-    with open(GEMM_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in GEMM_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic():
@@ -91,7 +96,7 @@ def read_traffic():
             if ": " in line and not line.lstrip().startswith("#"):
                 k, v = line.rsplit(": ", 1)     # keys may hold a colon themselves
                 kv[k.strip()] = v.strip()
-    if kv.get("gemm_fp8.hip sha256[:16]") != source_hash():
+    if kv.get("gemm sources sha256[:16]") != source_hash():
         return None
     try:
         return float(kv["hbm bytes per launch (scaled)"])

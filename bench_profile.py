@@ -7,15 +7,17 @@
 `traffic`: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the large-M GEMM
 launches, each scaled by true bytes / counter reading of the plain copy
 kernel of N MiB that `bench.py --copy-calib-mib N` runs first; records the
-sha256 of the GEMM source so bench.py only uses it for the same kernel.
+sha256 of the GEMM sources (gemm_fp8.hip and the bsfp8_internal.h device
+helpers) so bench.py only uses it for the same kernel.
 `stats`: the kernel table of a --kernel-trace --stats run.
 `mfma`: MFMA busy share and counted flops of the large-M GEMM from a
 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_F8 run
 (--kernel, --mops, --peak and --title select another kernel, other MOPS
 counters -- summed -- and their peak, e.g. the FP8 x MXFP4 tile with
 SQ_INSTS_VALU_MFMA_MOPS_F8,SQ_INSTS_VALU_MFMA_MOPS_F6F4).
-`decode`: HBM bytes per decode-GEMM dispatch over its duration, from the
-FETCH_SIZE run (scaled by the same copy calibration).
+`decode`: HBM bytes per decode-GEMM dispatch (gemm_decode_kernel and
+gemm_decode_pers_kernel) over its duration, from the FETCH_SIZE run (scaled
+by the same copy calibration).
 `l1`: what bounds the operand loads of the large-M GEMM, from two --pmc
 runs (a third, TCC_HIT_sum TCC_MISS_sum, adds the L2 hit rate): texture-data stalls on L1, L1 pending and tag-conflict stalls, address
 stalls, and the L1-to-L2 request count and average latency, with the
@@ -45,7 +47,9 @@ import os
 import sys
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-GEMM_SOURCE = os.path.join(ROOT, "block_scaled_precision_fp8_amd", "csrc", "gemm_fp8.hip")
+# the large-M GEMM's code: its kernel source and the device helpers it includes
+GEMM_SOURCES = [os.path.join(ROOT, "block_scaled_precision_fp8_amd", "csrc", f)
+                for f in ("gemm_fp8.hip", "bsfp8_internal.h")]
 # the dense fp32-scale 256x256 tile (grouped, W4, SiLU-mul off), whatever follows
 GEMM_KERNEL = "gemm_lds_kernel<0, 4, 2, 64, 128, false, false, false,"
 
@@ -82,13 +86,16 @@ def traffic(a):
         sys.exit("no large-M GEMM launches found")
     fkib, wkib = sum(gf) / len(gf), sum(gw) / len(gw)
     tot = (fkib * sf + wkib * sw) * 1024.0
-    with open(GEMM_SOURCE, "rb") as f:
-        h = hashlib.sha256(f.read()).hexdigest()[:16]
+    hs = hashlib.sha256()
+    for path in GEMM_SOURCES:
+        with open(path, "rb") as f:
+            hs.update(f.read())
+    h = hs.hexdigest()[:16]
     lines = [
         "# HBM traffic of the large-M block-scaled GEMM (fp32 scales), Llama-3-8B linears",
         f"# commands: {a.cmd}",
         f"kernel: {GEMM_KERNEL}",
-        f"gemm_fp8.hip sha256[:16]: {h}",
+        f"gemm sources sha256[:16]: {h}",
         f"launches averaged: {len(gf)}",
         f"copy kernel: {a.copy_mib} MiB read + {a.copy_mib} MiB written; "
         f"FETCH_SIZE {cf:.0f} KiB, WRITE_SIZE {cw:.0f} KiB",
@@ -157,13 +164,13 @@ def decode(a):
     sf = a.copy_mib * 1024.0 / max(d["FETCH_SIZE"] for d in copy)
     groups = {}
     for d in ds.values():
-        if "gemm_decode_kernel" not in d["name"]:
+        if "gemm_decode_" not in d["name"]:   # gemm_decode_kernel, gemm_decode_pers_kernel
             continue
         mb = d["FETCH_SIZE"] * sf * 1024 / 1e6
         key = (d["name"].split("(")[0].replace("void bsfp8::detail::", ""), d["grid"] // 1024,
                round(mb))
         groups.setdefault(key, []).append((mb, d["ns"]))
-    lines = ["# HBM reads of the decode GEMM (M <= 16) per dispatch, Llama-3-8B linears",
+    lines = [f"# HBM reads of the decode GEMM (M <= 16) per dispatch, {a.title}",
              f"# command: {a.cmd}",
              f"FETCH_SIZE scale (true / counter, {a.copy_mib} MiB copy): {sf:.4f}",
              "# kernel | workgroups (N/16) | dispatches | MB fetched | us | GB/s"]
@@ -401,6 +408,7 @@ def main():
     d.add_argument("--copy-mib", type=int, required=True)
     d.add_argument("--cmd", required=True)
     d.add_argument("--out", required=True)
+    d.add_argument("--title", default="Llama-3-8B linears")
     l = sub.add_parser("l1")
     l.add_argument("--pmc1", required=True)
     l.add_argument("--pmc2", required=True)
