@@ -291,6 +291,16 @@ def trace(a):
         f"timed window: {span:.1f} us, {len(win)} kernels, {busy:.1f} us busy, "
         f"{span - busy:.1f} us between kernels ({(span - busy) / len(win):.2f} us per kernel)",
     ]
+    # where one timed step's time goes, by kernel (name cut at the argument list)
+    by = {}
+    for r in win:
+        name = r["Kernel_Name"].split("(")[0]
+        t = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        n, tot = by.get(name, (0, 0.0))
+        by[name] = (n + 1, tot + t)
+    lines.append(f"# per timed step ({a.steps} steps): kernel | launches | us | share of the step span")
+    for name, (n, tot) in sorted(by.items(), key=lambda kv: -kv[1][1]):
+        lines.append(f"{name} | {n / a.steps:.1f} | {tot / a.steps:.1f} | {tot / span:.3f}")
     with open(a.out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))

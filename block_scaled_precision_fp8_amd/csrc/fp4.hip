@@ -551,7 +551,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void fp4_gemm_lds_kernel
 // wave dequantizes its fragments in registers after reading them (hardware
 // fp4 -> fp16 convert, one packed multiply by the group scale; exact, as in
 // fp4_gemm_lds_kernel): about 55 KB of LDS traffic per K block.
-//   tile 128 x 128, four waves of 64 x 64 (2 x 2), two workgroups per CU;
+//   tiles of 128 x 128 (four waves of 64 x 64, two workgroups per CU) or
+//   256 x 256 (eight waves of 64 x 128, one workgroup per CU; the kernel is
+//   bound by the dequantization on the vector ALU, and a wave's weight
+//   fragment then feeds eight MFMAs instead of four);
 //   lane (l16, g4) reads 16 contiguous code bytes of a row -- K
 //   [32 g4, 32 g4 + 32) of the block -- and feeds 8 of them to each of the
 //   four 16x16x32 MFMA steps (step s: K [32 g4 + 8 s, + 8)), the same K
@@ -562,19 +565,30 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void fp4_gemm_lds_kernel
 //   stays contiguous: the swizzle is applied to its source offsets).
 // ------------------------------------------------------------------------
 constexpr int kDmaStages = 4;
-constexpr int kDmaCodes = 128 * 64;                          // one operand's codes per stage
-constexpr int kDmaScales = 128 * 8;                          // one operand's group scales
-constexpr int kDmaStage = 2 * (kDmaCodes + kDmaScales);      // 18 KB
 constexpr int kDmaLoads = 6;                                 // DMA ops per lane per stage
 
-__global__ __launch_bounds__(256, 2) void fp4_gemm_dma_kernel(
+// Tile BM x BN with WAVES_M x WAVES_N waves of (BM / WAVES_M) x (BN /
+// WAVES_N); a stage holds both operands' codes (64 bytes per row) and group
+// scales (8 bytes per row) of one K block.  Either tile forms every output
+// from the same MFMA sequence over K, so both give the same bits.
+template <int BM, int BN, int WAVES_M, int WAVES_N>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 512 / (64 * WAVES_M * WAVES_N))
+void fp4_gemm_dma_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
     const float* __restrict__ xt, const uint8_t* __restrict__ wq,
     const uint8_t* __restrict__ ws, const float* __restrict__ wt, uint16_t* __restrict__ y,
     int64_t M, int64_t N, int64_t K) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  constexpr int BM = 128, BN = 128, WM = 64, WN = 64, MI = WM / 16, NI = WN / 16;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kDmaStages * kDmaStage];
+  constexpr int WAVES = WAVES_M * WAVES_N, THREADS = 64 * WAVES;
+  constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N, MI = WM / 16, NI = WN / 16;
+  constexpr int XCODES = BM * 64, WCODES = BN * 64;           // codes per stage
+  constexpr int XSC = BM * 8, WSC = BN * 8;                   // group scales per stage
+  constexpr int STAGE = XCODES + WCODES + XSC + WSC;
+  constexpr int CJ = XCODES / (THREADS * 16);                 // 16-byte code loads per lane
+  static_assert(BM == BN && CJ * THREADS * 16 == XCODES && XSC == THREADS * 4,
+                "square tile, whole code chunks and one scale dword per lane");
+  static_assert(2 * CJ + 2 == kDmaLoads, "DMA ops per lane per stage");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kDmaStages * STAGE];
   const int64_t MT = (M + BM - 1) / BM;
   const int64_t NT = (N + BN - 1) / BN;
   // XCD-aware order, M tiles fastest within groups of 8 (as fp4_gemm_lds_kernel)
@@ -594,7 +608,7 @@ __global__ __launch_bounds__(256, 2) void fp4_gemm_dma_kernel(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g4 = lane >> 4;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % WAVES_M, wn = wave / WAVES_M;
   const int KB = (int)(K / 128);
   const int64_t KH = K / 2, KG = K / 16;            // code and scale bytes per row
   const int64_t mrows = min((int64_t)BM, M - m0), nrows = min((int64_t)BN, N - n0);
@@ -608,25 +622,25 @@ __global__ __launch_bounds__(256, 2) void fp4_gemm_dma_kernel(
   // holding code chunk (q & 3) ^ ((row >> 1) & 3)), then scales (row q >> 1,
   // dword q & 1); rows past the tile and blocks past K read zeros
   auto issue = [&](int kb, int b) __attribute__((always_inline)) {
-    uint8_t* st = lds + b * kDmaStage;
+    uint8_t* st = lds + b * STAGE;
     const uint32_t kc = (uint32_t)kb * 64, ks = (uint32_t)kb * 8;
     const bool kin = kb < KB;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int q = (j * 4 + wave) * 64 + lane;
+    for (int j = 0; j < CJ; ++j) {
+      const int q = (j * WAVES + wave) * 64 + lane;
       const int row = q >> 2, c = (q & 3) ^ ((row >> 1) & 3);
       const uint32_t off = kin ? (uint32_t)(row * KH) + kc + c * 16 : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, BSFP8_LDS(st + (j * 4 + wave) * 1024), 16, off,
-                                               0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, BSFP8_LDS(st + (j * WAVES + wave) * 1024), 16,
+                                               off, 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rw, BSFP8_LDS(st + kDmaCodes + (j * 4 + wave) * 1024), 16, off, 0, 0, 0);
+          rw, BSFP8_LDS(st + XCODES + (j * WAVES + wave) * 1024), 16, off, 0, 0, 0);
     }
     const int q = wave * 64 + lane;
     const uint32_t so = kin ? (uint32_t)((q >> 1) * KG) + ks + (q & 1) * 4 : kOOB;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rxs, BSFP8_LDS(st + 2 * kDmaCodes + wave * 256), 4,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rxs, BSFP8_LDS(st + XCODES + WCODES + wave * 256), 4,
                                              so, 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rws, BSFP8_LDS(st + 2 * kDmaCodes + kDmaScales + wave * 256), 4, so, 0, 0, 0);
+        rws, BSFP8_LDS(st + XCODES + WCODES + XSC + wave * 256), 4, so, 0, 0, 0);
   };
 
   v4f acc[NI][MI];
@@ -636,40 +650,52 @@ __global__ __launch_bounds__(256, 2) void fp4_gemm_dma_kernel(
     for (int j = 0; j < MI; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
   // one K block from buffer b: 16 code bytes and two scale bytes per row
+  // (BM > 128: the code words are read per step, 4 bytes per fragment, so
+  // that the 64 x 128 accumulators and the fragments fit two waves per SIMD)
   auto compute = [&](int b) __attribute__((always_inline)) {
-    const uint8_t* st = lds + b * kDmaStage;
-    uint4 xc[MI], wc[NI];
+    const uint8_t* st = lds + b * STAGE;
+    constexpr bool WIDE = BM <= 128;
+    uint4 xc[WIDE ? MI : 1], wc[WIDE ? NI : 1];
     uint32_t xsc[MI], wsc[NI];
+    // row r = (first row of the wave) + 16 f + l16: the swizzle (r >> 1) & 3
+    // is that of l16 for every fragment f, so fragment f sits 1024 f bytes
+    // (codes) and 128 f bytes (scales) past fragment 0
+    const int sw = (g4 ^ ((l16 >> 1) & 3)) << 4;
+    const int xo0 = (wm * WM + l16) * 64 + sw, wo0 = (wn * WN + l16) * 64 + sw;
+    const int xs0 = (wm * WM + l16) * 8 + 2 * g4, ws0 = (wn * WN + l16) * 8 + 2 * g4;
+    int xo[MI], wo[NI];
 #pragma unroll
     for (int j = 0; j < MI; ++j) {
-      const int r = wm * WM + j * 16 + l16;
-      xc[j] = read_u128(st, r * 64 + ((g4 ^ ((r >> 1) & 3)) << 4));
-      xsc[j] = read_u16(st + 2 * kDmaCodes, r * 8 + 2 * g4);
+      xo[j] = xo0 + j * 1024;
+      if constexpr (WIDE) xc[j] = read_u128(st, xo[j]);
+      xsc[j] = read_u16(st + XCODES + WCODES, xs0 + j * 128);
     }
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int r = wn * WN + i * 16 + l16;
-      wc[i] = read_u128(st + kDmaCodes, r * 64 + ((g4 ^ ((r >> 1) & 3)) << 4));
-      wsc[i] = read_u16(st + 2 * kDmaCodes + kDmaScales, r * 8 + 2 * g4);
+      wo[i] = wo0 + i * 1024;
+      if constexpr (WIDE) wc[i] = read_u128(st + XCODES, wo[i]);
+      wsc[i] = read_u16(st + XCODES + WCODES + XSC, ws0 + i * 128);
     }
+    auto word = [&](const uint4* c, const uint8_t* base, int off, int s) __attribute__((always_inline)) {
+      if constexpr (WIDE) return s == 0 ? c->x : s == 1 ? c->y : s == 2 ? c->z : c->w;
+      else return *(const uint32_t*)(base + off + 4 * s);
+    };
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      half8 bx[MI], aw[NI];
+      half8 bx[MI];
 #pragma unroll
       for (int j = 0; j < MI; ++j) {
-        const uint32_t w = s == 0 ? xc[j].x : s == 1 ? xc[j].y : s == 2 ? xc[j].z : xc[j].w;
+        const uint32_t w = word(&xc[WIDE ? j : 0], st, xo[j], s);
         bx[j] = dequant8(w, e4m3_to_f16((xsc[j] >> (8 * (s >> 1))) & 0xffu));
       }
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        const uint32_t w = s == 0 ? wc[i].x : s == 1 ? wc[i].y : s == 2 ? wc[i].z : wc[i].w;
-        aw[i] = dequant8(w, e4m3_to_f16((wsc[i] >> (8 * (s >> 1))) & 0xffu));
-      }
-#pragma unroll
-      for (int i = 0; i < NI; ++i)
+        const uint32_t w = word(&wc[WIDE ? i : 0], st + XCODES, wo[i], s);
+        const half8 aw = dequant8(w, e4m3_to_f16((wsc[i] >> (8 * (s >> 1))) & 0xffu));
 #pragma unroll
         for (int j = 0; j < MI; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw[i], bx[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, bx[j], acc[i][j], 0, 0, 0);
+      }
     }
   };
 
@@ -700,6 +726,7 @@ __global__ __launch_bounds__(256, 2) void fp4_gemm_dma_kernel(
 
   // bf16 epilogue through LDS (as fp4_gemm_lds_kernel)
   constexpr int CPR = BN / 8;                  // 16-byte chunks per output row
+  static_assert(BM * BN * 2 <= kDmaStages * STAGE, "output tile fits the stage buffers");
   uint8_t* ot = lds;
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
@@ -717,8 +744,8 @@ __global__ __launch_bounds__(256, 2) void fp4_gemm_dma_kernel(
   }
   __syncthreads();
 #pragma unroll
-  for (int p = 0; p < BM * CPR / 256; ++p) {
-    const int L = p * 256 + tid;
+  for (int p = 0; p < BM * CPR / THREADS; ++p) {
+    const int L = p * THREADS + tid;
     const int row = L / CPR, c = L % CPR;
     const int64_t m = m0 + row, n = n0 + c * 8;
     if (m < M && n < N)
@@ -790,10 +817,23 @@ hipError_t launch_fp4_gemm(const uint8_t* xq, const uint8_t* xs, const float* xt
   if (M > kStreamMaxM) {
     int64_t tiles = ((M + kLdsBM - 1) / kLdsBM) * ((N + kLdsBN - 1) / kLdsBN);
     tiles = (tiles + 7) / 8 * 8;
-    if (K % 128 == 0)   // staged codes, dequantized per fragment
-      hipLaunchKernelGGL(fp4_gemm_dma_kernel, dim3((unsigned)tiles), dim3(256), 0, s, xq, xs, xt,
-                         wq, wsc, wt, y, M, N, K);
-    else
+    if (K % 128 == 0) {   // staged codes, dequantized per fragment
+      // 256 x 256 tiles (one workgroup per CU, 1.15-1.2x the rate of a
+      // 128 x 128 tile pair in a round of the Llama-sized MLP) when their
+      // rounds over the 256 CUs take no longer: a round of big tiles costs
+      // about 1.75 rounds of 512 small ones, and up to 256 small tiles run
+      // one per CU at about 0.56 of a round
+      const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
+      const int64_t rb = (big + 255) / 256, rs = (tiles + 511) / 512;
+      if (tiles > 256 && 7 * rb <= 4 * rs) {
+        const int64_t bt = (big + 7) / 8 * 8;
+        hipLaunchKernelGGL((fp4_gemm_dma_kernel<256, 256, 4, 2>), dim3((unsigned)bt), dim3(512), 0,
+                           s, xq, xs, xt, wq, wsc, wt, y, M, N, K);
+      } else {
+        hipLaunchKernelGGL((fp4_gemm_dma_kernel<128, 128, 2, 2>), dim3((unsigned)tiles), dim3(256),
+                           0, s, xq, xs, xt, wq, wsc, wt, y, M, N, K);
+      }
+    } else
       hipLaunchKernelGGL((fp4_gemm_lds_kernel<2, kFp4WavesN>), dim3((unsigned)tiles),
                          dim3(64 * 2 * kFp4WavesN), 0, s, xq, xs, xt, wq, wsc, wt, y, M, N, K);
     return hipGetLastError();
@@ -827,3 +867,4 @@ hipError_t launch_fp4_gemm(const uint8_t* xq, const uint8_t* xs, const float* xt
 }
 
 }  // namespace bsfp8
+

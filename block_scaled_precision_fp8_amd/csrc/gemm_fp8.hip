@@ -1224,44 +1224,60 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_pers_kernel(
     // 1 x 128 group per quarter-wave, 8 values per lane, the group amax
     // gathered over the quarter-wave's 16 lanes; xstat: the static scheme's
     // calibrated scale.  (Every workgroup repeats this M x K quantization, so
-    // the launcher keeps it to small M.)
+    // the launcher keeps it to small M: at 16 x 4096 the repeated encoding
+    // costs more vector-ALU time than the quantization launch it saves.)
+    // Each lane has XU groups' loads in flight before encoding any of them.
     const int ql = threadIdx.x & 15;
     const int ngroups = M * KB;
-    for (int gi = threadIdx.x >> 4; gi < ngroups; gi += 4 * kDecodeWaves) {
-      const int m = gi / KB, g = gi - m * KB;
-      const int64_t k0 = (int64_t)g * 128 + ql * 8;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (k0 < K) v = *(const uint4*)(x + (int64_t)m * ldx + k0);
-      const float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
-                          bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
-      float sc = 0.0f;
-      int e = 0;
-      if (xstat) {
-        if (FMT == 0) sc = *(const float*)xstat;
-        else e = (int)*(const uint8_t*)xstat - 127;
-      } else {
-        float amax = 0.0f;
+    constexpr int QW = 4 * kDecodeWaves;     // quarter-waves per workgroup
+    constexpr int XU = 4;                    // groups (loads) in flight per lane
+    for (int gi0 = threadIdx.x >> 4; gi0 < ngroups; gi0 += XU * QW) {
+      uint4 v[XU];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+      for (int u = 0; u < XU; ++u) {
+        const int gi = gi0 + u * QW;
+        const int m = gi / KB, g = gi - m * KB;
+        const int64_t k0 = (int64_t)g * 128 + ql * 8;
+        v[u] = make_uint4(0, 0, 0, 0);
+        if (gi < ngroups && k0 < K) v[u] = *(const uint4*)(x + (int64_t)m * ldx + k0);
+      }
 #pragma unroll
-        for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-        if (FMT == 0) sc = act_scale_f32(amax);
-        else e = ue8m0_exp(amax);
-      }
-      uint2 codes;
-      if (FMT == 0 && (xstat || !(sc >= kMinNormal))) {
-        // a subnormal or static scale: divide directly (as the other fused paths)
-        codes.x = act_encode4<FMT>(f[0], f[1], f[2], f[3], sc, e);
-        codes.y = act_encode4<FMT>(f[4], f[5], f[6], f[7], sc, e);
-      } else {
-        const RcpDiv dv = rcp_div(FMT == 0 ? sc : 1.0f);
-        codes.x = act_encode4_rcp<FMT>(f[0], f[1], f[2], f[3], dv, e);
-        codes.y = act_encode4_rcp<FMT>(f[4], f[5], f[6], f[7], dv, e);
-      }
-      if (k0 < K) *(uint2*)(sxl + m * KP + k0) = codes;
-      if (ql == 0) {
-        if (FMT == 0) ((float*)sxs)[gi] = sc;
-        else sxs[gi] = (uint8_t)(e + 127);
+      for (int u = 0; u < XU; ++u) {
+        const int gi = gi0 + u * QW;
+        if (gi >= ngroups) break;            // uniform per quarter-wave
+        const int m = gi / KB, g = gi - m * KB;
+        const int64_t k0 = (int64_t)g * 128 + ql * 8;
+        const float f[8] = {bf16_lo(v[u].x), bf16_hi(v[u].x), bf16_lo(v[u].y), bf16_hi(v[u].y),
+                            bf16_lo(v[u].z), bf16_hi(v[u].z), bf16_lo(v[u].w), bf16_hi(v[u].w)};
+        float sc = 0.0f;
+        int e = 0;
+        if (xstat) {
+          if (FMT == 0) sc = *(const float*)xstat;
+          else e = (int)*(const uint8_t*)xstat - 127;
+        } else {
+          float amax = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+#pragma unroll
+          for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+          if (FMT == 0) sc = act_scale_f32(amax);
+          else e = ue8m0_exp(amax);
+        }
+        uint2 codes;
+        if (FMT == 0 && (xstat || !(sc >= kMinNormal))) {
+          // a subnormal or static scale: divide directly (as the other fused paths)
+          codes.x = act_encode4<FMT>(f[0], f[1], f[2], f[3], sc, e);
+          codes.y = act_encode4<FMT>(f[4], f[5], f[6], f[7], sc, e);
+        } else {
+          const RcpDiv dv = rcp_div(FMT == 0 ? sc : 1.0f);
+          codes.x = act_encode4_rcp<FMT>(f[0], f[1], f[2], f[3], dv, e);
+          codes.y = act_encode4_rcp<FMT>(f[4], f[5], f[6], f[7], dv, e);
+        }
+        if (k0 < K) *(uint2*)(sxl + m * KP + k0) = codes;
+        if (ql == 0) {
+          if (FMT == 0) ((float*)sxs)[gi] = sc;
+          else sxs[gi] = (uint8_t)(e + 127);
+        }
       }
     }
   } else {

@@ -83,6 +83,9 @@ def _gemm_dev(h, M, N):
     (200, 264, 2144), (129, 136, 96),     # K blocks ending after 96 of 128 values
     # K % 128 == 0, M > 64: codes staged through the four-stage LDS pipeline
     (384, 1024, 4096), (300, 1000, 1152), (129, 136, 128), (4100, 264, 640),
+    # enough 128 x 128 tiles for two rounds, one round of 256 x 256 tiles:
+    # the 256 x 256 tile, ragged in M and N, with 1 and 5 K blocks
+    (1536, 6144, 128), (1300, 8200, 256), (1100, 8296, 640),
 ])
 def test_fp4_gemm_parity(M, N, K):
     say(f"fp4 gemm M={M} N={N} K={K}")
