@@ -629,7 +629,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
     const int kb_cur = kb_next - 1;
     const uint8_t* sx = lds + buf * STAGE + (wm * WM + l16) * kRowBytes;
     const uint8_t* swl = lds + buf * STAGE + XBYTES + (wn * WN + l16) * kWRow;
-    issue(kb_next, buf ^ 1);
+    // dense 256 x 256 tiles: the upper half of the waves issues its share of
+    // the next stage after its first MFMA group, so half the waves reach
+    // their MFMAs without queueing behind the whole stage's DMA (1-4% on the
+    // Llama and DeepSeek shapes, same bits; after the second group instead,
+    // the stage lands late and fp32-scale runs take 1.7x)
+    constexpr bool LATE = BM == 256 && BN == 256 && !GROUPED && !W4 && !SWIGLU && !XQ;
+    if (!LATE || wave < WAVES / 2) issue(kb_next, buf ^ 1);
     float sa[MI];
     float sw = W4 ? 0.0f : sw_reg[buf];
     if (FMT == 1) sw = __int_as_float(__float_as_int(sw) & 0xff);
@@ -710,6 +716,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
         }
       }
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (LATE && g == 0) {
+        if (wave >= WAVES / 2) issue(kb_next, buf ^ 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     });
   };
 
