@@ -515,7 +515,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
 
   // issue one stage: X and W tiles into LDS buffer `buf`, scales into
   // registers; exactly LOADS vector-memory ops per lane, in this order.
-  auto issue = [&](int kb, int buf) {
+  // part 1 issues the X tile only, part 2 the rest (0: all).
+  auto issue = [&](int kb, int buf, int part = 0) {
     uint8_t* sx = lds + buf * STAGE;
     uint8_t* sw = sx + XBYTES;
     const uint32_t kbyte = (uint32_t)kb * 128;
@@ -528,7 +529,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
         xr[j] = u32x4{0u, 0u, 0u, 0u};
         if (row < mrows && k < K) xr[j] = *(const u32x4*)(xrow + row * ldx + k);
       }
-    } else {
+    } else if (part != 2) {
 #pragma unroll
       for (int j = 0; j < XJ; ++j) {
         const int q = (j * WAVES + wave) * 64 + lane;
@@ -536,6 +537,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
                                                  16, dma_src(q, mrows, kbyte), 0, 0, 0);
       }
     }
+    if (part == 1) return;
 #pragma unroll
     for (int j = 0; j < WJ; ++j) {
       const int q = (j * WAVES + wave) * 64 + lane;
@@ -629,13 +631,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
     const int kb_cur = kb_next - 1;
     const uint8_t* sx = lds + buf * STAGE + (wm * WM + l16) * kRowBytes;
     const uint8_t* swl = lds + buf * STAGE + XBYTES + (wn * WN + l16) * kWRow;
-    // dense 256 x 256 tiles: the upper half of the waves issues its share of
-    // the next stage after its first MFMA group, so half the waves reach
-    // their MFMAs without queueing behind the whole stage's DMA (1-4% on the
-    // Llama and DeepSeek shapes, same bits; after the second group instead,
-    // the stage lands late and fp32-scale runs take 1.7x)
+    // dense 256 x 256 tiles: every wave issues the next stage's X tile here
+    // and its W tile and scales after its first MFMA group, so no wave waits
+    // behind its whole share of the stage's DMA before its first MFMAs
+    // (2-5% on the Llama and DeepSeek shapes, same bits; half the waves
+    // issuing all of theirs after the first group: 1-4%; after the second
+    // group, the stage lands late and fp32-scale runs take 1.7x)
     constexpr bool LATE = BM == 256 && BN == 256 && !GROUPED && !W4 && !SWIGLU && !XQ;
-    if (!LATE || wave < WAVES / 2) issue(kb_next, buf ^ 1);
+    issue(kb_next, buf ^ 1, LATE ? 1 : 0);
     float sa[MI];
     float sw = W4 ? 0.0f : sw_reg[buf];
     if (FMT == 1) sw = __int_as_float(__float_as_int(sw) & 0xff);
@@ -717,7 +720,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
       }
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (LATE && g == 0) {
-        if (wave >= WAVES / 2) issue(kb_next, buf ^ 1);
+        issue(kb_next, buf ^ 1, 2);
         __builtin_amdgcn_sched_barrier(0);
       }
     });
