@@ -631,13 +631,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
     const int kb_cur = kb_next - 1;
     const uint8_t* sx = lds + buf * STAGE + (wm * WM + l16) * kRowBytes;
     const uint8_t* swl = lds + buf * STAGE + XBYTES + (wn * WN + l16) * kWRow;
-    // dense 256 x 256 tiles: every wave issues the next stage's X tile here
-    // and its W tile and scales after its first MFMA group, so no wave waits
-    // behind its whole share of the stage's DMA before its first MFMAs
-    // (2-5% on the Llama and DeepSeek shapes, same bits; half the waves
-    // issuing all of theirs after the first group: 1-4%; after the second
-    // group, the stage lands late and fp32-scale runs take 1.7x)
-    constexpr bool LATE = BM == 256 && BN == 256 && !GROUPED && !W4 && !SWIGLU && !XQ;
+    // 256 x 256 tiles and grouped tiles: every wave issues the next stage's
+    // X tile here and its W tile and scales after its first MFMA group, so
+    // no wave waits behind its whole share of the stage's DMA before its
+    // first MFMAs (same bits; 2-5% on the dense Llama and DeepSeek shapes,
+    // 2-3% with MXFP4 weights, 6% on the MXFP4 MoE experts, 0-1% on the
+    // FP8 ones; 2% slower on dense 128 x 256 MXFP4 and 64-row tiles, 3-4%
+    // on dense 128 x 256 FP8 tiles at M = 128, which keep one issue point.
+    // Half the waves issuing all of theirs after the first group: 1-4%;
+    // after the second group, the stage lands late: fp32 scales 1.7x slower)
+    constexpr bool LATE = !XQ && ((BM == 256 && BN == 256) || GROUPED);
     issue(kb_next, buf ^ 1, LATE ? 1 : 0);
     float sa[MI];
     float sw = W4 ? 0.0f : sw_reg[buf];
