@@ -227,6 +227,14 @@ __device__ __forceinline__ Tile grouped_tile(const int32_t* __restrict__ seg, in
 __device__ __forceinline__ v8i read_frag(const uint8_t* __restrict__ row, int ch0, int ch1) {
   return join(*(const uint4*)(row + ch0), *(const uint4*)(row + ch1));
 }
+// an MXFP4 weight fragment: one 16-byte chunk per lane.  Like read_frag, it
+// reads through a restrict-qualified pointer: the alias scope that gives
+// the load lets the compiler see that it does not read the stage the DMA
+// in flight writes (a plain dereference made it wait for all of that DMA
+// before every W4 fragment read).
+__device__ __forceinline__ v8i read_frag_w4(const uint8_t* __restrict__ row, int chw) {
+  return join(*(const uint4*)(row + chw), make_uint4(0, 0, 0, 0));
+}
 // a staged scale, read the same way (no wait for the in-flight DMA)
 __device__ __forceinline__ float read_scale(const float* __restrict__ p, int idx) { return p[idx]; }
 __device__ __forceinline__ uint32_t read_byte(const uint8_t* __restrict__ p, int idx) { return p[idx]; }
@@ -614,7 +622,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_lds_kernel(
   const int chw = (g4 ^ ((l16 >> 2) & 3)) << 4;   // MXFP4 W rows: chunk g4
   // a W fragment: FP8 rows as X, MXFP4 rows one 16-byte chunk per lane
   auto wfrag = [&](const uint8_t* row) -> v8i {
-    if constexpr (W4) return join(*(const uint4*)(row + chw), make_uint4(0, 0, 0, 0));
+    if constexpr (W4) return read_frag_w4(row, chw);
     else return read_frag(row, ch0, ch1);
   };
 
