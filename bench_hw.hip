@@ -7,7 +7,10 @@
 //   2. LDS read throughput per CU with 16-byte reads;
 //   3. the scaled FP8 MFMA (16x16x128) alone, and followed by the fp32
 //      promotion of its 16x16 result (acc += t * c, four FMAs per lane), at
-//      one and two waves per SIMD.
+//      one and two waves per SIMD;
+//   4. the floor of a decode-shaped launch: 256 workgroups of 1024 lanes
+//      reading 0-117 MB once (each lane 16-byte loads, four in flight),
+//      back to back, the per-launch time and the rate.
 // Build and run:
 //   hipcc -O3 -std=c++17 --offload-arch=gfx950 -Xclang -target-feature \
 //     -Xclang -packed-fp32-ops -o /tmp/bench_hw bench_hw.hip && /tmp/bench_hw
@@ -15,6 +18,7 @@
 #include <hip/hip_runtime.h>
 #include <cstdio>
 #include <cstdint>
+#include <algorithm>
 
 #define CHECK(x)                                                                \
   do {                                                                          \
@@ -142,6 +146,23 @@ __global__ __launch_bounds__(512) void mfma_loop(int iters, float c, uint32_t* s
   if (s == 1234.5f) sink[blockIdx.x] = 5;
 }
 
+// 4. one pass over `bytes` (a multiple of 16 x 1024 x 256): workgroup b
+// reads its contiguous share, 16 bytes per lane per load, four in flight
+__global__ __launch_bounds__(1024) void stream_once(const uint4* __restrict__ src, int64_t n16,
+                                                    uint32_t* sink) {
+  const int64_t per = n16 / gridDim.x;
+  const uint4* p = src + (int64_t)blockIdx.x * per;
+  uint4 acc = make_uint4(0, 0, 0, 0);
+  for (int64_t i = threadIdx.x; i < per; i += 4 * 1024) {
+    uint4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = i + u * 1024 < per ? p[i + u * 1024] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) { acc.x ^= v[u].x; acc.y ^= v[u].y; acc.z ^= v[u].z; acc.w ^= v[u].w; }
+  }
+  if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x2468ace0u) sink[blockIdx.x] = 6;
+}
+
 template <typename F>
 static float time_ms(F launch, int reps) {
   hipEvent_t a, b;
@@ -226,6 +247,20 @@ int main() {
       printf("%-34s | %d | %8.1f | %7.1f\n", promote ? "MFMA + fp32 promotion (4 FMAs)" : "MFMA accumulating",
              threads / 256, ms * 1e3, fl / (ms * 1e-3) / 1e12);
     }
+  }
+  CHECK(hipGetLastError());
+
+  printf("# 4. decode-shaped launches (256 x 1024 lanes), back to back over rotating buffers: MB | us per launch | TB/s\n");
+  for (int mb : {0, 17, 25, 60, 117}) {
+    const int64_t bytes = (int64_t)mb << 20;
+    const int64_t n16 = bytes / 16 / (1024 * 256) * (1024 * 256);
+    const int copies = mb ? (int)std::min<int64_t>(8, (int64_t)(big / std::max<int64_t>(bytes, 1))) : 1;
+    int it = 0;
+    const float ms = time_ms([&] {
+      const uint4* p = (const uint4*)(src + (size_t)(it++ % copies) * (size_t)bytes);
+      hipLaunchKernelGGL(stream_once, dim3(256), dim3(1024), 0, 0, p, n16, sink);
+    }, 40);
+    printf("%4d | %7.2f | %6.2f\n", mb, ms * 1e3, n16 * 16.0 / (ms * 1e-3) / 1e12);
   }
   CHECK(hipGetLastError());
   CHECK(hipDeviceSynchronize());
