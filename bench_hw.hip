@@ -148,15 +148,16 @@ __global__ __launch_bounds__(512) void mfma_loop(int iters, float c, uint32_t* s
 
 // 4. one pass over `bytes` (a multiple of 16 x 1024 x 256): workgroup b
 // reads its contiguous share, 16 bytes per lane per load, four in flight
-__global__ __launch_bounds__(1024) void stream_once(const uint4* __restrict__ src, int64_t n16,
-                                                    uint32_t* sink) {
+template <int T>
+__global__ __launch_bounds__(T) void stream_once(const uint4* __restrict__ src, int64_t n16,
+                                                 uint32_t* sink) {
   const int64_t per = n16 / gridDim.x;
   const uint4* p = src + (int64_t)blockIdx.x * per;
   uint4 acc = make_uint4(0, 0, 0, 0);
-  for (int64_t i = threadIdx.x; i < per; i += 4 * 1024) {
+  for (int64_t i = threadIdx.x; i < per; i += 4 * T) {
     uint4 v[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = i + u * 1024 < per ? p[i + u * 1024] : make_uint4(0, 0, 0, 0);
+    for (int u = 0; u < 4; ++u) v[u] = i + u * T < per ? p[i + u * T] : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int u = 0; u < 4; ++u) { acc.x ^= v[u].x; acc.y ^= v[u].y; acc.z ^= v[u].z; acc.w ^= v[u].w; }
   }
@@ -250,17 +251,20 @@ int main() {
   }
   CHECK(hipGetLastError());
 
-  printf("# 4. decode-shaped launches (256 x 1024 lanes), back to back over rotating buffers: MB | us per launch | TB/s\n");
-  for (int mb : {0, 17, 25, 60, 117}) {
-    const int64_t bytes = (int64_t)mb << 20;
-    const int64_t n16 = bytes / 16 / (1024 * 256) * (1024 * 256);
-    const int copies = mb ? (int)std::min<int64_t>(8, (int64_t)(big / std::max<int64_t>(bytes, 1))) : 1;
-    int it = 0;
-    const float ms = time_ms([&] {
-      const uint4* p = (const uint4*)(src + (size_t)(it++ % copies) * (size_t)bytes);
-      hipLaunchKernelGGL(stream_once, dim3(256), dim3(1024), 0, 0, p, n16, sink);
-    }, 40);
-    printf("%4d | %7.2f | %6.2f\n", mb, ms * 1e3, n16 * 16.0 / (ms * 1e-3) / 1e12);
+  printf("# 4. decode-shaped launches (256 workgroups), back to back over rotating buffers: lanes per workgroup | MB | us per launch | TB/s\n");
+  for (int lanes : {1024, 256}) {
+    for (int mb : {0, 17, 25, 60, 117}) {
+      const int64_t bytes = (int64_t)mb << 20;
+      const int64_t n16 = bytes / 16 / (1024 * 256) * (1024 * 256);
+      const int copies = mb ? (int)std::min<int64_t>(8, (int64_t)(big / std::max<int64_t>(bytes, 1))) : 1;
+      int it = 0;
+      const float ms = time_ms([&] {
+        const uint4* p = (const uint4*)(src + (size_t)(it++ % copies) * (size_t)bytes);
+        if (lanes == 1024) hipLaunchKernelGGL(stream_once<1024>, dim3(256), dim3(1024), 0, 0, p, n16, sink);
+        else hipLaunchKernelGGL(stream_once<256>, dim3(256), dim3(256), 0, 0, p, n16, sink);
+      }, 40);
+      printf("%4d | %4d | %7.2f | %6.2f\n", lanes, mb, ms * 1e3, n16 * 16.0 / (ms * 1e-3) / 1e12);
+    }
   }
   CHECK(hipGetLastError());
   CHECK(hipDeviceSynchronize());
