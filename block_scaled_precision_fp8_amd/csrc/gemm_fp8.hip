@@ -241,6 +241,9 @@ __device__ __forceinline__ uint32_t read_byte(const uint8_t* __restrict__ p, int
 __device__ __forceinline__ uint32_t read_u32(const uint8_t* __restrict__ p, int off) {
   return *(const uint32_t*)(p + off);
 }
+__device__ __forceinline__ long read_u64(const uint8_t* __restrict__ p, int off) {
+  return *(const long*)(p + off);
+}
 __device__ __forceinline__ float4 read_scale4(const uint8_t* __restrict__ p, int off) {
   return *(const float4*)(p + off);
 }
@@ -1559,33 +1562,49 @@ __global__ __launch_bounds__(256, 2) void gemm_b32_kernel(
 #pragma unroll
         for (int g = 0; g < 4; ++g) sa[j][g] = sa_reg[buf][j][g];
     }
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      // rows start at multiples of 16: the row swizzle is the lane's (l16 >> 1)
+    // fragments of group g: rows start at multiples of 16, so the row
+    // swizzle is the lane's (l16 >> 1)
+    long bx[2][MI], aw[2][NI];
+    auto rd = [&](int g, int s) {
       const int u = 4 * g + g4;
       const int off = (((u >> 1) ^ (l16 >> 1)) << 4) + ((u & 1) << 3);
-      long bx[MI], aw[NI];
 #pragma unroll
-      for (int j = 0; j < MI; ++j) bx[j] = *(const long*)(sx + j * 16 * kRowBytes + off);
+      for (int j = 0; j < MI; ++j) bx[s][j] = read_u64(sx + j * 16 * kRowBytes, off);
 #pragma unroll
-      for (int i = 0; i < NI; ++i) aw[i] = *(const long*)(swl + i * 16 * kRowBytes + off);
+      for (int i = 0; i < NI; ++i) aw[s][i] = read_u64(swl + i * 16 * kRowBytes, off);
+    };
+    rd(0, 0);
+    static_for<4>([&](auto gc) {
+      constexpr int g = decltype(gc)::value;
+      if constexpr (g + 1 < 4) rd(g + 1, (g + 1) & 1);
       float sc[2][MI];
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int j = 0; j < MI; ++j) sc[b][j] = sa[j][g] * sw_reg[buf][b][g];
+      // the group's 16 products first, then their promotions: long runs of
+      // independent MFMAs and of FMAs, which the two waves of a SIMD overlap
+      // (with the next group's fragments read ahead: same bits, 1.15-1.3x
+      // over one product promoted after each MFMA)
+      v4f t[NI][MI];
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int j = 0; j < MI; ++j)
+          t[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(aw[g & 1][i], bx[g & 1][j], zero, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int j = 0; j < MI; ++j) {
-          const v4f t = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(aw[i], bx[j], zero, 0, 0, 0);
           const float s = sc[i >> 1][j];
-          acc[i][j][0] = fmaf(t[0], s, acc[i][j][0]);
-          acc[i][j][1] = fmaf(t[1], s, acc[i][j][1]);
-          acc[i][j][2] = fmaf(t[2], s, acc[i][j][2]);
-          acc[i][j][3] = fmaf(t[3], s, acc[i][j][3]);
+          acc[i][j][0] = fmaf(t[i][j][0], s, acc[i][j][0]);
+          acc[i][j][1] = fmaf(t[i][j][1], s, acc[i][j][1]);
+          acc[i][j][2] = fmaf(t[i][j][2], s, acc[i][j][2]);
+          acc[i][j][3] = fmaf(t[i][j][3], s, acc[i][j][3]);
         }
-    }
+      __builtin_amdgcn_sched_barrier(0);
+    });
   };
 
   issue(0, 0);
