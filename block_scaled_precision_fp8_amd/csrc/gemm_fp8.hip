@@ -1400,9 +1400,11 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_pers_kernel(
 // scale groups and, with fp32 scales, each group's partial product needs a
 // promotion of its own, so a K block runs as four 16x16x32 FP8 MFMAs per
 // output tile: acc += (s_a[m, g] s_w[n / 32, g]) P_g.  (The 16x16x128
-// scaled form applies one power of two per lane's 32 values and cannot
-// carry fp32 scales.)  UE8M0 scales take the same path as the powers of two
-// they encode.  Tile 128 (m) x 128 (n), four waves of 64 x 64, two LDS
+// scaled form applies one power of two per row and 32-wide K group and
+// cannot carry fp32 scales.)  UE8M0 scales are exactly such powers of two:
+// they run one scaled 16x16x128 MFMA per tile and K block, each group's
+// pair of scale bytes passed as its operands (1.8-2.9x over the fp32 form
+// on the same shapes).  Tile 128 (m) x 128 (n), four waves of 64 x 64, two LDS
 // stages laid out as in the large-M kernel: the 8-byte fragment a lane
 // takes for group g is half (u & 1) of logical chunk u >> 1, u = 4 g + g4,
 // and the chunk swizzle keeps those reads free of bank conflicts.
@@ -1472,6 +1474,9 @@ __global__ __launch_bounds__(256, 2) void gemm_b32_kernel(
   const int64_t nb0 = (tl.n0 + wn * 64) >> 5;        // the wave's two weight blocks
   float sa_reg[SCL ? 1 : 2][MI][4];
   float sw_reg[2][2][4];
+  // UE8M0: the raw scale bytes of this lane's group 4 kb + g4 (see step)
+  int sa_raw[FMT == 1 && !SCL ? 2 : 1][MI];
+  int sw_raw[FMT == 1 ? 2 : 1][2];
 
   auto issue = [&](int kb, int buf) {
     uint8_t* sx = lds + buf * STAGE;
@@ -1500,6 +1505,22 @@ __global__ __launch_bounds__(256, 2) void gemm_b32_kernel(
         }
       }
     }
+    if constexpr (FMT == 1) {
+      const int gi = kb * 4 + g4;
+      if constexpr (!SCL) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+          const uint32_t off = (saoff[i] == kOOB || gi >= GS) ? kOOB : saoff[i] + gi;
+          sa_raw[buf][i] = (int)__builtin_amdgcn_raw_buffer_load_b8(rsa, off, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int64_t nbs = nb0 + b;
+        const uint32_t off = (nbs < NBS && gi < GS) ? (uint32_t)(nbs * GS + gi) : kOOB;
+        sw_raw[buf][b] = (int)__builtin_amdgcn_raw_buffer_load_b8(rsw, off, 0, 0);
+      }
+    } else {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int gi = kb * 4 + g;
@@ -1521,6 +1542,7 @@ __global__ __launch_bounds__(256, 2) void gemm_b32_kernel(
             : e8m0_f32(__builtin_amdgcn_raw_buffer_load_b8(rsw, off, 0, 0));
       }
     }
+    }
   };
 
   v4f acc[NI][MI];
@@ -1534,6 +1556,45 @@ __global__ __launch_bounds__(256, 2) void gemm_b32_kernel(
     const uint8_t* sx = lds + buf * STAGE + (wm * 64 + l16) * kRowBytes;
     const uint8_t* swl = lds + buf * STAGE + XBYTES + (wn * 64 + l16) * kRowBytes;
     issue(kb_next, buf ^ 1);
+    if constexpr (FMT == 1) {
+      // UE8M0: one scaled 16x16x128 MFMA per tile and K block.  Its per-lane
+      // scale operands follow the operand's K order, not the lane's own
+      // bytes: lane (l16, g4) holds K [16 g4, 16 g4 + 16) and
+      // [64 + 16 g4, 80 + 16 g4) of row l16 (the fragment layout of the
+      // 128-block kernel), while its scale byte serves row l16's K group
+      // [32 g4, 32 g4 + 32) -- two other lanes' bytes (checked on the GPU,
+      // every lane and byte of both operands).  So lane g4 passes group
+      // 4 kb + g4: the row's activation scale, the subtile's weight-block
+      // scale.  Groups past K take 2^0 (their codes are zeros).
+      const int kb = kb_next - 1;
+      const bool gin = kb * 4 + g4 < GS;
+      int sxb[MI], swb[2];
+#pragma unroll
+      for (int j = 0; j < MI; ++j) {
+        if constexpr (SCL) {
+          const uint8_t* sc = sbuf + ((kb / SCH) & 1) * SBUF + (kb % SCH) * 4;
+          sxb[j] = gin ? (int)read_byte(sc, (wm * 64 + j * 16 + l16) * 32 + g4) : 127;
+        } else {
+          sxb[j] = gin ? sa_raw[buf][j] & 0xff : 127;
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < 2; ++b) swb[b] = gin ? sw_raw[buf][b] & 0xff : 127;
+      const int ch0 = (g4 ^ (l16 >> 1)) << 4;
+      const int ch1 = ((g4 + 4) ^ (l16 >> 1)) << 4;
+      v8i bx[MI];
+#pragma unroll
+      for (int j = 0; j < MI; ++j) bx[j] = read_frag(sx + j * 16 * kRowBytes, ch0, ch1);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const v8i aw = read_frag(swl + i * 16 * kRowBytes, ch0, ch1);
+#pragma unroll
+        for (int j = 0; j < MI; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aw, bx[j], acc[i][j], 0, 0, 0,
+                                                                        swb[i >> 1], 0, sxb[j]);
+      }
+      return;
+    }
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
     // this block's token scales (4 groups per row) from the chunk buffer;
     // groups past K take 0 so no other row's scale meets a zero product

@@ -123,23 +123,26 @@ def test_block32_linear_equals_quant_then_gemm(fmt):
     assert np.array_equal(F.bf16_decode(bf16_bits(y)), got)
 
 
-def test_block32_gemm_full_size_sampled():
-    """Llama-3-8B o_proj shape at M = 2048 with (32, 32) blocks; the oracle
-    recomputes 2048 sampled outputs."""
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_block32_gemm_full_size_sampled(fmt):
+    """Llama-3-8B o_proj shape at M = 2048 with (32, 32) blocks (fp32 scales;
+    UE8M0 scales run the scaled-MFMA form); the oracle recomputes 2048
+    sampled outputs."""
     import torch
     from block_scaled_precision_fp8_amd import lib as L
-    M, N, K, fmt = 2048, 4096, 4096, 0
-    say(f"gemm 32x32 full size M={M} N={N} K={K}")
+    M, N, K = 2048, 4096, 4096
+    say(f"gemm 32x32 full size M={M} N={N} K={K} fmt={fmt}")
     x = synth.llama_acts(M, K, seed=1)
     w = synth.normal_bf16((N, K), 0.02, "llama", "w", seed=2)
+    sdt = torch.uint8 if fmt else torch.float32
     xq = torch.empty((M, K), dtype=torch.uint8, device="cuda")
-    xs = torch.empty((M, K // 32), dtype=torch.float32, device="cuda")
+    xs = torch.empty((M, K // 32), dtype=sdt, device="cuda")
     wq = torch.empty((N, K), dtype=torch.uint8, device="cuda")
-    ws = torch.empty((N // 32, K // 32), dtype=torch.float32, device="cuda")
-    L.fp8_quant_act(to_dev_bf16(x), xq, xs, group_k=32)
-    L.fp8_quant_weight(to_dev_bf16(w), wq, ws, block_n=32, block_k=32)
+    ws = torch.empty((N // 32, K // 32), dtype=sdt, device="cuda")
+    L.fp8_quant_act(to_dev_bf16(x), xq, xs, group_k=32, scale_fmt=fmt)
+    L.fp8_quant_weight(to_dev_bf16(w), wq, ws, block_n=32, block_k=32, scale_fmt=fmt)
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-    L.fp8_block_gemm(xq, xs, wq, ws, y, block_n=32, block_k=32)
+    L.fp8_block_gemm(xq, xs, wq, ws, y, block_n=32, block_k=32, scale_fmt=fmt)
     torch.cuda.synchronize()
     g = np.random.default_rng(3)
     rows, cols = g.integers(0, M, 2048), g.integers(0, N, 2048)
