@@ -551,19 +551,20 @@ def run_mxfp4(torch, L, synth, steps, warmup, dev, sp):
     return out
 
 
-def run_block32(torch, L, synth, steps, warmup, dev, sp):
+def run_block32(torch, L, synth, steps, warmup, dev, sp, fmt=0):
     """FP8 linears with (32, 32) weight blocks and 1x32 act groups (fp32
-    scales) at Llama-3-8B o_proj / gate+up shapes: fp8_linear, act quant
-    included."""
+    scales, or UE8M0 with fmt=1) at Llama-3-8B o_proj / gate+up shapes:
+    fp8_linear, act quant included."""
     out = []
     stream = torch.cuda.current_stream()
+    sdt = torch.uint8 if fmt else torch.float32
     for M, K, N in ((16, 4096, 4096), (2048, 4096, 4096), (8192, 4096, 28672)):
         wb = synth.device_normal_bf16((N, K), 0.02, "llama", "w", index=N + 32)
         copies = []
         for c in range(copies_for(N * K)):
             wq = torch.empty((N, K), dtype=torch.uint8, device=dev)
-            ws = torch.empty((N // 32, K // 32), dtype=torch.float32, device=dev)
-            L.fp8_quant_weight(wb, wq, ws, block_n=32, block_k=32, stream=sp)
+            ws = torch.empty((N // 32, K // 32), dtype=sdt, device=dev)
+            L.fp8_quant_weight(wb, wq, ws, block_n=32, block_k=32, scale_fmt=fmt, stream=sp)
             copies.append((wq, ws))
         del wb
         x = synth.device_llama_acts(M, K, index=M)
@@ -573,7 +574,8 @@ def run_block32(torch, L, synth, steps, warmup, dev, sp):
 
         def call(i):
             wq, ws = copies[i % len(copies)]
-            L.fp8_linear(x, wq, ws, y, block_n=32, block_k=32, workspace=wsp, stream=sp)
+            L.fp8_linear(x, wq, ws, y, block_n=32, block_k=32, scale_fmt=fmt, workspace=wsp,
+                         stream=sp)
         for i in range(warmup):
             call(i)
         torch.cuda.synchronize()
@@ -585,14 +587,15 @@ def run_block32(torch, L, synth, steps, warmup, dev, sp):
         torch.cuda.synchronize()
         ms = tm.ms("a", "b")
         fl = 2.0 * M * N * K
-        sa, sw = 4 * M * (K // 32), 4 * (N // 32) * (K // 32)     # fp32 scales
+        sb = 1 if fmt else 4                                      # bytes per scale
+        sa, sw = sb * M * (K // 32), sb * (N // 32) * (K // 32)
         byt = (3 * M * K + sa) + (M * K + sa + N * K + sw + 2 * M * N)   # quant + GEMM
         d = dict(M=M, K=K, N=N, linear_us=round(ms * 1e3, 2),
                  tflops=round(fl / (ms * 1e-3) / 1e12, 1),
                  frac_fp8_peak=round(fl / (ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
                  gbs=round(byt / (ms * 1e-3) / 1e9, 1))
         out.append(d)
-        log(f"[block32] {d}")
+        log(f"[block32 fmt={fmt}] {d}")
         del copies, x, y, wsp
         torch.cuda.empty_cache()
     return out
@@ -737,6 +740,8 @@ def main():
     if "block32" in suites:
         detail["block32_fp32_scales"] = run_block32(torch, L, synth, max(5, args.steps // 2), 2,
                                                     dev, sp)
+        detail["block32_ue8m0"] = run_block32(torch, L, synth, max(5, args.steps // 2), 2, dev,
+                                              sp, fmt=1)
     if "wquant" in suites:
         detail["weight_quant"] = run_wquant(torch, L, synth, 10, 2, dev, sp)
 
