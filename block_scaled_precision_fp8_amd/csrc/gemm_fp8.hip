@@ -1007,9 +1007,23 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
     float swb[DEPTH];
     uint4 xa[XD], xb[XD];
     float sx[XD];
-    // FUSED: this lane's 32 bf16 activations of each block, loaded with the
-    // weights so that no block waits on a second round trip
+    // FUSED: this lane's 32 bf16 activations of each block, issued before
+    // the weights: loads complete in issue order, so encoding them then
+    // waits for them alone, while the weight loads are still in flight
     uint4 xv[FUSED ? DEPTH : 1][4];
+    if constexpr (FUSED) {
+#pragma unroll
+      for (int u = 0; u < DEPTH; ++u) {
+        const int kb = kb0 + u * kDecodeWaves;
+        const int64_t k0 = (int64_t)kb * 128 + kx0, k1 = (int64_t)kb * 128 + kx1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t k = (i < 2 ? k0 : k1) + 8 * (i & 1);
+          xv[u][i] = make_uint4(0, 0, 0, 0);
+          if (kb < KB && mvalid && k < K) xv[u][i] = *(const uint4*)(x + (int64_t)l16 * ldx + k);
+        }
+      }
+    }
     // B32: the four groups' scales (fp32), or this lane's group's bytes
     float sx4[B32 ? DEPTH : 1][4], sw32[B32 ? DEPTH : 1][4];
 #pragma unroll
@@ -1061,15 +1075,6 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
           const int64_t k = (int64_t)kb * 128 + g4 * 32;
           if (k < K) wa[u] = ld_stream16(wrow + k);
           if (k + 16 < K) wb[u] = ld_stream16(wrow + k + 16);
-        }
-      }
-      if constexpr (FUSED) {
-        const int64_t k0 = (int64_t)kb * 128 + kx0, k1 = (int64_t)kb * 128 + kx1;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t k = (i < 2 ? k0 : k1) + 8 * (i & 1);
-          xv[u][i] = make_uint4(0, 0, 0, 0);
-          if (kb < KB && mvalid && k < K) xv[u][i] = *(const uint4*)(x + (int64_t)l16 * ldx + k);
         }
       }
       if constexpr (!FUSED) {
@@ -1242,6 +1247,26 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_pers_kernel(
   };
 
   int t0 = blockIdx.x, c0 = 0;       // the launcher sizes the grid <= ntiles
+
+  // FUSED: the first XU groups' bf16 loads of every lane go out before the
+  // first weight chunk, so encoding them waits for them alone (loads
+  // complete in issue order); at M K <= 40960 that covers every group of
+  // up to 2.5 tokens
+  constexpr int QW = 4 * kDecodeWaves;     // quarter-waves per workgroup
+  constexpr int XU = 4;                    // groups (loads) in flight per lane
+  uint4 xv[FUSED ? XU : 1];
+  auto xload = [&](int gi0) __attribute__((always_inline)) {
+    const int ql = threadIdx.x & 15;
+#pragma unroll
+    for (int u = 0; u < XU; ++u) {
+      const int gi = gi0 + u * QW;
+      const int m = gi / KB, g = gi - m * KB;
+      const int64_t k0 = (int64_t)g * 128 + ql * 8;
+      xv[u] = make_uint4(0, 0, 0, 0);
+      if (gi < M * KB && k0 < K) xv[u] = *(const uint4*)(x + (int64_t)m * ldx + k0);
+    }
+  };
+  if constexpr (FUSED) xload(threadIdx.x >> 4);
   issue(std::integral_constant<int, 0>{}, t0, c0);   // in flight during the copy below
 
   // activation scales (M x KB) and codes (M x K), once per workgroup
@@ -1256,18 +1281,9 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_pers_kernel(
     // Each lane has XU groups' loads in flight before encoding any of them.
     const int ql = threadIdx.x & 15;
     const int ngroups = M * KB;
-    constexpr int QW = 4 * kDecodeWaves;     // quarter-waves per workgroup
-    constexpr int XU = 4;                    // groups (loads) in flight per lane
     for (int gi0 = threadIdx.x >> 4; gi0 < ngroups; gi0 += XU * QW) {
-      uint4 v[XU];
-#pragma unroll
-      for (int u = 0; u < XU; ++u) {
-        const int gi = gi0 + u * QW;
-        const int m = gi / KB, g = gi - m * KB;
-        const int64_t k0 = (int64_t)g * 128 + ql * 8;
-        v[u] = make_uint4(0, 0, 0, 0);
-        if (gi < ngroups && k0 < K) v[u] = *(const uint4*)(x + (int64_t)m * ldx + k0);
-      }
+      if (gi0 != (int)(threadIdx.x >> 4)) xload(gi0);   // the first batch is in flight
+      const uint4* v = xv;
 #pragma unroll
       for (int u = 0; u < XU; ++u) {
         const int gi = gi0 + u * QW;

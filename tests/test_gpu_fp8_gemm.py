@@ -47,6 +47,9 @@ def _gemm_dev(d, M, N, bias_bits=None, fmt=0):
     (4100, 4104, 384, True),      # enough tiles for the 256 x 256 tile, ragged in M and N
     (5, 16400, 1040, True),       # decode, N past 16K, ragged N and K
     (16, 16384, 256, False),      # decode, N = 16K
+    # decode with M x K codes too large to stage in LDS (the one-launch
+    # weight-streaming kernel): long and ragged rows
+    (16, 4104, 14336, True), (12, 1040, 14352, False), (4, 1032, 32784, True),
 ])
 def test_block_gemm_parity(M, N, K, bias, fmt):
     say(f"block gemm M={M} N={N} K={K} bias={bias} fmt={fmt}")
