@@ -571,3 +571,63 @@ def test_linear_fused_large_m_tiny_scales(fmt):
         b1, b2 = bf16_bits(y1), bf16_bits(y2)
         bad = np.argwhere(b1 != b2)
         assert bad.size == 0, f"{stat}: rows {np.unique(bad[:, 0])} differ"
+
+
+@pytest.mark.parametrize("M,fmt", [(1, 1), (17, 1), (1, 0), (17, 0)])
+def test_block_gemm_max_k(M, fmt):
+    """The largest K the entry points accept, 2^22 (32768 K blocks), through
+    the device quantizers and fp8_block_gemm: the decode kernel (M = 1) and
+    the split-K tile kernel (M = 17).  The activations are zero except in 24
+    K blocks spread over the whole range, both ends included; each of those
+    1 x 128 groups holds one power-of-two magnitude 2^a (a in -2..2, a third
+    of the signs negative), and the 24-row weights hold 2^-(3 + j) with j in
+    0..5 varying by row and block.  Both quantizers are then lossless: with
+    UE8M0 scales a group gets 2^(a - 8) and codes +-256 and every weight
+    block gets 2^-11 and codes 2^(8 - j), so dequantized operands equal the
+    inputs; with fp32 scales they differ from them by one fp32 rounding of
+    the scale.  The product is then the plain sum over the 24 blocks, exact
+    in fp64 and in the kernels' fp32 accumulation (multiples of 2^-10 below
+    2^11): UE8M0 must give its bf16 rounding bit for bit (a dropped, doubled
+    or mispaired K block, or a wrong far-end offset, moves the sum by at
+    least 2^-3), fp32 scales must be within the acceptance bound."""
+    import torch
+    from block_scaled_precision_fp8_amd import lib as L
+    K, N = 1 << 22, 24
+    KB = K // 128
+    say(f"max-K block gemm M={M} N={N} K={K} fmt={fmt}")
+    g = np.random.default_rng(22 + M)
+    blocks = np.array(sorted({0, 1, 2, 127, 128, 4095, 4096, 16383, 16384, KB - 2, KB - 1}
+                             | set(int(b) for b in g.choice(np.arange(3, KB - 2), 13, replace=False))))
+    assert len(blocks) == 24
+    kk = (blocks[:, None] * 128 + np.arange(128)[None, :]).reshape(-1)      # the nonzero columns
+    x = np.zeros((M, K), dtype=np.float32)
+    for i, b in enumerate(blocks):
+        for m in range(M):
+            a = (i + m) % 5 - 2
+            k = b * 128 + np.arange(128)
+            x[m, k] = np.where(k % 3 == 0, -1.0, 1.0) * np.float32(2.0 ** a)
+    j = (np.arange(KB)[None, :] + np.arange(N)[:, None]) % 6                # (N, KB)
+    w = np.repeat(np.exp2(-(3.0 + j)).astype(np.float32), 128, axis=1)     # (N, K)
+    ref = x[:, kk].astype(np.float64) @ w[:, kk].astype(np.float64).T        # the 24 blocks
+    xd = to_dev_bf16(synth.f32_to_bf16_bits(x))
+    wd = to_dev_bf16(synth.f32_to_bf16_bits(w))
+    del x, w
+    sdt = torch.float32 if fmt == 0 else torch.uint8
+    xq = torch.empty((M, K), dtype=torch.uint8, device=xd.device)
+    xs = torch.empty((M, KB), dtype=sdt, device=xd.device)
+    wq = torch.empty((N, K), dtype=torch.uint8, device=xd.device)
+    ws = torch.empty((1, KB), dtype=sdt, device=xd.device)
+    L.fp8_quant_act(xd, xq, xs, scale_fmt=fmt)
+    L.fp8_quant_weight(wd, wq, ws, scale_fmt=fmt)
+    y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=xd.device)
+    L.fp8_block_gemm(xq, xs, wq, ws, y, scale_fmt=fmt)
+    torch.cuda.synchronize()
+    got = F.bf16_decode(bf16_bits(y))
+    assert np.isfinite(got).all(), "unwritten outputs"
+    if fmt == 1:
+        bad = np.argwhere(got != F.bf16_round(ref))
+        assert bad.size == 0, f"{len(bad)} outputs differ, first {bad[0]}: {got[tuple(bad[0])]} vs {ref[tuple(bad[0])]}"
+    else:
+        err = rel_fro(got, ref)
+        say(f"  rel fro {err:.3e}")
+        assert err <= TOL
