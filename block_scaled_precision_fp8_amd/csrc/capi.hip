@@ -434,6 +434,9 @@ int32_t fp4_group_gemm(const void* xq4, const void* x_gscale, const float* x_tsc
   if (M < 0 || N < 0 || K < 0 || !fits_i32(M) || !fits_i32(N) || !fits_i32(K))
     return BSFP8_EINVAL;
   if (K % 32 != 0 || N % 8 != 0) return BSFP8_EINVAL;
+  // the kernels address a tile's rows (up to 256 of K/2 bytes) with 32-bit
+  // offsets from one base: the same K bound as the FP8 GEMMs
+  if (K > kMaxGemmK) return BSFP8_ENOTSUP;
   if (M == 0) return BSFP8_OK;
   if (N == 0 || K == 0) return BSFP8_EINVAL;
   if (!xq4 || !x_gscale || !x_tscale || !wq4 || !w_gscale || !w_tscale || !y)

@@ -319,6 +319,8 @@ BSFP8_API int32_t fp4_quant(const void* x, int64_t R, int64_t K, int32_t dynamic
  *   wq4, w_gscale, w_tscale   as written by fp4_quant for W (N rows).
  *   y                          out, bf16 [M][N].  K % 32 == 0.
  *   workspace  >= bsfp8_workspace_size(BSFP8_OP_FP4_GEMM, M, N, K, 0).
+ * Errors: EINVAL (sizes, null pointers, misalignment), ENOTSUP (K > 2^22,
+ * the bound of the FP8 GEMMs), ENOSPC (workspace).
  */
 BSFP8_API int32_t fp4_group_gemm(const void* xq4, const void* x_gscale,
                        const float* x_tscale, const void* wq4,

@@ -231,6 +231,9 @@ def test_fp4_argument_checks():
                               None) == L.EINVAL
     assert lib.fp4_group_gemm(FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 4, 64, 64, None, 0,
                               None) == L.EINVAL
+    # K beyond 2^22: its 32-bit tile offsets would wrap (as the FP8 GEMMs)
+    assert lib.fp4_group_gemm(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 64, 2**22 + 32, None,
+                              0, None) == L.ENOTSUP
 
 
 def test_workspace_size_unknown_op():
