@@ -18,7 +18,7 @@ Readings where the pages are silent:
      E2M1(w * 2^-e) rounded to nearest even; amax = 0 gives e = 0;
  18. activations are the FP8 1 x 128 groups of the FP8 path (fp32 or UE8M0
      scales); Y = sum_k dec(xq) s_a dec(wq) s_w in fp64, bf16 output
-     rounding judged by the usual 2e-3 relative Frobenius bound.
+     rounding held to the usual 2e-3 relative Frobenius bound.
 """
 
 import numpy as np
