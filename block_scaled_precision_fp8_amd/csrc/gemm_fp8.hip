@@ -933,6 +933,13 @@ constexpr int kDecodeDepth = 2;
 // and takes the X chunks g4 and g4 + 4 (the FP4 x FP8 lane pairing of the
 // scaled MFMA).  The kernel is bound by the latency of each workgroup's one
 // round of loads, not by bytes, so MXFP4 rows run at about the FP8 time.
+// XB (plain FP8 weights, from 8 tokens): every load of a block goes out
+// unconditionally through a buffer resource (out-of-range offsets read
+// zeros) instead of behind a branch per load, and the activation loads are
+// held ahead of the weight loads: with no branch between them the compiler
+// knows how many loads are in flight at each use, so the fused encoding waits
+// for its activations alone and runs under the weight loads (behind branches
+// it waited for all of them first).
 // B32: (32, 32) weight blocks with 1 x 32 act groups.  A lane's 32 weight
 // and activation bytes of a block are exactly the 32-wide group g4, so the
 // block runs as four MFMAs whose weight operand keeps only group g's lanes,
@@ -942,7 +949,7 @@ constexpr int kDecodeDepth = 2;
 constexpr int kDecodeXsBytes = 16384;
 
 template <int FMT, bool FUSED, bool W4 = false, bool B32 = false, bool SXL = false,
-          bool SWL = false>
+          bool SWL = false, bool XB = true>
 __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
     const uint8_t* __restrict__ xq, const void* __restrict__ xs,
     const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ wq,
@@ -961,7 +968,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
   static_assert(!SWL || W4 || B32, "staged weight scales: MXFP4 or (32, 32) blocks");
   __shared__ __attribute__((aligned(16))) uint8_t sws[SWL ? kDecodeXsBytes : 16];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  constexpr bool PLAIN = !W4 && !B32 && XB;
+  const int wave = PLAIN ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : threadIdx.x >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
   const int64_t n0 = (int64_t)blockIdx.x * 16;
   const int64_t nrow = n0 + l16;
@@ -998,6 +1006,17 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
     __syncthreads();
   }
   const uint8_t* wrow = wq + nrow * KW;
+  // PLAIN (FP8 weights in 128-blocks): every load of a block is issued
+  // unconditionally through a buffer resource (out-of-range offsets read
+  // zeros), so no load sits behind a branch and the compiler's count of the
+  // loads in flight stays exact: the encoding of a block then waits for its
+  // activations only, not for every weight load issued after them
+  const int64_t wrows = min((int64_t)16, N - n0);
+  const __amdgpu_buffer_rsrc_t rwb = make_rsrc(wq + n0 * KW, PLAIN ? wrows * KW : 0);
+  const uint32_t wlo = (uint32_t)(l16 * KW);
+  const __amdgpu_buffer_rsrc_t rxb = make_rsrc(FUSED ? (const void*)x : (const void*)xq,
+                                               FUSED ? (int64_t)M * ldx * 2 : (int64_t)M * K);
+  const __amdgpu_buffer_rsrc_t rxs = make_rsrc(xs, (int64_t)M * KB * SBX);
   // this lane's X elements of a block: two runs of 16 starting at kx0, kx1
   const int kx0 = W4 ? 16 * g4 : 32 * g4;
   const int kx1 = W4 ? 64 + 16 * g4 : 32 * g4 + 16;
@@ -1023,11 +1042,19 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int64_t k = (i < 2 ? k0 : k1) + 8 * (i & 1);
-          xv[u][i] = make_uint4(0, 0, 0, 0);
-          if (kb < KB && mvalid && k < K) xv[u][i] = *(const uint4*)(x + (int64_t)l16 * ldx + k);
+          if constexpr (PLAIN) {
+            const uint32_t o = (kb < KB && mvalid && k < K) ? (uint32_t)(((int64_t)l16 * ldx + k) * 2) : kOOB;
+            const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rxb, o, 0, 0);
+            xv[u][i] = make_uint4(t.x, t.y, t.z, t.w);
+          } else {
+            xv[u][i] = make_uint4(0, 0, 0, 0);
+            if (kb < KB && mvalid && k < K) xv[u][i] = *(const uint4*)(x + (int64_t)l16 * ldx + k);
+          }
         }
       }
     }
+    // keep the activation loads ahead of the weight loads in issue order
+    if constexpr (FUSED && PLAIN) __builtin_amdgcn_sched_barrier(0);
     // B32: the four groups' scales (fp32), or this lane's group's bytes
     float sx4[B32 ? DEPTH : 1][4], sw32[B32 ? DEPTH : 1][4];
 #pragma unroll
@@ -1039,7 +1066,9 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
       // the weight block scale: with fp32 scales it multiplies this lane's
       // OUTPUT column (token l16), so every lane needs it, whatever its row
       swb[u] = (FMT == 0) ? 0.f : __int_as_float(127);
-      if (!W4 && !B32 && kb < KB) swb[u] = load_scale<FMT>(wsc, nblk * KB + kb);
+      // a uniform address (kb, nblk): a scalar load, clamped in range
+      if (PLAIN) swb[u] = load_scale<FMT>(wsc, min(nblk * KB + kb, ((N + 127) / 128) * KB - 1));
+      else if (!W4 && !B32 && kb < KB) swb[u] = load_scale<FMT>(wsc, nblk * KB + kb);
       if constexpr (B32) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
@@ -1075,11 +1104,19 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
             sw4[u] = SWL ? (int)sws[l16 * G32 + (int64_t)kb * 4 + g4]
                          : (int)((const uint8_t*)wsc)[nrow * G32 + (int64_t)kb * 4 + g4];
           }
-        } else {
+        } else if constexpr (!PLAIN) {
           const int64_t k = (int64_t)kb * 128 + g4 * 32;
           if (k < K) wa[u] = ld_stream16(wrow + k);
           if (k + 16 < K) wb[u] = ld_stream16(wrow + k + 16);
         }
+      }
+      if constexpr (PLAIN) {
+        const int64_t k = (int64_t)kb * 128 + g4 * 32;
+        const bool kin = kb < KB;
+        u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rwb, kin && k < K ? wlo + (uint32_t)k : kOOB, 0, 2);
+        wa[u] = make_uint4(t.x, t.y, t.z, t.w);
+        t = __builtin_amdgcn_raw_buffer_load_b128(rwb, kin && k + 16 < K ? wlo + (uint32_t)k + 16 : kOOB, 0, 2);
+        wb[u] = make_uint4(t.x, t.y, t.z, t.w);
       }
       if constexpr (!FUSED) {
         // the quantized X fragment and its scale (L2-resident), issued with
@@ -1087,7 +1124,27 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
         xa[u] = make_uint4(0, 0, 0, 0);
         xb[u] = make_uint4(0, 0, 0, 0);
         sx[u] = (FMT == 0) ? 0.f : __int_as_float(127);
-        if (kb < KB && mvalid) {
+        if constexpr (PLAIN) {
+          const int64_t k0 = (int64_t)kb * 128 + kx0, k1 = (int64_t)kb * 128 + kx1;
+          const bool ok = kb < KB && mvalid;
+          const uint32_t xo = (uint32_t)(l16 * K);
+          u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rxb, ok && k0 < K ? xo + (uint32_t)k0 : kOOB, 0, 0);
+          xa[u] = make_uint4(t.x, t.y, t.z, t.w);
+          t = __builtin_amdgcn_raw_buffer_load_b128(rxb, ok && k1 < K ? xo + (uint32_t)k1 : kOOB, 0, 0);
+          xb[u] = make_uint4(t.x, t.y, t.z, t.w);
+          if constexpr (SXL) {
+            if (ok) sx[u] = FMT == 0 ? ((const float*)sxs)[l16 * KB + kb]
+                                     : __int_as_float((int)sxs[l16 * KB + kb]);
+          } else {
+            const uint32_t so = ok ? (uint32_t)((l16 * KB + kb) * SBX) : kOOB;
+            if constexpr (FMT == 0) {
+              sx[u] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rxs, so, 0, 0));
+            } else {
+              const int b = (int)__builtin_amdgcn_raw_buffer_load_b8(rxs, so, 0, 0);
+              sx[u] = __int_as_float(ok ? b : 127);
+            }
+          }
+        } else if (kb < KB && mvalid) {
           const int64_t k0 = (int64_t)kb * 128 + kx0, k1 = (int64_t)kb * 128 + kx1;
           if (k0 < K) xa[u] = *(const uint4*)(xq + (int64_t)l16 * K + k0);
           if (k1 < K) xb[u] = *(const uint4*)(xq + (int64_t)l16 * K + k1);
@@ -2126,9 +2183,17 @@ hipError_t launch_decode(const GemmArgs& a, hipStream_t st) {
   const bool pers = decode_pers(a.M, a.N, a.K);
   if (a.x_bf16 && pers && a.M * a.K <= kPersFusedMaxMK) {
     return launch_pers_depth<FMT, true>(a, st);
-  } else if (a.x_bf16) {
+  } else if (a.x_bf16 && a.M >= 8 && a.M * a.ldx * 2 <= 0x7fffffffLL) {
+    // from 8 tokens the branch-free loads (XB; the activations through a
+    // buffer resource over M ldx bf16 values, so that span must fit its
+    // 32-bit range): 1.12x at 16 x 4096 x 4096; below 8 tokens they measured
+    // 1-4% slower and the loads stay behind their branches
     hipLaunchKernelGGL((gemm_decode_kernel<FMT, true>), grid, block, 0, st, nullptr, nullptr,
                        a.x_bf16, a.ldx, a.wq, a.ws, a.bias, a.y, (int)a.M, a.N, a.K, a.xstat);
+  } else if (a.x_bf16) {
+    hipLaunchKernelGGL((gemm_decode_kernel<FMT, true, false, false, false, false, false>), grid,
+                       block, 0, st, nullptr, nullptr, a.x_bf16, a.ldx, a.wq, a.ws, a.bias, a.y,
+                       (int)a.M, a.N, a.K, a.xstat);
   } else if (a.blk == 32) {
     // (32, 32) blocks: the M x K/32 activation scales (M >= 4) and the tile's
     // row of weight-block scales from LDS
@@ -2162,9 +2227,13 @@ hipError_t launch_decode(const GemmArgs& a, hipStream_t st) {
       hipLaunchKernelGGL((gemm_decode_kernel<FMT, false, false, false, true>), grid, block, 0, st,
                          a.xq, a.xs, nullptr, (int64_t)0, a.wq, a.ws, a.bias, a.y, (int)a.M, a.N,
                          a.K, nullptr);
-    else
+    else if (a.M >= 8)
       hipLaunchKernelGGL((gemm_decode_kernel<FMT, false>), grid, block, 0, st, a.xq, a.xs, nullptr,
                          (int64_t)0, a.wq, a.ws, a.bias, a.y, (int)a.M, a.N, a.K, nullptr);
+    else
+      hipLaunchKernelGGL((gemm_decode_kernel<FMT, false, false, false, false, false, false>), grid,
+                         block, 0, st, a.xq, a.xs, nullptr, (int64_t)0, a.wq, a.ws, a.bias, a.y,
+                         (int)a.M, a.N, a.K, nullptr);
   }
   return hipGetLastError();
 }

@@ -631,3 +631,49 @@ def test_block_gemm_max_k(M, fmt):
         err = rel_fro(got, ref)
         say(f"  rel fro {err:.3e}")
         assert err <= TOL
+
+
+@pytest.mark.parametrize("M,N,K,ldx,fmt", [
+    (16, 4088, 4096, 4160, 0),    # branch-free loads (8+ tokens), ragged N
+    (8, 520, 1024, 1096, 1),      # the smallest token count on those loads
+    (5, 264, 640, 648, 0),        # below 8 tokens: the branch-guarded loads
+    (16, 2048, 6144, 6208, 1),    # the longest row the fused form takes
+])
+def test_linear_fused_decode_row_stride(M, N, K, ldx, fmt):
+    """fp8_linear's one-launch decode form on activations with a row stride
+    above K (a view of wider rows): bit-identical to fp8_quant_act +
+    fp8_block_gemm on the same view, codes equal to the oracle's, the
+    product within the bound of the oracle's."""
+    import torch
+    from block_scaled_precision_fp8_amd import lib as L
+    assert L.gemm_kernel(M, N, K)[0] == L.GEMM_DECODE
+    assert L.workspace_size(L.OP_LINEAR, M, N, K) == 0            # fused in the decode launch
+    say(f"fused decode linear M={M} N={N} K={K} ldx={ldx} fmt={fmt}")
+    xfull = synth.deepseek_acts(M, ldx, seed=M + K) if fmt else synth.llama_acts(M, ldx, seed=M + K)
+    x = np.ascontiguousarray(xfull[:, :K])
+    w = synth.normal_bf16((N, K), 0.02, "llama", "w", seed=N + K)
+    b = synth.normal_bf16((N,), 0.5, "llama", "bias", seed=N)
+    xd = to_dev_bf16(xfull)[:, :K]
+    assert xd.stride(0) == ldx
+    wd, bd = to_dev_bf16(w), to_dev_bf16(b)
+    sdt = torch.float32 if fmt == 0 else torch.uint8
+    G_ = -(-K // 128)
+    xq = torch.empty((M, K), dtype=torch.uint8, device=wd.device)
+    xs = torch.empty((M, G_), dtype=sdt, device=wd.device)
+    wq = torch.empty((N, K), dtype=torch.uint8, device=wd.device)
+    ws = torch.empty((-(-N // 128), G_), dtype=sdt, device=wd.device)
+    L.fp8_quant_act(xd, xq, xs, scale_fmt=fmt)
+    L.fp8_quant_weight(wd, wq, ws, scale_fmt=fmt)
+    y1 = torch.empty((M, N), dtype=torch.bfloat16, device=wd.device)
+    y2 = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=wd.device)
+    L.fp8_block_gemm(xq, xs, wq, ws, y1, bias=bd, scale_fmt=fmt)
+    L.fp8_linear(xd, wq, ws, y2, bias=bd, scale_fmt=fmt)
+    torch.cuda.synchronize()
+    b1, b2 = bf16_bits(y1), bf16_bits(y2)
+    assert np.array_equal(b1, b2), f"{np.count_nonzero(b1 != b2)} outputs differ from quant + gemm"
+    hq, hs = Q.quant_act(x, 128, fmt)
+    assert np.array_equal(xq.cpu().numpy(), hq)
+    ref = G.block_gemm(hq, hs, *Q.quant_weight(w, 128, 128, fmt), bias=F.bf16_decode(b), fmt=fmt)
+    err = rel_fro(F.bf16_decode(b2), ref)
+    say(f"  rel fro {err:.3e}")
+    assert err <= TOL
