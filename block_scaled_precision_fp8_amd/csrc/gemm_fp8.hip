@@ -1309,25 +1309,32 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_pers_kernel(
 
   int t0 = blockIdx.x, c0 = 0;       // the launcher sizes the grid <= ntiles
 
-  // FUSED: the first XU groups' bf16 loads of every lane go out before the
-  // first weight chunk, so encoding them waits for them alone (loads
-  // complete in issue order); at M K <= 40960 that covers every group of
-  // up to 2.5 tokens
+  // FUSED: every lane's bf16 loads of all its groups (at most XB batches of
+  // XU: M K <= 40960 is at most 336 groups) go out before the first weight
+  // chunk, unconditionally through a buffer resource over the M rows of ldx
+  // values (out-of-range offsets read zeros; the launcher keeps that span in
+  // the 32-bit range): with no branch between the loads the compiler counts
+  // them exactly, so encoding a batch waits for its own loads alone (loads
+  // complete in issue order), not for the weight chunk behind them
   constexpr int QW = 4 * kDecodeWaves;     // quarter-waves per workgroup
-  constexpr int XU = 4;                    // groups (loads) in flight per lane
-  uint4 xv[FUSED ? XU : 1];
-  auto xload = [&](int gi0) __attribute__((always_inline)) {
+  constexpr int XU = 4;                    // groups (loads) per lane and batch
+  constexpr int XB = 2;                    // batches
+  uint4 xv[FUSED ? XB * XU : 1];
+  if constexpr (FUSED) {
+    const __amdgpu_buffer_rsrc_t rxv = make_rsrc(x, (int64_t)M * ldx * 2);
     const int ql = threadIdx.x & 15;
 #pragma unroll
-    for (int u = 0; u < XU; ++u) {
-      const int gi = gi0 + u * QW;
+    for (int b = 0; b < XB * XU; ++b) {
+      const int gi = (int)(threadIdx.x >> 4) + b * QW;
       const int m = gi / KB, g = gi - m * KB;
       const int64_t k0 = (int64_t)g * 128 + ql * 8;
-      xv[u] = make_uint4(0, 0, 0, 0);
-      if (gi < M * KB && k0 < K) xv[u] = *(const uint4*)(x + (int64_t)m * ldx + k0);
+      const uint32_t off =
+          (gi < M * KB && k0 < K) ? (uint32_t)(((int64_t)m * ldx + k0) * 2) : kOOB;
+      const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rxv, off, 0, 0);
+      xv[b] = make_uint4(t.x, t.y, t.z, t.w);
     }
-  };
-  if constexpr (FUSED) xload(threadIdx.x >> 4);
+    __builtin_amdgcn_sched_barrier(0);     // ahead of the weight chunk
+  }
   issue(std::integral_constant<int, 0>{}, t0, c0);   // in flight during the copy below
 
   // activation scales (M x KB) and codes (M x K), once per workgroup
@@ -1342,9 +1349,10 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_pers_kernel(
     // Each lane has XU groups' loads in flight before encoding any of them.
     const int ql = threadIdx.x & 15;
     const int ngroups = M * KB;
-    for (int gi0 = threadIdx.x >> 4; gi0 < ngroups; gi0 += XU * QW) {
-      if (gi0 != (int)(threadIdx.x >> 4)) xload(gi0);   // the first batch is in flight
-      const uint4* v = xv;
+#pragma unroll
+    for (int bt = 0; bt < XB; ++bt) {
+      const int gi0 = (int)(threadIdx.x >> 4) + bt * XU * QW;
+      const uint4* v = xv + bt * XU;
 #pragma unroll
       for (int u = 0; u < XU; ++u) {
         const int gi = gi0 + u * QW;
@@ -2181,7 +2189,7 @@ hipError_t launch_decode(const GemmArgs& a, hipStream_t st) {
   // than the one scale row's loads it saves)
   const bool sxl = a.M >= 4 && a.M * ((a.K + 127) / 128) * (a.fmt == 0 ? 4 : 1) <= kDecodeXsBytes;
   const bool pers = decode_pers(a.M, a.N, a.K);
-  if (a.x_bf16 && pers && a.M * a.K <= kPersFusedMaxMK) {
+  if (a.x_bf16 && pers && a.M * a.K <= kPersFusedMaxMK && a.M * a.ldx * 2 <= 0x7fffffffLL) {
     return launch_pers_depth<FMT, true>(a, st);
   } else if (a.x_bf16 && a.M >= 8 && a.M * a.ldx * 2 <= 0x7fffffffLL) {
     // from 8 tokens the branch-free loads (XB; the activations through a
